@@ -1,0 +1,461 @@
+// C ABI of the Lighthouse layer (declared in include/lh.h): argument checks,
+// the static plan of a call, workspace carving and the launch sequence.
+// Nothing here allocates, synchronises or reads device memory.
+#include <math.h>
+#include <string.h>
+
+#include "lh_internal.h"
+
+namespace lh {
+
+static int ilog2_exact(int p)
+{
+    for (int b = 0; b < 31; ++b)
+        if ((1 << b) == p)
+            return b;
+    return -1;
+}
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, Plan *pl)
+{
+    memset(pl, 0, sizeof(*pl));
+    if (N < 1 || H < 1 || L < 1 || k < 0)
+        return LH_EINVAL;
+    if (dt != LH_BF16 && dt != LH_F32)
+        return LH_EINVAL;
+    if (d < 16 || d % 16 != 0)
+        return LH_EINVAL;
+    if (d != 64 && d != 128)
+        return LH_EUNSUPPORTED;
+    if (L > kMaxLevels)
+        return LH_EUNSUPPORTED;
+    int log2p = 1;
+    if (L > 1) {
+        if (p < 2)
+            return LH_EINVAL;
+        log2p = ilog2_exact(p);
+        if (log2p < 1 || log2p > 3)
+            return LH_EUNSUPPORTED; // p in {2, 4, 8}
+        if ((L - 1) * log2p > 27)
+            return LH_EUNSUPPORTED;
+    }
+    if (N > kMaxN)
+        return LH_EUNSUPPORTED;
+    const int top_shift = (L - 1) * log2p;
+    if (L > 1 && (N & ((int64_t(1) << top_shift) - 1)) != 0)
+        return LH_EINVAL; // N must be a multiple of p^(L-1)
+    pl->N = N; pl->H = H; pl->d = d; pl->L = L; pl->p = L > 1 ? p : 2; pl->log2p = log2p; pl->k = L > 1 ? k : 0;
+    pl->dt = dt;
+    int64_t tot = 0;
+    for (int l = 0; l < L; ++l) {
+        pl->n[l] = N >> (l * log2p);
+        pl->lvl_off[l] = tot;
+        tot += pl->n[l];
+    }
+    pl->lvl_total = tot;
+    if (L > 1) {
+        if (k > pl->n[L - 1])
+            return LH_EINVAL;
+        for (int l = 1; l < L; ++l) {
+            if (pl->n[l] > kStratum && pl->n[l] % kStratum != 0)
+                return LH_EINVAL;
+            pl->C[l] = pl->n[l] <= kStratum ? 1 : (int)(pl->n[l] / kStratum);
+            pl->strata_total += pl->C[l];
+        }
+        if ((int64_t)(L - 1) * k > kMaxSelTotal)
+            return LH_EUNSUPPORTED;
+    }
+    const int64_t pk = (int64_t)pl->p * pl->k;
+    pl->S = pl->n[L - 1] + (int64_t)(L - 1) * pk;
+    pl->S_pad = (int64_t)round_up((size_t)pl->S, kSubseqAlign);
+
+    // Pooled levels the front pass writes (fp32 rows): the top level (gathered
+    // whole) and every middle level whose full write plus the gathered reads
+    // moves fewer bytes than averaging the gathered entries' p^l input rows
+    // again in the gather.
+    for (int l = 0; l < kMaxLevels; ++l)
+        pl->mat_off[l] = -1;
+    pl->mat_rows = 0;
+    const int64_t in_bytes = dt == LH_BF16 ? 2 : 4;
+    if (L > 1) {
+        for (int l = 1; l < L; ++l) {
+            const bool top = l == L - 1;
+            const bool cheaper = (pl->n[l] + pk) * 4 < (pk << (l * log2p)) * in_bytes;
+            if (top || cheaper) {
+                pl->mat_mask |= 1u << l;
+                pl->mat_off[l] = pl->mat_rows;
+                pl->mat_rows += pl->n[l];
+            }
+        }
+    }
+    // Rows one lane group streams: a whole number of top-level windows, up to 64 rows.
+    const int64_t P = int64_t(1) << top_shift;
+    int64_t w = 1;
+    while (P * w * 2 <= 64 && (pl->n[L - 1] % (w * 2)) == 0)
+        w *= 2;
+    pl->run = (int)(P * w);
+
+    const size_t Hs = (size_t)H, Sp = (size_t)pl->S_pad, D = (size_t)d;
+    size_t b[IR_COUNT];
+    b[LH_R_SCORES] = 4 * Hs * (size_t)tot;
+    b[LH_R_SEL] = 4 * Hs * (size_t)(L - 1) * (size_t)pl->k;
+    b[LH_R_SLOT] = 4 * Hs * (size_t)tot;
+    b[LH_R_ENT] = 4 * Hs * Sp;
+    for (int r = LH_R_QHI; r <= LH_R_V_T; ++r)
+        b[r] = 2 * Hs * Sp * D;
+    b[LH_R_OSUB] = 4 * Hs * Sp * D;
+    b[LH_R_LSE] = 4 * Hs * Sp;
+    b[LH_R_DOSUB] = 4 * Hs * Sp * D;
+    b[LH_R_DQSUB] = b[LH_R_DKSUB] = b[LH_R_DVSUB] = 4 * Hs * Sp * D;
+    b[IR_POOLED] = 4 * 3 * Hs * (size_t)pl->mat_rows * D;
+    b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
+    b[IR_DELTA] = 4 * Hs * Sp;
+    size_t off = 0;
+    for (int r = 0; r < IR_COUNT; ++r) {
+        pl->off[r] = off;
+        pl->bytes[r] = b[r];
+        off = round_up(off + b[r], 256);
+    }
+    pl->total = off;
+    return LH_OK;
+}
+
+template <typename Tp> static Tp *at(void *ws, const Plan &pl, int r)
+{
+    return reinterpret_cast<Tp *>(static_cast<char *>(ws) + pl.off[r]);
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static lh_status check_ws(const Plan &pl, void *ws, size_t ws_bytes)
+{
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < pl.total)
+        return LH_EWORKSPACE;
+    return LH_OK;
+}
+
+static void record(void *const *events, int i, hipStream_t s)
+{
+    if (events)
+        (void)hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
+}
+
+static const char *kFwdStages[] = {"front", "topk", "index", "gather", "attn_fwd", "scatter"};
+static const char *kBwdStages[] = {"scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd"};
+
+static lh_status forward_impl(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
+                              int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, hipStream_t s,
+                              void *const *events)
+{
+    Plan pl;
+    lh_status st = make_plan(N, H, d, L, p, k_sel, dt, &pl);
+    if (st != LH_OK)
+        return st;
+    if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LH_EINVAL;
+    if ((st = check_ws(pl, ws, ws_bytes)) != LH_OK)
+        return st;
+
+    float *scores = at<float>(ws, pl, LH_R_SCORES);
+    int32_t *sel = at<int32_t>(ws, pl, LH_R_SEL);
+    int32_t *slot = at<int32_t>(ws, pl, LH_R_SLOT);
+    int32_t *ent = at<int32_t>(ws, pl, LH_R_ENT);
+    float *pooled = at<float>(ws, pl, IR_POOLED);
+    const int64_t tensor_stride = (int64_t)H * pl.mat_rows * d;
+
+    record(events, 0, s);
+    if (L > 1) {
+        FrontArgs fa;
+        memset(&fa, 0, sizeof(fa));
+        fa.q = q; fa.k = k; fa.v = v; fa.scores = scores; fa.pooled = pooled;
+        fa.N = N; fa.lvl_total = pl.lvl_total; fa.mat_rows = pl.mat_rows; fa.tensor_stride = tensor_stride;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            fa.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+            fa.mat_off[l] = pl.mat_off[l];
+        }
+        fa.H = H; fa.L = L; fa.log2p = pl.log2p; fa.run = pl.run; fa.runs_per_head = (int)(N / pl.run);
+        if (launch_front(pl, fa, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 1, s);
+    if (L > 1) {
+        TopkArgs ta;
+        memset(&ta, 0, sizeof(ta));
+        ta.scores = scores; ta.sel = sel; ta.slot = slot; ta.lvl_total = pl.lvl_total;
+        int before = 0;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            ta.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+            ta.n[l] = l < L ? pl.n[l] : 0;
+            ta.C[l] = pl.C[l];
+            ta.strata_before[l] = before;
+            if (l >= 1 && l < L)
+                before += pl.C[l];
+        }
+        ta.L = L; ta.log2p = pl.log2p; ta.k = pl.k;
+        if (launch_topk(pl, ta, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 2, s);
+    {
+        IndexArgs ia;
+        memset(&ia, 0, sizeof(ia));
+        ia.sel = sel; ia.slot = slot; ia.ent = ent;
+        ia.lvl_total = pl.lvl_total; ia.S = pl.S; ia.S_pad = pl.S_pad;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            ia.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+            ia.n[l] = l < L ? pl.n[l] : 0;
+        }
+        ia.L = L; ia.log2p = pl.log2p; ia.k = pl.k;
+        if (launch_index(pl, ia, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 3, s);
+    {
+        GatherArgs ga;
+        memset(&ga, 0, sizeof(ga));
+        ga.q = q; ga.k = k; ga.v = v; ga.pooled = pooled; ga.ent = ent;
+        ga.hi[0] = at<uint16_t>(ws, pl, LH_R_QHI);
+        ga.hi[1] = at<uint16_t>(ws, pl, LH_R_KHI);
+        ga.hi[2] = at<uint16_t>(ws, pl, LH_R_V);
+        ga.lo[0] = at<uint16_t>(ws, pl, LH_R_QLO);
+        ga.lo[1] = at<uint16_t>(ws, pl, LH_R_KLO);
+        ga.hi_t[0] = at<uint16_t>(ws, pl, LH_R_QHI_T);
+        ga.hi_t[1] = at<uint16_t>(ws, pl, LH_R_KHI_T);
+        ga.hi_t[2] = at<uint16_t>(ws, pl, LH_R_V_T);
+        ga.N = N; ga.S = pl.S; ga.S_pad = pl.S_pad; ga.mat_rows = pl.mat_rows; ga.tensor_stride = tensor_stride;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            ga.mat_off[l] = pl.mat_off[l];
+            ga.n[l] = l < L ? pl.n[l] : 0;
+        }
+        ga.H = H; ga.L = L; ga.log2p = pl.log2p;
+        if (launch_gather(pl, ga, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 4, s);
+    {
+        AttnFwdArgs aa;
+        aa.qhi = at<uint16_t>(ws, pl, LH_R_QHI);
+        aa.qlo = at<uint16_t>(ws, pl, LH_R_QLO);
+        aa.khi = at<uint16_t>(ws, pl, LH_R_KHI);
+        aa.klo = at<uint16_t>(ws, pl, LH_R_KLO);
+        aa.vt = at<uint16_t>(ws, pl, LH_R_V_T);
+        aa.o = at<float>(ws, pl, LH_R_OSUB);
+        aa.lse = at<float>(ws, pl, LH_R_LSE);
+        aa.S = pl.S; aa.S_pad = pl.S_pad; aa.H = H;
+        aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+        if (launch_attn_fwd(pl, aa, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 5, s);
+    {
+        ScatterArgs sa;
+        memset(&sa, 0, sizeof(sa));
+        sa.osub = at<float>(ws, pl, LH_R_OSUB); sa.slot = slot; sa.out = out;
+        sa.N = N; sa.lvl_total = pl.lvl_total; sa.S_pad = pl.S_pad;
+        for (int l = 0; l < kMaxLevels; ++l)
+            sa.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+        sa.H = H; sa.L = L; sa.log2p = pl.log2p;
+        if (launch_scatter(pl, sa, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 6, s);
+    return LH_OK;
+}
+
+static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
+                               void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, hipStream_t s,
+                               void *const *events)
+{
+    Plan pl;
+    lh_status st = make_plan(N, H, d, L, p, k_sel, dt, &pl);
+    if (st != LH_OK)
+        return st;
+    if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return LH_EINVAL;
+    if ((st = check_ws(pl, ws, ws_bytes)) != LH_OK)
+        return st;
+    int32_t *slot = at<int32_t>(ws, pl, LH_R_SLOT);
+    float *dosub = at<float>(ws, pl, LH_R_DOSUB);
+
+    record(events, 0, s);
+    {
+        ScatterBwdArgs a;
+        memset(&a, 0, sizeof(a));
+        a.dout = dout; a.slot = slot; a.dosub = dosub;
+        a.N = N; a.lvl_total = pl.lvl_total; a.S_pad = pl.S_pad;
+        for (int l = 0; l < kMaxLevels; ++l)
+            a.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+        a.H = H; a.L = L; a.log2p = pl.log2p; a.run = pl.run;
+        // u = j + 1 runs over [0, N + p^(L-1)): every top-level u-window, the last one partial.
+        const int64_t P = int64_t(1) << ((L - 1) * pl.log2p);
+        a.tiles_per_head = (int)((N + P + pl.run - 1) / pl.run);
+        if (launch_scatter_bwd(pl, a, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 1, s);
+    {
+        BwdPrepArgs a;
+        a.dosub = dosub; a.osub = at<float>(ws, pl, LH_R_OSUB);
+        a.dohi = at<uint16_t>(ws, pl, IR_DOHI); a.dolo = at<uint16_t>(ws, pl, IR_DOLO);
+        a.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
+        a.delta = at<float>(ws, pl, IR_DELTA);
+        a.S = pl.S; a.S_pad = pl.S_pad; a.H = H;
+        if (launch_bwd_prep(pl, a, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 2, s);
+    AttnBwdArgs ab;
+    ab.qhi = at<uint16_t>(ws, pl, LH_R_QHI);
+    ab.qlo = at<uint16_t>(ws, pl, LH_R_QLO);
+    ab.khi = at<uint16_t>(ws, pl, LH_R_KHI);
+    ab.klo = at<uint16_t>(ws, pl, LH_R_KLO);
+    ab.v = at<uint16_t>(ws, pl, LH_R_V);
+    ab.qhi_t = at<uint16_t>(ws, pl, LH_R_QHI_T);
+    ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);
+    ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);
+    ab.dolo = at<uint16_t>(ws, pl, IR_DOLO);
+    ab.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
+    ab.lse = at<float>(ws, pl, LH_R_LSE);
+    ab.delta = at<float>(ws, pl, IR_DELTA);
+    ab.dq = at<float>(ws, pl, LH_R_DQSUB);
+    ab.dk = at<float>(ws, pl, LH_R_DKSUB);
+    ab.dv = at<float>(ws, pl, LH_R_DVSUB);
+    ab.S = pl.S; ab.S_pad = pl.S_pad; ab.H = H;
+    ab.scale = (float)(1.0 / sqrt((double)d));
+    ab.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    if (launch_attn_bwd_dkdv(pl, ab, s) != hipSuccess)
+        return LH_EHIP;
+    record(events, 3, s);
+    if (launch_attn_bwd_dq(pl, ab, s) != hipSuccess)
+        return LH_EHIP;
+    record(events, 4, s);
+    {
+        PoolBwdArgs a;
+        memset(&a, 0, sizeof(a));
+        a.dsub[0] = ab.dq; a.dsub[1] = ab.dk; a.dsub[2] = ab.dv;
+        a.slot = slot;
+        a.dx[0] = dq; a.dx[1] = dk; a.dx[2] = dv;
+        a.N = N; a.lvl_total = pl.lvl_total; a.S_pad = pl.S_pad;
+        for (int l = 0; l < kMaxLevels; ++l)
+            a.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
+        a.H = H; a.L = L; a.log2p = pl.log2p;
+        if (launch_pool_bwd(pl, a, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    record(events, 5, s);
+    return LH_OK;
+}
+
+} // namespace lh
+
+using namespace lh;
+
+extern "C" {
+
+const char *lh_strerror(lh_status s)
+{
+    switch (s) {
+    case LH_OK: return "ok";
+    case LH_EINVAL: return "invalid argument";
+    case LH_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case LH_EUNSUPPORTED: return "shape not supported by this build";
+    case LH_EHIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+lh_status lh_check_shape(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt)
+{
+    Plan pl;
+    return make_plan(N, H, d, L, p, k, dt, &pl);
+}
+
+int64_t lh_subseq_len(int64_t N, int L, int p, int k)
+{
+    Plan pl;
+    if (make_plan(N, 1, 128, L, p, k, LH_BF16, &pl) != LH_OK)
+        return -1;
+    return pl.S;
+}
+
+int64_t lh_padded_subseq_len(int64_t N, int L, int p, int k)
+{
+    Plan pl;
+    if (make_plan(N, 1, 128, L, p, k, LH_BF16, &pl) != LH_OK)
+        return -1;
+    return pl.S_pad;
+}
+
+size_t lh_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt)
+{
+    Plan pl;
+    if (make_plan(N, H, d, L, p, k, dt, &pl) != LH_OK)
+        return 0;
+    return pl.total;
+}
+
+lh_status lh_region_info(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, lh_region region,
+                         size_t *offset, size_t *bytes)
+{
+    Plan pl;
+    lh_status st = make_plan(N, H, d, L, p, k, dt, &pl);
+    if (st != LH_OK)
+        return st;
+    if ((int)region < 0 || (int)region >= LH_R_COUNT || !offset || !bytes)
+        return LH_EINVAL;
+    *offset = pl.off[region];
+    *bytes = pl.bytes[region];
+    return LH_OK;
+}
+
+int lh_stage_count(int backward) { return backward ? 5 : 6; }
+
+const char *lh_stage_name(int backward, int stage)
+{
+    if (stage < 0 || stage >= lh_stage_count(backward))
+        return "";
+    return backward ? kBwdStages[stage] : kFwdStages[stage];
+}
+
+lh_status lh_forward(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p, int k_sel,
+                     lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+lh_status lh_forward_timed(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
+                           int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream,
+                           void *const *events)
+{
+    if (!events)
+        return LH_EINVAL;
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, events);
+}
+
+lh_status lh_backward(const void *dout, int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt, void *dq,
+                      void *dk, void *dv, void *ws, size_t ws_bytes, void *stream)
+{
+    return backward_impl(dout, N, H, d, L, p, k_sel, dt, dq, dk, dv, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+lh_status lh_backward_timed(const void *dout, int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
+                            void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream,
+                            void *const *events)
+{
+    if (!events)
+        return LH_EINVAL;
+    return backward_impl(dout, N, H, d, L, p, k_sel, dt, dq, dk, dv, ws, ws_bytes, (hipStream_t)stream, events);
+}
+
+lh_status lh_selftest_sqrt(uint32_t first, uint32_t count, uint32_t *mismatches, void *stream)
+{
+    if (!mismatches || ((uintptr_t)mismatches & 3u))
+        return LH_EINVAL;
+    if (launch_selftest_sqrt(first, count, mismatches, (hipStream_t)stream) != hipSuccess)
+        return LH_EHIP;
+    return LH_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,487 @@
+// Dense causal softmax attention over the gathered sub-sequence (aitrends
+// summary, 핵심 기여 and 기술 상세 item 3: stock FlashAttention on the S
+// gathered entries; its default: causal, scale 1/sqrt(d)), forward and
+// backward, as fp16 MFMA kernels for gfx950 with fp32 accumulation.
+//
+// MFMA used: v_mfma_f32_32x32x16_f16. Operand A supplies rows (lane l: row
+// l%32, 8 k-values of group l/32), operand B supplies columns the same way,
+// and the 32x32 fp32 result leaves row 8*(v/4) + 4*(l/32) + v%4, column l%32
+// in register v of lane l. Each lane therefore owns ONE column and 16 rows.
+//
+// The kernels use this to give every lane one query (forward, dQ) or one key
+// (dK/dV) and keep the softmax row statistics in-lane:
+//   * forward and dQ compute S^T = K Q^T (keys as rows). The A rows are loaded
+//     in a permuted key order kappa(r) so that register v of lane group g holds
+//     key 16*(v/8) + 8*g + v%8: two runs of 8 consecutive keys. Those runs are
+//     exactly the 8 k-values a lane must supply as operand B of the next
+//     product O^T += V^T P^T, so P goes from accumulator to operand without a
+//     shuffle, and V^T rows are read as 16-byte runs of 8 keys.
+//   * dK/dV computes S = Q K^T with queries permuted the same way.
+// Tiles of K/V (forward, dQ) or Q/dO (dK/dV) are staged in LDS with an XOR
+// swizzle on 16-byte chunks so that the 32 rows one MFMA operand read touches
+// fall in distinct banks.
+//
+// Precision: a logit is the sum of three products, q_hi.k_hi + q_hi.k_lo +
+// q_lo.k_hi, over fp16 pairs x = hi + lo of the gathered rows; dP uses the
+// fp16 pair of dO_sub (two products). P, dS, V, dO_sub's hi part and the
+// query / key hi parts of the gradient products are single fp16 operands.
+//
+// The backward is split into a dK/dV kernel (one workgroup per 128 keys) and a
+// dQ kernel (one workgroup per 128 queries) so that no gradient needs atomics
+// and results are bitwise reproducible.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+#define LH_LOG2E 1.4426950408889634f
+#define LH_LN2 0.6931471805599453f
+
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 pack8h(const float *x)
+{
+    return make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7]));
+}
+
+// Row kappa(r) of the 32-row block that MFMA row r reads (see header).
+__device__ __forceinline__ int kappa(int r)
+{
+    return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+
+// Physical 16-byte chunk of logical chunk `ch` in row `row` of an LDS tile
+// whose rows hold NCH chunks (16 for 256-byte rows, 8 for 128-byte rows).
+template <int NCH>
+__device__ __forceinline__ int swz(int row, int ch)
+{
+    if constexpr (NCH >= 16)
+        return ch ^ (row & 15);
+    else
+        return ch ^ ((row >> 1) & (NCH - 1));
+}
+
+__device__ __forceinline__ f32x16_t zero16()
+{
+    f32x16_t z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        z[v] = 0.0f;
+    return z;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ============================================================== forward
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
+{
+    constexpr int BM = 128, BN = 64;
+    constexpr int KCH = D / 8;  // chunks per K row
+    constexpr int VCH = BN / 8; // chunks per V^T row
+    constexpr int NS = D / 16;  // k-steps over d
+    constexpr int NT = D / 32;  // 32-dim tiles of the output
+    constexpr int KPT = BN * KCH / 256;
+    constexpr int VPT = D * VCH / 256;
+    __shared__ uint4 sKh[BN * KCH];
+    __shared__ uint4 sKl[BN * KCH];
+    __shared__ uint4 sV[D * VCH];
+
+    const int nqb = (int)((a.S + BM - 1) / BM);
+    const int h = blockIdx.x % a.H;
+    const int qb = nqb - 1 - (int)(blockIdx.x / a.H); // longest rows first
+    const int64_t q0 = (int64_t)qb * BM;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int64_t qw = q0 + wave * 32;
+    const int64_t hS = (int64_t)h * a.S_pad;
+    const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D;
+    const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
+
+    uint4 qh[NS], ql[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        qh[s] = ld16(a.qhi + (hS + qw + c32) * D + 16 * s + 8 * g);
+        ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
+    }
+
+    f32x16_t o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        o[t] = zero16();
+    float m = -INFINITY, lsum = 0.0f;
+
+    const int64_t kend = min(q0 + BM, a.S);
+    const int nkb = (int)((kend + BN - 1) / BN);
+    const int kap = kappa(c32);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int64_t k0 = (int64_t)kb * BN;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const int c = tid + 256 * u, key = c / KCH, ch = c % KCH;
+            const int at = key * KCH + swz<KCH>(key, ch);
+            sKh[at] = ld16(khi + (k0 + key) * D + ch * 8);
+            sKl[at] = ld16(klo + (k0 + key) * D + ch * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int c = tid + 256 * u, dim = c / VCH, ch = c % VCH;
+            sV[dim * VCH + swz<VCH>(dim, ch)] = ld16(vt + (int64_t)dim * a.S_pad + k0 + ch * 8);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < BN / 32; ++j) {
+            const int64_t kt0 = k0 + 32 * j;
+            if (kt0 > qw + 31)
+                break; // this wave's queries all precede these keys
+            f32x16_t st = zero16();
+            const int kl = 32 * j + kap;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int idx = kl * KCH + swz<KCH>(kl, 2 * s + g);
+                const uint4 kh = sKh[idx];
+                st = mfma32(kh, qh[s], st);
+                st = mfma32(sKl[idx], qh[s], st);
+                st = mfma32(kh, ql[s], st);
+            }
+            const bool diag = kt0 + 31 > qw;
+            float y[16];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                y[v] = st[v] * a.scale_log2;
+                if (diag && kt0 + 16 * (v >> 3) + 8 * g + (v & 7) > qw + c32)
+                    y[v] = -INFINITY;
+                mx = fmaxf(mx, y[v]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    o[t][v] *= alpha;
+            float pr[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                pr[v] = __builtin_amdgcn_exp2f(y[v] - mn);
+                lsum += pr[v];
+            }
+            const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int dim = 32 * t + c32;
+                o[t] = mfma32(sV[dim * VCH + swz<VCH>(dim, 4 * j + g)], pb0, o[t]);
+                o[t] = mfma32(sV[dim * VCH + swz<VCH>(dim, 4 * j + 2 + g)], pb1, o[t]);
+            }
+        }
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.0f / ltot;
+    float *orow = a.o + (hS + qw + c32) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<float4 *>(orow + 32 * t + 8 * i4 + 4 * g) =
+                make_float4(o[t][4 * i4] * inv, o[t][4 * i4 + 1] * inv, o[t][4 * i4 + 2] * inv, o[t][4 * i4 + 3] * inv);
+    if (g == 0)
+        a.lse[hS + qw + c32] = (m + __log2f(ltot)) * LH_LN2;
+}
+
+hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
+{
+    const unsigned nqb = (unsigned)((pl.S + 127) / 128);
+    const dim3 grid(nqb * pl.H);
+    if (pl.d == 128)
+        hipLaunchKernelGGL((k_attn_fwd<128>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_attn_fwd<64>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ============================================================== backward: dK, dV
+// One workgroup per 128 keys (32 per wave); queries are streamed through LDS
+// 64 at a time from the key block onwards. S = Q K^T with queries as
+// (permuted) rows, so a lane owns one key:
+//   dV^T += dO^T P,  dP = dO V^T,  dS = P * (dP - delta),  dK^T += Q^T dS.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
+{
+    constexpr int BK = 128, BQ = 64;
+    constexpr int RCH = D / 8;  // chunks per row-major row
+    constexpr int TCH = BQ / 8; // chunks per transposed row
+    constexpr int NS = D / 16, NT = D / 32;
+    constexpr int RPT = BQ * RCH / 256, TPT = D * TCH / 256;
+    extern __shared__ uint4 lds_dkdv[];
+    uint4 *sQh = lds_dkdv;         // [BQ][RCH]
+    uint4 *sQl = sQh + BQ * RCH;   // [BQ][RCH]
+    uint4 *sDh = sQl + BQ * RCH;   // [BQ][RCH]
+    uint4 *sDl = sDh + BQ * RCH;   // [BQ][RCH]
+    uint4 *sQT = sDl + BQ * RCH;   // [D][TCH]
+    uint4 *sDT = sQT + D * TCH;    // [D][TCH]
+    float *sL = reinterpret_cast<float *>(sDT + D * TCH); // [BQ] lse * log2(e)
+    float *sDel = sL + BQ;                                 // [BQ] delta
+
+    const int h = blockIdx.x % a.H;
+    const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
+    const int64_t k0 = (int64_t)kb * BK;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int64_t kw = k0 + wave * 32;
+    const int64_t hS = (int64_t)h * a.S_pad;
+    const int64_t key = kw + c32;
+
+    uint4 kh[NS], kl[NS], vf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t off = (hS + key) * D + 16 * s + 8 * g;
+        kh[s] = ld16(a.khi + off);
+        kl[s] = ld16(a.klo + off);
+        vf[s] = ld16(a.v + off);
+    }
+    f32x16_t dvT[NT], dkT[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        dvT[t] = zero16();
+        dkT[t] = zero16();
+    }
+    const int qap = kappa(c32);
+
+    for (int64_t q0 = k0; q0 < a.S; q0 += BQ) {
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int c = tid + 256 * u, r = c / RCH, ch = c % RCH;
+            const int64_t off = (hS + q0 + r) * D + ch * 8;
+            const int at = r * RCH + swz<RCH>(r, ch);
+            sQh[at] = ld16(a.qhi + off);
+            sQl[at] = ld16(a.qlo + off);
+            sDh[at] = ld16(a.dohi + off);
+            sDl[at] = ld16(a.dolo + off);
+        }
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+            const int c = tid + 256 * u, dim = c / TCH, ch = c % TCH;
+            const int64_t off = ((int64_t)h * D + dim) * a.S_pad + q0 + ch * 8;
+            const int at = dim * TCH + swz<TCH>(dim, ch);
+            sQT[at] = ld16(a.qhi_t + off);
+            sDT[at] = ld16(a.dohi_t + off);
+        }
+        if (tid < BQ) {
+            const int64_t q = q0 + tid;
+            sL[tid] = q < a.S ? a.lse[hS + q] * LH_LOG2E : 0.0f;
+            sDel[tid] = q < a.S ? a.delta[hS + q] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < BQ / 32; ++j) {
+            const int64_t qt0 = q0 + 32 * j;
+            if (qt0 + 31 < kw || qt0 >= a.S)
+                continue; // every query of the tile precedes this wave's keys, or is padding
+            const int ql = 32 * j + qap;
+            f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int at = ql * RCH + swz<RCH>(ql, 2 * s + g);
+                const uint4 q_h = sQh[at];
+                st = mfma32(q_h, kh[s], st);
+                st = mfma32(sQl[at], kh[s], st);
+                st = mfma32(q_h, kl[s], st);
+                dp = mfma32(sDh[at], vf[s], dp);
+                dp = mfma32(sDl[at], vf[s], dp);
+            }
+            float pr[16], ds[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 32 * j + 16 * (v >> 3) + 8 * g + (v & 7);
+                const int64_t q = q0 + qi;
+                const bool ok = q >= key && q < a.S;
+                pr[v] = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
+                ds[v] = pr[v] * (dp[v] - sDel[qi]);
+            }
+            const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
+            const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int dim = 32 * t + c32;
+                const int c0 = dim * TCH + swz<TCH>(dim, 4 * j + g);
+                const int c1 = dim * TCH + swz<TCH>(dim, 4 * j + 2 + g);
+                dvT[t] = mfma32(sDT[c0], pb0, dvT[t]);
+                dvT[t] = mfma32(sDT[c1], pb1, dvT[t]);
+                dkT[t] = mfma32(sQT[c0], db0, dkT[t]);
+                dkT[t] = mfma32(sQT[c1], db1, dkT[t]);
+            }
+        }
+    }
+
+    float *dk = a.dk + (hS + key) * D;
+    float *dv = a.dv + (hS + key) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int dim = 32 * t + 8 * i4 + 4 * g;
+            *reinterpret_cast<float4 *>(dk + dim) = make_float4(dkT[t][4 * i4] * a.scale, dkT[t][4 * i4 + 1] * a.scale,
+                                                                dkT[t][4 * i4 + 2] * a.scale, dkT[t][4 * i4 + 3] * a.scale);
+            *reinterpret_cast<float4 *>(dv + dim) =
+                make_float4(dvT[t][4 * i4], dvT[t][4 * i4 + 1], dvT[t][4 * i4 + 2], dvT[t][4 * i4 + 3]);
+        }
+}
+
+template <int D>
+static size_t dkdv_lds_bytes()
+{
+    return (size_t)(4 * 64 * (D / 8) + 2 * D * 8) * sizeof(uint4) + 2 * 64 * sizeof(float);
+}
+
+template <int D>
+static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
+{
+    const size_t lds = dkdv_lds_bytes<D>();
+    if (lds > 65536)
+        (void)hipFuncSetAttribute((const void *)k_attn_bwd_dkdv<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+    hipLaunchKernelGGL((k_attn_bwd_dkdv<D>), grid, dim3(256), lds, s, a);
+}
+
+hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
+{
+    const unsigned nkb = (unsigned)((pl.S + 127) / 128);
+    const dim3 grid(nkb * pl.H);
+    if (pl.d == 128)
+        launch_dkdv_t<128>(grid, a, s);
+    else
+        launch_dkdv_t<64>(grid, a, s);
+    return hipGetLastError();
+}
+
+// ============================================================== backward: dQ
+// One workgroup per 128 queries (32 per wave); keys are streamed through LDS
+// 64 at a time up to the diagonal. S^T = K Q^T as in the forward, so a lane
+// owns one query:  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
+{
+    constexpr int BM = 128, BN = 64;
+    constexpr int RCH = D / 8, TCH = BN / 8;
+    constexpr int NS = D / 16, NT = D / 32;
+    constexpr int RPT = BN * RCH / 256, TPT = D * TCH / 256;
+    __shared__ uint4 sKh[BN * RCH];
+    __shared__ uint4 sKl[BN * RCH];
+    __shared__ uint4 sV[BN * RCH];
+    __shared__ uint4 sKT[D * TCH];
+
+    const int nqb = (int)((a.S + BM - 1) / BM);
+    const int h = blockIdx.x % a.H;
+    const int qb = nqb - 1 - (int)(blockIdx.x / a.H);
+    const int64_t q0 = (int64_t)qb * BM;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int64_t qw = q0 + wave * 32;
+    const int64_t hS = (int64_t)h * a.S_pad;
+    const int64_t query = qw + c32;
+
+    uint4 qh[NS], ql[NS], dh[NS], dl[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t off = (hS + query) * D + 16 * s + 8 * g;
+        qh[s] = ld16(a.qhi + off);
+        ql[s] = ld16(a.qlo + off);
+        dh[s] = ld16(a.dohi + off);
+        dl[s] = ld16(a.dolo + off);
+    }
+    const bool qok = query < a.S;
+    const float lse2 = qok ? a.lse[hS + query] * LH_LOG2E : 0.0f;
+    const float del = qok ? a.delta[hS + query] : 0.0f;
+    f32x16_t dqT[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        dqT[t] = zero16();
+    const int kap = kappa(c32);
+    const int64_t kend = min(q0 + BM, a.S);
+    const int nkb = (int)((kend + BN - 1) / BN);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int64_t k0 = (int64_t)kb * BN;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int c = tid + 256 * u, r = c / RCH, ch = c % RCH;
+            const int64_t off = (hS + k0 + r) * D + ch * 8;
+            const int at = r * RCH + swz<RCH>(r, ch);
+            sKh[at] = ld16(a.khi + off);
+            sKl[at] = ld16(a.klo + off);
+            sV[at] = ld16(a.v + off);
+        }
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+            const int c = tid + 256 * u, dim = c / TCH, ch = c % TCH;
+            sKT[dim * TCH + swz<TCH>(dim, ch)] = ld16(a.khi_t + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < BN / 32; ++j) {
+            const int64_t kt0 = k0 + 32 * j;
+            if (kt0 > qw + 31)
+                break;
+            const int kl = 32 * j + kap;
+            f32x16_t st = zero16(), dpt = zero16();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int at = kl * RCH + swz<RCH>(kl, 2 * s + g);
+                const uint4 k_h = sKh[at];
+                st = mfma32(k_h, qh[s], st);
+                st = mfma32(sKl[at], qh[s], st);
+                st = mfma32(k_h, ql[s], st);
+                const uint4 vv = sV[at];
+                dpt = mfma32(vv, dh[s], dpt);
+                dpt = mfma32(vv, dl[s], dpt);
+            }
+            float ds[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t kk = kt0 + 16 * (v >> 3) + 8 * g + (v & 7);
+                const bool ok = qok && kk <= query;
+                const float pr = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - lse2) : 0.0f;
+                ds[v] = pr * (dpt[v] - del);
+            }
+            const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int dim = 32 * t + c32;
+                dqT[t] = mfma32(sKT[dim * TCH + swz<TCH>(dim, 4 * j + g)], db0, dqT[t]);
+                dqT[t] = mfma32(sKT[dim * TCH + swz<TCH>(dim, 4 * j + 2 + g)], db1, dqT[t]);
+            }
+        }
+    }
+
+    float *dq = a.dq + (hS + query) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<float4 *>(dq + 32 * t + 8 * i4 + 4 * g) =
+                make_float4(dqT[t][4 * i4] * a.scale, dqT[t][4 * i4 + 1] * a.scale, dqT[t][4 * i4 + 2] * a.scale,
+                            dqT[t][4 * i4 + 3] * a.scale);
+}
+
+hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
+{
+    const unsigned nqb = (unsigned)((pl.S + 127) / 128);
+    const dim3 grid(nqb * pl.H);
+    if (pl.d == 128)
+        hipLaunchKernelGGL((k_attn_bwd_dq<128>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_attn_bwd_dq<64>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace lh

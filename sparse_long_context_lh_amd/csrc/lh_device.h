@@ -1,0 +1,108 @@
+// Device helpers shared by the Lighthouse kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lh.h"
+
+namespace lh {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Two fp32 values to two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two fp32 values to two fp16 (round to nearest even, v_cvt_pk_f16_f32; beyond
+// the fp16 range the result is +-inf), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void unpack_f16x2(uint32_t u, float &lo, float &hi)
+{
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, u);
+    lo = (float)v[0];
+    hi = (float)v[1];
+}
+
+// 8 fp32 values as 8 fp16 (one 16-byte word).
+__device__ __forceinline__ uint4 pack8_f16(const float (&x)[8])
+{
+    return make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7]));
+}
+
+__device__ __forceinline__ void unpack8_f16(uint4 u, float (&x)[8])
+{
+    unpack_f16x2(u.x, x[0], x[1]);
+    unpack_f16x2(u.y, x[2], x[3]);
+    unpack_f16x2(u.z, x[4], x[5]);
+    unpack_f16x2(u.w, x[6], x[7]);
+}
+
+// x = hi + lo with hi = fp16(x) and lo = fp16(x - hi): about 22 significant bits.
+__device__ __forceinline__ void split8_f16(const float (&x)[8], uint4 &hi, uint4 &lo)
+{
+    hi = pack8_f16(x);
+    float h[8], r[8];
+    unpack8_f16(hi, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        r[e] = x[e] - h[e];
+    lo = pack8_f16(r);
+}
+
+// ---------------------------------------------------------------- 8-element row pieces
+// A "piece" is 8 consecutive elements of a row, converted to fp32.
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8])
+{
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+    x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+    x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void load8(const float *p, float (&x)[8])
+{
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(uint16_t *p, const float (&x)[8])
+{
+    uint4 u;
+    u.x = pack_bf16x2(x[0], x[1]); u.y = pack_bf16x2(x[2], x[3]);
+    u.z = pack_bf16x2(x[4], x[5]); u.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4 *>(p) = u;
+}
+
+__device__ __forceinline__ void store8(float *p, const float (&x)[8])
+{
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// Element type tags for the layer's inputs / outputs.
+template <lh_dtype DT> struct Elem;
+template <> struct Elem<LH_BF16> { typedef uint16_t T; };
+template <> struct Elem<LH_F32> { typedef float T; };
+
+} // namespace lh

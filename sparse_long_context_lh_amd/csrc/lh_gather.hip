@@ -1,0 +1,134 @@
+// Gather of the Lighthouse sub-sequence (aitrends summary, 핵심 기여 and
+// 기술 상세 item 3: the chosen (Q, K, V) triples form one contiguous
+// sub-sequence of S entries).
+//
+// One workgroup per 64 consecutive positions of one head. For position s it
+// reads the entry (l, i) the index kernel placed there and fetches its
+// pooled rows: level 0 is the input row itself; a materialised level is
+// copied from the front pass (fp32); any other level is averaged here from
+// its p^l input rows (fp32 sum). Rows go out as fp16, the layouts the
+// attention kernels read as MFMA operands: queries and keys as an fp16 pair
+// (hi = fp16(x), lo = fp16(x - hi)) so the logits keep about 22 bits of the
+// pooled value, values as one fp16; row-major [S_pad][d] and, through an LDS
+// tile, the hi parts transposed [d][S_pad]. Positions past S are zero.
+#include "lh_device.h"
+#include "lh_internal.h"
+
+namespace lh {
+
+constexpr int kGatherTile = 64;
+
+template <int D, lh_dtype DT>
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a)
+{
+    typedef typename Elem<DT>::T T;
+    constexpr int LANES = D / 8;
+    constexpr int NLG = 256 / LANES;
+    constexpr int LD = D + 8; // LDS row pitch in bf16 (16 B pad)
+    __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
+    const int h = blockIdx.y;
+    const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
+    const int lane = threadIdx.x % LANES;
+    const int lg = threadIdx.x / LANES;
+    const T *src[3] = {reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
+                       reinterpret_cast<const T *>(a.v)};
+
+    for (int r = lg; r < kGatherTile; r += NLG) {
+        const int64_t s = s0 + r;
+        const int32_t en = a.ent[(int64_t)h * a.S_pad + s];
+        float x[3][8];
+        // an entry outside the pyramid (never produced by the index kernel) reads as zeros
+        if (en < 0 || (en & 7) >= a.L || (int64_t)(en >> 3) >= a.n[en & 7]) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[t][e] = 0.0f;
+        } else {
+            const int l = en & 7;
+            const int64_t i = (int64_t)(en >> 3);
+            if (l == 0) {
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    load8(src[t] + ((int64_t)h * a.N + i) * D + lane * 8, x[t]);
+            } else if (a.mat_off[l] >= 0) {
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    load8(a.pooled + t * a.tensor_stride + ((int64_t)h * a.mat_rows + a.mat_off[l] + i) * D + lane * 8,
+                          x[t]);
+            } else {
+                const int sh = l * a.log2p;
+                const int64_t w = int64_t(1) << sh;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        x[t][e] = 0.0f;
+                    const T *p0 = src[t] + ((int64_t)h * a.N + (i << sh)) * D + lane * 8;
+                    for (int64_t j = 0; j < w; ++j) {
+                        float y[8];
+                        load8(p0 + j * D, y);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            x[t][e] += y[e];
+                    }
+                    const float inv = 1.0f / (float)w; // exact: power of two
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        x[t][e] *= inv;
+                }
+            }
+        }
+        const int64_t off = ((int64_t)h * a.S_pad + s) * D + lane * 8;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            uint4 hi, lo;
+            if (t < 2) {
+                split8_f16(x[t], hi, lo);
+                *reinterpret_cast<uint4 *>(a.lo[t] + off) = lo;
+            } else {
+                hi = pack8_f16(x[t]);
+            }
+            *reinterpret_cast<uint4 *>(a.hi[t] + off) = hi;
+            *reinterpret_cast<uint4 *>(&tile[t][r * LD + lane * 8]) = hi;
+        }
+    }
+    __syncthreads();
+
+    // Transposed copy: 8 consecutive positions of one dimension per 16-byte store.
+    constexpr int CH = kGatherTile / 8;
+    for (int c = threadIdx.x; c < 3 * D * CH; c += 256) {
+        const int t = c / (D * CH);
+        const int rem = c - t * D * CH;
+        const int dim = rem / CH;
+        const int sc = rem - dim * CH;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = tile[t][(sc * 8 + 2 * e) * LD + dim];
+            const uint32_t hi = tile[t][(sc * 8 + 2 * e + 1) * LD + dim];
+            w[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(a.hi_t[t] + ((int64_t)h * D + dim) * a.S_pad + s0 + sc * 8) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(pl.S_pad / kGatherTile), pl.H);
+    if (pl.d == 128) {
+        if (pl.dt == LH_BF16)
+            hipLaunchKernelGGL((k_gather<128, LH_BF16>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gather<128, LH_F32>), grid, dim3(256), 0, s, a);
+    } else {
+        if (pl.dt == LH_BF16)
+            hipLaunchKernelGGL((k_gather<64, LH_BF16>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gather<64, LH_F32>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+} // namespace lh

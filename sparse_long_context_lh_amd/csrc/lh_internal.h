@@ -1,0 +1,166 @@
+// Host-side plan of one Lighthouse layer call and the argument blocks of its
+// kernels. Everything here is computed on the host from the shape alone, so
+// the launch sequence is static (no device value is ever read back).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lh.h"
+
+namespace lh {
+
+constexpr int kMaxLevels = 8;       // L <= 8
+constexpr int kStratum = 2048;      // entries per top-K stratum
+constexpr int kMaxSelTotal = 16384; // (L-1)*k held in LDS by the index kernel
+constexpr int kSubseqAlign = 256;   // S is padded to this for the attention tiles
+constexpr int64_t kMaxN = int64_t(1) << 27;
+
+// Extra workspace regions that are not exposed through lh_region.
+enum InternalRegion {
+    IR_POOLED = LH_R_COUNT, // fp32 [3][H][mat_rows][d]: materialized pooled levels
+    IR_DOHI,                // fp16 [H][S_pad][d]: hi part of dO_sub
+    IR_DOLO,                // fp16 [H][S_pad][d]: lo part of dO_sub
+    IR_DOHI_T,              // fp16 [H][d][S_pad]: transpose of the hi part
+    IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub)
+    IR_COUNT
+};
+
+struct Plan {
+    int64_t N;
+    int H, d, L, p, log2p, k;
+    lh_dtype dt;
+    int64_t n[kMaxLevels];       // entries at level l
+    int64_t lvl_off[kMaxLevels]; // offset of level l inside one head's score / slot block
+    int64_t lvl_total;           // sum of n[l]
+    int64_t S, S_pad;
+    int C[kMaxLevels];           // strata at level l (l >= 1)
+    int strata_total;            // sum over l >= 1
+    uint32_t mat_mask;           // bit l set: level l pooled rows are written by the front kernel
+    int64_t mat_off[kMaxLevels]; // row offset of a materialized level inside one head's pooled block
+    int64_t mat_rows;
+    int run;                     // rows streamed by one lane group in the front / scatter kernels
+    size_t off[IR_COUNT], bytes[IR_COUNT];
+    size_t total;
+};
+
+// Fills `pl` and returns LH_OK, or the validation error.
+lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, Plan *pl);
+
+// ---------------------------------------------------------------- kernels
+struct FrontArgs {
+    const void *q, *k, *v;
+    float *scores;           // [H][lvl_total]
+    float *pooled;           // [3][H][mat_rows][d]
+    int64_t N, lvl_total, mat_rows, tensor_stride; // tensor_stride = H*mat_rows*d
+    int64_t lvl_off[kMaxLevels];
+    int64_t mat_off[kMaxLevels]; // -1: level not materialized
+    int H, L, log2p, run, runs_per_head;
+};
+
+struct TopkArgs {
+    const float *scores; // [H][lvl_total]
+    int32_t *sel;        // [H][L-1][k]
+    int32_t *slot;       // [H][lvl_total]
+    int64_t lvl_total;
+    int64_t lvl_off[kMaxLevels];
+    int64_t n[kMaxLevels];
+    int C[kMaxLevels];
+    int strata_before[kMaxLevels]; // strata of levels 1..l-1
+    int L, log2p, k;
+};
+
+struct IndexArgs {
+    const int32_t *sel;  // [H][L-1][k]
+    int32_t *slot;       // [H][lvl_total]
+    int32_t *ent;        // [H][S_pad]
+    int64_t lvl_total, S, S_pad;
+    int64_t lvl_off[kMaxLevels];
+    int64_t n[kMaxLevels];
+    int L, log2p, k;
+};
+
+struct GatherArgs {
+    const void *q, *k, *v;     // [H][N][d] inputs
+    const float *pooled;       // [3][H][mat_rows][d]
+    const int32_t *ent;        // [H][S_pad]
+    uint16_t *hi[3];           // fp16 [H][S_pad][d]: Q hi, K hi, V
+    uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
+    uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
+    int64_t N, S, S_pad, mat_rows, tensor_stride;
+    int64_t mat_off[kMaxLevels];
+    int64_t n[kMaxLevels];
+    int H, L, log2p;
+};
+
+struct AttnFwdArgs {
+    const uint16_t *qhi, *qlo, *khi, *klo, *vt; // fp16 gathered rows (vt: [H][d][S_pad])
+    float *o;                           // [H][S_pad][d]
+    float *lse;                         // [H][S_pad]
+    int64_t S, S_pad;
+    int H;
+    float scale_log2; // log2(e) / sqrt(d)
+};
+
+struct AttnBwdArgs {
+    const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
+    const uint16_t *qhi_t, *khi_t;              // fp16 [H][d][S_pad]
+    const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
+    const float *lse, *delta;                        // [H][S_pad]
+    float *dq, *dk, *dv;                             // [H][S_pad][d]
+    int64_t S, S_pad;
+    int H;
+    float scale_log2; // log2(e) / sqrt(d)
+    float scale;      // 1 / sqrt(d)
+};
+
+struct ScatterArgs {
+    const float *osub;   // [H][S_pad][d]
+    const int32_t *slot; // [H][lvl_total]
+    void *out;           // [H][N][d] in the input dtype
+    int64_t N, lvl_total, S_pad;
+    int64_t lvl_off[kMaxLevels];
+    int H, L, log2p;
+};
+
+struct ScatterBwdArgs {
+    const void *dout;    // [H][N][d] in the input dtype
+    const int32_t *slot; // [H][lvl_total]
+    float *dosub;        // [H][S_pad][d]
+    int64_t N, lvl_total, S_pad;
+    int64_t lvl_off[kMaxLevels];
+    int H, L, log2p, run, tiles_per_head;
+};
+
+struct BwdPrepArgs {
+    const float *dosub, *osub;       // [H][S_pad][d]
+    uint16_t *dohi, *dolo, *dohi_t;  // fp16 pair, and the hi transpose
+    float *delta;              // [H][S_pad]
+    int64_t S, S_pad;
+    int H;
+};
+
+struct PoolBwdArgs {
+    const float *dsub[3];  // [H][S_pad][d]: dQ_sub, dK_sub, dV_sub
+    const int32_t *slot;   // [H][lvl_total]
+    void *dx[3];           // [H][N][d] in the input dtype
+    int64_t N, lvl_total, S_pad;
+    int64_t lvl_off[kMaxLevels];
+    int H, L, log2p;
+};
+
+hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s);
+hipError_t launch_topk(const Plan &pl, const TopkArgs &a, hipStream_t s);
+hipError_t launch_index(const Plan &pl, const IndexArgs &a, hipStream_t s);
+hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s);
+hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s);
+hipError_t launch_scatter(const Plan &pl, const ScatterArgs &a, hipStream_t s);
+hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s);
+hipError_t launch_bwd_prep(const Plan &pl, const BwdPrepArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_t s);
+hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s);
+hipError_t launch_pool_bwd(const Plan &pl, const PoolBwdArgs &a, hipStream_t s);
+hipError_t launch_selftest_sqrt(uint32_t first, uint32_t count, uint32_t *mismatches, hipStream_t s);
+
+} // namespace lh

@@ -1,0 +1,107 @@
+"""GPU parity of the whole Lighthouse path against the CPU oracle, at sizes the
+oracle finishes in seconds: several tiles per kernel, ragged sub-sequence
+tails, every dtype / head size, and the method's degenerate cases. Calls go
+through the C ABI (liblh.so via ctypes)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_context_lh_amd as lh
+from parity import GpuRun, check_case, say
+from synth_inputs import make_dout, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(N, H, d, L, p, k, dtype=torch.bfloat16, n_plant=8, seed=0, bwd=False, heads=None, tag=""):
+    say("case %s: N=%d H=%d d=%d L=%d p=%d k=%d dtype=%s S=%d bwd=%s"
+        % (tag, N, H, d, L, p, k, dtype, oracle.subseq_len(N, L, p, k), bwd))
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, dtype, n_plant, seed))
+    dout = make_dout(N, H, d, dtype, seed + 1).cuda() if bwd else None
+    return check_case(q, kk, v, L, p, k, dout, heads=heads, tag=tag)
+
+
+def test_sqrt_correctly_rounded_all_positive_floats():
+    # every positive finite fp32 value, in two launches
+    bad = lh.selftest_sqrt(1, 0x40000000) + lh.selftest_sqrt(0x40000001, 0x7f800000 - 0x40000001)
+    assert bad == 0
+
+
+def test_fp32_d64_small_workload():
+    # the 4K fp32 workload itself: N=4096, H=4, d=64, L=3, p=2, k=256 (S=2048)
+    _case(4096, 4, 64, 3, 2, 256, torch.float32, n_plant=0, tag="fp32-4k")
+
+
+def test_bf16_d128_p2_strata_ragged():
+    # level 1 has 4 strata, level 2 has 2; S = 4096 + 2*2*300 = 5296 (ragged tail)
+    _case(16384, 2, 128, 3, 2, 300, tag="p2-strata")
+
+
+def test_bf16_d128_p4_L4_ragged():
+    _case(32768, 2, 128, 4, 4, 100, n_plant=32, tag="p4-L4")
+
+
+def test_bf16_d64_p8():
+    _case(8192, 2, 64, 3, 8, 100, tag="p8")
+
+
+def test_backward_p4_L3():
+    _case(8192, 2, 128, 3, 4, 50, bwd=True, tag="bwd-p4")
+
+
+def test_backward_p2_d64_fp32():
+    _case(4096, 2, 64, 3, 2, 200, torch.float32, n_plant=0, bwd=True, tag="bwd-fp32")
+
+
+def test_backward_L5_p4_shape_of_512k():
+    # the 512K workload's pyramid (L=5, p=4) at N=32K: S = 128 + 4*4*32 = 640
+    _case(32768, 2, 128, 5, 4, 32, n_plant=32, bwd=True, tag="bwd-L5")
+
+
+def test_dense_L1_fwd_bwd_ragged():
+    # L = 1: S = N, dense causal attention; N = 1000 is not a multiple of any tile
+    _case(1000, 2, 64, 1, 2, 0, bwd=True, tag="L1")
+
+
+def test_k0_only_top_level():
+    _case(4096, 2, 128, 3, 2, 0, bwd=True, tag="k0")
+
+
+def test_everything_selected():
+    # L = 2, k = n_1: the whole pyramid is gathered (S = N + N/p)
+    _case(2048, 2, 64, 2, 2, 1024, bwd=True, tag="all")
+
+
+def test_ties_take_lowest_index():
+    # every row equal: all scores tie, each stratum keeps its lowest indices
+    N, H, d, L, p, k = 16384, 1, 128, 3, 2, 77
+    row = torch.randn(d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    q = row.expand(H, N, d).contiguous().cuda()
+    run = GpuRun(q, q, q, L, p, k)
+    sel = run.head("sel", 0).numpy()
+    for l in (1, 2):
+        want = oracle.stratified_topk(np.ones(N // p ** l, dtype=np.float32), k)
+        assert np.array_equal(sel[l - 1], want)
+    res = oracle.forward(q[0].float().cpu().numpy(), q[0].float().cpu().numpy(), q[0].float().cpu().numpy(), L, p, k)
+    assert np.array_equal(sel[0], res["sel"][1]) and np.array_equal(sel[1], res["sel"][2])
+
+
+def test_deterministic_bitwise():
+    N, H, d, L, p, k = 16384, 2, 128, 3, 4, 200
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 8, 5))
+    dout = make_dout(N, H, d, torch.bfloat16, 6).cuda()
+    a = GpuRun(q, kk, v, L, p, k, dout)
+    b = GpuRun(q, kk, v, L, p, k, dout)
+    assert torch.equal(a.out, b.out)
+    for x, y in zip(a.grads, b.grads):
+        assert torch.equal(x, y)
+
+
+def test_heads_are_independent():
+    # head h of an H-head call equals a 1-head call on head h alone
+    N, H, d, L, p, k = 8192, 3, 128, 3, 2, 64
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 8, 7))
+    full = GpuRun(q, kk, v, L, p, k)
+    one = GpuRun(q[1:2].contiguous(), kk[1:2].contiguous(), v[1:2].contiguous(), L, p, k)
+    assert torch.equal(full.out[1], one.out[0])
