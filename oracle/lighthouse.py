@@ -246,6 +246,12 @@ def gather(x: np.ndarray, ent_level: np.ndarray, ent_index: np.ndarray, p: int) 
     return out
 
 
+def _future(S: int) -> np.ndarray:
+    """Boolean [S, S] mask of the pairs (a, b) with b > a (key after query)."""
+    idx = np.arange(S)
+    return idx[None, :] > idx[:, None]
+
+
 def attention(qt: np.ndarray, kt: np.ndarray, vt: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Dense causal softmax attention over the sub-sequence, scale 1/sqrt(d).
 
@@ -255,7 +261,7 @@ def attention(qt: np.ndarray, kt: np.ndarray, vt: np.ndarray) -> tuple[np.ndarra
     """
     S, d = qt.shape
     logits = (qt @ kt.T) / np.sqrt(d)
-    logits[np.triu_indices(S, 1)] = -np.inf
+    logits[_future(S)] = -np.inf
     m = logits.max(axis=1, keepdims=True)
     np.subtract(logits, m, out=logits)
     np.exp(logits, out=logits)
@@ -341,7 +347,7 @@ def attention_bwd(qt, kt, vt, lse, dot):
     prob = (qt @ kt.T) * scale
     np.subtract(prob, lse[:, None], out=prob)
     np.exp(prob, out=prob)
-    prob[np.triu_indices(S, 1)] = 0.0
+    prob[_future(S)] = 0.0
     dvt = prob.T @ dot
     dprob = dot @ vt.T
     row = (prob * dprob).sum(axis=1, keepdims=True)

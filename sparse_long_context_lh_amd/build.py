@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -24,6 +25,18 @@ FLAGS = [
     # packed fp32 VALU ops stay off: hipcc must not emit v_pk_{add,mul,fma}_f32.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+
+def source_digest() -> str:
+    """SHA-256 over every source and header under csrc/ and include/ (names and bytes)."""
+    h = hashlib.sha256()
+    inc = os.path.join(os.path.dirname(HERE), "include")
+    for d in (CSRC, inc):
+        for name in sorted(os.listdir(d)):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def _compile(src: str) -> str:
