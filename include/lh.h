@@ -155,7 +155,9 @@ lh_status lh_backward_timed(const void *dout,
  *   LH_R_V       fp16  [H][S_pad][d]   gathered value rows
  *   LH_R_QHI_T/KHI_T/V_T fp16 [H][d][S_pad]  transposes of QHI, KHI, V
  *   LH_R_OSUB    fp32  [H][S_pad][d]   attention output of the sub-sequence
- *   LH_R_LSE     fp32  [H][S_pad]      its natural-log row log-sum-exp
+ *   LH_R_LSE     fp32  [H][S_pad]      its row log-sum-exp in the log2 domain:
+ *                                      log2 sum_b 2^(log2(e) q.k_b / sqrt(d))
+ *                                      (the natural-log value times log2(e))
  *   LH_R_DOSUB   fp32  [H][S_pad][d]   gradient at the sub-sequence output
  *   LH_R_DQSUB/DKSUB/DVSUB fp32 [H][S_pad][d]  gradients at the gathered rows
  * S_pad = S rounded up to a multiple of 256. Returns LH_EINVAL for a bad shape

@@ -23,19 +23,31 @@
 //
 // Precision: a logit is the sum of three products, q_hi.k_hi + q_hi.k_lo +
 // q_lo.k_hi, over fp16 pairs x = hi + lo of the gathered rows; dP uses the
-// fp16 pair of dO_sub (two products). P, dS, V, dO_sub's hi part and the
-// query / key hi parts of the gradient products are single fp16 operands.
+// fp16 pair of dO_sub (two products); the forward's P.V uses an fp16 pair of
+// P (two products), so O_sub, and with it delta = rowsum(dO_sub * O_sub),
+// agree with the P the backward recomputes (dS = P (dP - delta) cancels
+// heavily when |dO_sub| is large). dS, V, the backward's P, dO_sub's hi part
+// and the query / key hi parts of the gradient products are single fp16
+// operands.
 //
 // The backward is split into a dK/dV kernel (one workgroup per 128 keys) and a
 // dQ kernel (one workgroup per 128 queries) so that no gradient needs atomics
 // and results are bitwise reproducible.
+//
+// Range: probabilities enter fp16 products multiplied by 2^15 (kPScale), so
+// the many tiny probabilities of a long, sharply peaked row do not underflow
+// fp16 (they would vanish from P.V but stay in the fp32 normaliser, and the
+// resulting O_sub error is amplified by delta); the scale cancels against the
+// normaliser (forward) or is divided out of dV (backward). The log-sum-exp is
+// kept in the log2 domain of the scaled logits, as the backward uses it.
 #include "lh_device.h"
 #include "lh_internal.h"
 
 namespace lh {
 
-#define LH_LOG2E 1.4426950408889634f
-#define LH_LN2 0.6931471805599453f
+// exp2 offset and factor applied to probabilities before they become fp16
+constexpr float kPScaleLog2 = 15.0f;
+constexpr float kPScaleInv = 1.0f / 32768.0f;
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c)
 {
@@ -170,17 +182,41 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
                 for (int v = 0; v < 16; ++v)
                     o[t][v] *= alpha;
             float pr[16];
+            const float shift = mn - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                pr[v] = __builtin_amdgcn_exp2f(y[v] - mn);
-                lsum += pr[v];
+            for (int v = 0; v < 16; ++v)
+                pr[v] = __builtin_amdgcn_exp2f(y[v] - shift);
+            // The tile's 16 probabilities are summed first (pairwise) and then
+            // added to the running sum: added one by one, probabilities far
+            // below the running sum's half-ulp would all be rounded away, a
+            // systematic loss in the normaliser that the backward's
+            // dS = P (dP - delta) amplifies.
+            float t8[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                t8[v] = pr[v] + pr[v + 8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                t8[v] += t8[v + 4];
+            lsum += (t8[0] + t8[2]) + (t8[1] + t8[3]);
+            uint4 ph[2], pl[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                float x8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x8[e] = pr[8 * hh + e];
+                split8_f16(x8, ph[hh], pl[hh]);
             }
-            const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int dim = 32 * t + c32;
-                o[t] = mfma32(sV[dim * VCH + swz<VCH>(dim, 4 * j + g)], pb0, o[t]);
-                o[t] = mfma32(sV[dim * VCH + swz<VCH>(dim, 4 * j + 2 + g)], pb1, o[t]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint4 vv = sV[dim * VCH + swz<VCH>(dim, 4 * j + 2 * hh + g)];
+                    o[t] = mfma32(vv, ph[hh], o[t]);
+                    o[t] = mfma32(vv, pl[hh], o[t]);
+                }
             }
         }
     }
@@ -195,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
             *reinterpret_cast<float4 *>(orow + 32 * t + 8 * i4 + 4 * g) =
                 make_float4(o[t][4 * i4] * inv, o[t][4 * i4 + 1] * inv, o[t][4 * i4 + 2] * inv, o[t][4 * i4 + 3] * inv);
     if (g == 0)
-        a.lse[hS + qw + c32] = (m + __log2f(ltot)) * LH_LN2;
+        a.lse[hS + qw + c32] = m + (__log2f(ltot) - kPScaleLog2); // log2 domain
 }
 
 hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
@@ -278,7 +314,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
         }
         if (tid < BQ) {
             const int64_t q = q0 + tid;
-            sL[tid] = q < a.S ? a.lse[hS + q] * LH_LOG2E : 0.0f;
+            sL[tid] = q < a.S ? a.lse[hS + q] : 0.0f;
             sDel[tid] = q < a.S ? a.delta[hS + q] : 0.0f;
         }
         __syncthreads();
@@ -305,8 +341,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
                 const int qi = 32 * j + 16 * (v >> 3) + 8 * g + (v & 7);
                 const int64_t q = q0 + qi;
                 const bool ok = q >= key && q < a.S;
-                pr[v] = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
-                ds[v] = pr[v] * (dp[v] - sDel[qi]);
+                const float pv = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
+                ds[v] = pv * (dp[v] - sDel[qi]);
+                pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
             }
             const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
             const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
@@ -333,7 +370,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
             *reinterpret_cast<float4 *>(dk + dim) = make_float4(dkT[t][4 * i4] * a.scale, dkT[t][4 * i4 + 1] * a.scale,
                                                                 dkT[t][4 * i4 + 2] * a.scale, dkT[t][4 * i4 + 3] * a.scale);
             *reinterpret_cast<float4 *>(dv + dim) =
-                make_float4(dvT[t][4 * i4], dvT[t][4 * i4 + 1], dvT[t][4 * i4 + 2], dvT[t][4 * i4 + 3]);
+                make_float4(dvT[t][4 * i4] * kPScaleInv, dvT[t][4 * i4 + 1] * kPScaleInv,
+                            dvT[t][4 * i4 + 2] * kPScaleInv, dvT[t][4 * i4 + 3] * kPScaleInv);
         }
 }
 
@@ -399,7 +437,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
         dl[s] = ld16(a.dolo + off);
     }
     const bool qok = query < a.S;
-    const float lse2 = qok ? a.lse[hS + query] * LH_LOG2E : 0.0f;
+    const float lse2 = qok ? a.lse[hS + query] : 0.0f;
     const float del = qok ? a.delta[hS + query] : 0.0f;
     f32x16_t dqT[NT];
 #pragma unroll
