@@ -245,28 +245,54 @@ hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// ============================================================== async staging
+// global_load_lds_dwordx4: each lane fetches 16 bytes from its own global
+// address and the wave writes them to LDS at base + 16 * lane (base uniform
+// over the wave). A stage is a list of 16-byte LDS chunks; chunk c of a round
+// is handled by thread c % 256. The XOR swizzle of a tile is applied by
+// choosing which global chunk lands in each physical LDS chunk. No registers
+// hold the data, so the next stage's loads overlap the current stage's math.
+__device__ __forceinline__ void async16(const void *g, const uint4 *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
+                                     (void __attribute__((address_space(3))) *)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Generic swizzle for NCH chunks per row: rows per 256-byte bank window are
+// 16/NCH; XOR the chunk with the window index so 16 consecutive rows map the
+// same logical chunk to 16 distinct bank groups.
+template <int NCH>
+__device__ __forceinline__ int swzg(int row, int ch)
+{
+    return ch ^ ((row / (16 / NCH)) & (NCH - 1));
+}
+
 // ============================================================== backward: dK, dV
-// One workgroup per 128 keys (32 per wave); queries are streamed through LDS
-// 64 at a time from the key block onwards. S = Q K^T with queries as
-// (permuted) rows, so a lane owns one key:
+// One workgroup per 128 keys (32 per wave, K/V rows in registers); queries
+// stream through LDS 32 at a time from the key block onwards, double-buffered.
+// S = Q K^T with queries as (permuted) rows, so a lane owns one key:
 //   dV^T += dO^T P,  dP = dO V^T,  dS = P * (dP - delta),  dK^T += Q^T dS.
+template <int D>
+struct DkdvStage {
+    static constexpr int BQ = 32;
+    static constexpr int RCH = D / 8;  // chunks per row-major row
+    static constexpr int TCH = BQ / 8; // chunks per transposed row
+    static constexpr int ROWS = BQ * RCH;
+    static constexpr int COLS = D * TCH;
+    static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS, QT = 4 * ROWS, DT = 4 * ROWS + COLS;
+    static constexpr int LS = 4 * ROWS + 2 * COLS; // lse (BQ floats), then delta (BQ floats)
+    static constexpr int SIZE = LS + BQ / 2;        // in 16-byte chunks
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
-    constexpr int BK = 128, BQ = 64;
-    constexpr int RCH = D / 8;  // chunks per row-major row
-    constexpr int TCH = BQ / 8; // chunks per transposed row
+    typedef DkdvStage<D> St;
+    constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
-    constexpr int RPT = BQ * RCH / 256, TPT = D * TCH / 256;
-    extern __shared__ uint4 lds_dkdv[];
-    uint4 *sQh = lds_dkdv;         // [BQ][RCH]
-    uint4 *sQl = sQh + BQ * RCH;   // [BQ][RCH]
-    uint4 *sDh = sQl + BQ * RCH;   // [BQ][RCH]
-    uint4 *sDl = sDh + BQ * RCH;   // [BQ][RCH]
-    uint4 *sQT = sDl + BQ * RCH;   // [D][TCH]
-    uint4 *sDT = sQT + D * TCH;    // [D][TCH]
-    float *sL = reinterpret_cast<float *>(sDT + D * TCH); // [BQ] lse * log2(e)
-    float *sDel = sL + BQ;                                 // [BQ] delta
+    extern __shared__ uint4 lds_dkdv[]; // two stages
 
     const int h = blockIdx.x % a.H;
     const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
@@ -275,6 +301,32 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
     const int64_t kw = k0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
     const int64_t key = kw + c32;
+
+    // Issue the loads of the stage whose first query is q0 into buffer `buf`.
+    auto issue = [&](int64_t q0, int buf) {
+        const uint4 *base = lds_dkdv + buf * St::SIZE;
+#pragma unroll
+        for (int u = 0; u < St::LS / 256; ++u) {
+            const int c = 256 * u + tid;
+            const uint4 *wb = base + 256 * u + 64 * wave;
+            const void *src;
+            if (c < St::QT) { // row-major tiles
+                const int t = c / St::ROWS, cc = c % St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
+                const uint16_t *arr = t == 0 ? a.qhi : t == 1 ? a.qlo : t == 2 ? a.dohi : a.dolo;
+                src = arr + (hS + q0 + r) * D + ch * 8;
+            } else { // transposed tiles
+                const int t = (c - St::QT) / St::COLS, cc = (c - St::QT) % St::COLS, dim = cc / TCH;
+                const int ch = swzg<TCH>(dim, cc % TCH);
+                const uint16_t *arr = t == 0 ? a.qhi_t : a.dohi_t;
+                src = arr + ((int64_t)h * D + dim) * a.S_pad + q0 + ch * 8;
+            }
+            async16(src, wb);
+        }
+        if (tid < BQ / 2) { // 8 chunks of lse, 8 of delta (wave 0)
+            const float *arr = tid < BQ / 4 ? a.lse : a.delta;
+            async16(arr + hS + q0 + 4 * (tid % (BQ / 4)), base + St::LS);
+        }
+    };
 
     uint4 kh[NS], kl[NS], vf[NS];
 #pragma unroll
@@ -290,73 +342,53 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
         dvT[t] = zero16();
         dkT[t] = zero16();
     }
-    const int qap = kappa(c32);
+    const int ql = kappa(c32);
+    const int nst = (int)((a.S - k0 + BQ - 1) / BQ);
 
-    for (int64_t q0 = k0; q0 < a.S; q0 += BQ) {
-        __syncthreads();
+    issue(k0, 0);
+    for (int it = 0; it < nst; ++it) {
+        const int64_t q0 = k0 + (int64_t)it * BQ;
+        wait_async();
+        __syncthreads(); // this stage landed everywhere; the other buffer is free
+        if (it + 1 < nst)
+            issue(q0 + BQ, (it + 1) & 1);
+        if (q0 + 31 < kw)
+            continue; // every query of the stage precedes this wave's keys
+        const uint4 *base = lds_dkdv + (it & 1) * St::SIZE;
+        const float *sL = reinterpret_cast<const float *>(base + St::LS);
+        const float *sDel = sL + BQ;
+        f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int c = tid + 256 * u, r = c / RCH, ch = c % RCH;
-            const int64_t off = (hS + q0 + r) * D + ch * 8;
-            const int at = r * RCH + swz<RCH>(r, ch);
-            sQh[at] = ld16(a.qhi + off);
-            sQl[at] = ld16(a.qlo + off);
-            sDh[at] = ld16(a.dohi + off);
-            sDl[at] = ld16(a.dolo + off);
+        for (int s = 0; s < NS; ++s) {
+            const int at = ql * RCH + swzg<RCH>(ql, 2 * s + g);
+            const uint4 q_h = base[St::QH + at];
+            st = mfma32(q_h, kh[s], st);
+            st = mfma32(base[St::QL + at], kh[s], st);
+            st = mfma32(q_h, kl[s], st);
+            dp = mfma32(base[St::DH + at], vf[s], dp);
+            dp = mfma32(base[St::DL + at], vf[s], dp);
         }
+        float pr[16], ds[16];
 #pragma unroll
-        for (int u = 0; u < TPT; ++u) {
-            const int c = tid + 256 * u, dim = c / TCH, ch = c % TCH;
-            const int64_t off = ((int64_t)h * D + dim) * a.S_pad + q0 + ch * 8;
-            const int at = dim * TCH + swz<TCH>(dim, ch);
-            sQT[at] = ld16(a.qhi_t + off);
-            sDT[at] = ld16(a.dohi_t + off);
+        for (int v = 0; v < 16; ++v) {
+            const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
+            const int64_t q = q0 + qi;
+            const bool ok = q >= key && q < a.S;
+            const float pv = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
+            ds[v] = ok ? pv * (dp[v] - sDel[qi]) : 0.0f;
+            pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
         }
-        if (tid < BQ) {
-            const int64_t q = q0 + tid;
-            sL[tid] = q < a.S ? a.lse[hS + q] : 0.0f;
-            sDel[tid] = q < a.S ? a.delta[hS + q] : 0.0f;
-        }
-        __syncthreads();
+        const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
+        const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
 #pragma unroll
-        for (int j = 0; j < BQ / 32; ++j) {
-            const int64_t qt0 = q0 + 32 * j;
-            if (qt0 + 31 < kw || qt0 >= a.S)
-                continue; // every query of the tile precedes this wave's keys, or is padding
-            const int ql = 32 * j + qap;
-            f32x16_t st = zero16(), dp = zero16();
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int at = ql * RCH + swz<RCH>(ql, 2 * s + g);
-                const uint4 q_h = sQh[at];
-                st = mfma32(q_h, kh[s], st);
-                st = mfma32(sQl[at], kh[s], st);
-                st = mfma32(q_h, kl[s], st);
-                dp = mfma32(sDh[at], vf[s], dp);
-                dp = mfma32(sDl[at], vf[s], dp);
-            }
-            float pr[16], ds[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 32 * j + 16 * (v >> 3) + 8 * g + (v & 7);
-                const int64_t q = q0 + qi;
-                const bool ok = q >= key && q < a.S;
-                const float pv = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
-                ds[v] = pv * (dp[v] - sDel[qi]);
-                pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
-            }
-            const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
-            const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int dim = 32 * t + c32;
-                const int c0 = dim * TCH + swz<TCH>(dim, 4 * j + g);
-                const int c1 = dim * TCH + swz<TCH>(dim, 4 * j + 2 + g);
-                dvT[t] = mfma32(sDT[c0], pb0, dvT[t]);
-                dvT[t] = mfma32(sDT[c1], pb1, dvT[t]);
-                dkT[t] = mfma32(sQT[c0], db0, dkT[t]);
-                dkT[t] = mfma32(sQT[c1], db1, dkT[t]);
-            }
+        for (int t = 0; t < NT; ++t) {
+            const int dim = 32 * t + c32;
+            const int c0 = dim * TCH + swzg<TCH>(dim, g);
+            const int c1 = dim * TCH + swzg<TCH>(dim, 2 + g);
+            dvT[t] = mfma32(base[St::DT + c0], pb0, dvT[t]);
+            dvT[t] = mfma32(base[St::DT + c1], pb1, dvT[t]);
+            dkT[t] = mfma32(base[St::QT + c0], db0, dkT[t]);
+            dkT[t] = mfma32(base[St::QT + c1], db1, dkT[t]);
         }
     }
 
@@ -376,15 +408,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
 }
 
 template <int D>
-static size_t dkdv_lds_bytes()
-{
-    return (size_t)(4 * 64 * (D / 8) + 2 * D * 8) * sizeof(uint4) + 2 * 64 * sizeof(float);
-}
-
-template <int D>
 static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
 {
-    const size_t lds = dkdv_lds_bytes<D>();
+    const size_t lds = 2 * (size_t)DkdvStage<D>::SIZE * sizeof(uint4);
     if (lds > 65536)
         (void)hipFuncSetAttribute((const void *)k_attn_bwd_dkdv<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
@@ -403,20 +429,26 @@ hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_
 }
 
 // ============================================================== backward: dQ
-// One workgroup per 128 queries (32 per wave); keys are streamed through LDS
-// 64 at a time up to the diagonal. S^T = K Q^T as in the forward, so a lane
-// owns one query:  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
+// One workgroup per 128 queries (32 per wave, Q and dO_sub in registers); keys
+// stream through LDS 64 at a time up to the diagonal, double-buffered.
+// S^T = K Q^T as in the forward, so a lane owns one query:
+//   dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
+template <int D>
+struct DqStage {
+    static constexpr int BN = 64;
+    static constexpr int RCH = D / 8, TCH = BN / 8;
+    static constexpr int ROWS = BN * RCH, COLS = D * TCH;
+    static constexpr int KH = 0, KL = ROWS, VV = 2 * ROWS, KT = 3 * ROWS;
+    static constexpr int SIZE = 3 * ROWS + COLS;
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
 {
-    constexpr int BM = 128, BN = 64;
-    constexpr int RCH = D / 8, TCH = BN / 8;
+    typedef DqStage<D> St;
+    constexpr int BM = 128, BN = St::BN, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
-    constexpr int RPT = BN * RCH / 256, TPT = D * TCH / 256;
-    __shared__ uint4 sKh[BN * RCH];
-    __shared__ uint4 sKl[BN * RCH];
-    __shared__ uint4 sV[BN * RCH];
-    __shared__ uint4 sKT[D * TCH];
+    extern __shared__ uint4 lds_dq[]; // two stages
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -426,6 +458,25 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
     const int64_t qw = q0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
     const int64_t query = qw + c32;
+
+    auto issue = [&](int64_t k0, int buf) {
+        const uint4 *base = lds_dq + buf * St::SIZE;
+#pragma unroll
+        for (int u = 0; u < St::SIZE / 256; ++u) {
+            const int c = 256 * u + tid;
+            const uint4 *wb = base + 256 * u + 64 * wave;
+            const void *src;
+            if (c < St::KT) {
+                const int t = c / St::ROWS, cc = c % St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
+                const uint16_t *arr = t == 0 ? a.khi : t == 1 ? a.klo : a.v;
+                src = arr + (hS + k0 + r) * D + ch * 8;
+            } else {
+                const int cc = c - St::KT, dim = cc / TCH, ch = swzg<TCH>(dim, cc % TCH);
+                src = a.khi_t + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8;
+            }
+            async16(src, wb);
+        }
+    };
 
     uint4 qh[NS], ql[NS], dh[NS], dl[NS];
 #pragma unroll
@@ -447,24 +498,14 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
 
+    issue(0, 0);
     for (int kb = 0; kb < nkb; ++kb) {
         const int64_t k0 = (int64_t)kb * BN;
+        wait_async();
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int c = tid + 256 * u, r = c / RCH, ch = c % RCH;
-            const int64_t off = (hS + k0 + r) * D + ch * 8;
-            const int at = r * RCH + swz<RCH>(r, ch);
-            sKh[at] = ld16(a.khi + off);
-            sKl[at] = ld16(a.klo + off);
-            sV[at] = ld16(a.v + off);
-        }
-#pragma unroll
-        for (int u = 0; u < TPT; ++u) {
-            const int c = tid + 256 * u, dim = c / TCH, ch = c % TCH;
-            sKT[dim * TCH + swz<TCH>(dim, ch)] = ld16(a.khi_t + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8);
-        }
-        __syncthreads();
+        if (kb + 1 < nkb)
+            issue(k0 + BN, (kb + 1) & 1);
+        const uint4 *base = lds_dq + (kb & 1) * St::SIZE;
 #pragma unroll
         for (int j = 0; j < BN / 32; ++j) {
             const int64_t kt0 = k0 + 32 * j;
@@ -474,12 +515,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
             f32x16_t st = zero16(), dpt = zero16();
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int at = kl * RCH + swz<RCH>(kl, 2 * s + g);
-                const uint4 k_h = sKh[at];
+                const int at = kl * RCH + swzg<RCH>(kl, 2 * s + g);
+                const uint4 k_h = base[St::KH + at];
                 st = mfma32(k_h, qh[s], st);
-                st = mfma32(sKl[at], qh[s], st);
+                st = mfma32(base[St::KL + at], qh[s], st);
                 st = mfma32(k_h, ql[s], st);
-                const uint4 vv = sV[at];
+                const uint4 vv = base[St::VV + at];
                 dpt = mfma32(vv, dh[s], dpt);
                 dpt = mfma32(vv, dl[s], dpt);
             }
@@ -489,14 +530,14 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
                 const int64_t kk = kt0 + 16 * (v >> 3) + 8 * g + (v & 7);
                 const bool ok = qok && kk <= query;
                 const float pr = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - lse2) : 0.0f;
-                ds[v] = pr * (dpt[v] - del);
+                ds[v] = ok ? pr * (dpt[v] - del) : 0.0f;
             }
             const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int dim = 32 * t + c32;
-                dqT[t] = mfma32(sKT[dim * TCH + swz<TCH>(dim, 4 * j + g)], db0, dqT[t]);
-                dqT[t] = mfma32(sKT[dim * TCH + swz<TCH>(dim, 4 * j + 2 + g)], db1, dqT[t]);
+                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + g)], db0, dqT[t]);
+                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + 2 + g)], db1, dqT[t]);
             }
         }
     }
@@ -511,14 +552,24 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
                             dqT[t][4 * i4 + 3] * a.scale);
 }
 
+template <int D>
+static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
+{
+    const size_t lds = 2 * (size_t)DqStage<D>::SIZE * sizeof(uint4);
+    if (lds > 65536)
+        (void)hipFuncSetAttribute((const void *)k_attn_bwd_dq<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+    hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), lds, s, a);
+}
+
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
 {
     const unsigned nqb = (unsigned)((pl.S + 127) / 128);
     const dim3 grid(nqb * pl.H);
     if (pl.d == 128)
-        hipLaunchKernelGGL((k_attn_bwd_dq<128>), grid, dim3(256), 0, s, a);
+        launch_dq_t<128>(grid, a, s);
     else
-        hipLaunchKernelGGL((k_attn_bwd_dq<64>), grid, dim3(256), 0, s, a);
+        launch_dq_t<64>(grid, a, s);
     return hipGetLastError();
 }
 
