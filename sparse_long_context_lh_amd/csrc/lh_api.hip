@@ -70,6 +70,8 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     const int64_t pk = (int64_t)pl->p * pl->k;
     pl->S = pl->n[L - 1] + (int64_t)(L - 1) * pk;
     pl->S_pad = (int64_t)round_up((size_t)pl->S, kSubseqAlign);
+    if (pl->S_pad * d > (int64_t(1) << 30))
+        return LH_EUNSUPPORTED; // attention kernels address a head's sub-sequence with 32-bit offsets
 
     // Pooled levels the front pass writes (fp32 rows): the top level (gathered
     // whole) and every middle level whose full write plus the gathered reads

@@ -284,58 +284,82 @@ struct DkdvStage {
     static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS, QT = 4 * ROWS, DT = 4 * ROWS + COLS;
     static constexpr int LS = 4 * ROWS + 2 * COLS; // lse (BQ floats), then delta (BQ floats)
     static constexpr int SIZE = LS + BQ / 2;        // in 16-byte chunks
+    static constexpr int KLO = 2 * SIZE;            // after the two stages: the block's K lo rows [128][RCH]
+    static constexpr int TOTAL = KLO + 128 * RCH;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     typedef DkdvStage<D> St;
     constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
+    constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
     extern __shared__ uint4 lds_dkdv[]; // two stages
 
     const int h = blockIdx.x % a.H;
     const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
-    const int64_t k0 = (int64_t)kb * BK;
+    const int k0 = kb * BK;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
-    const int64_t kw = k0 + wave * 32;
-    const int64_t hS = (int64_t)h * a.S_pad;
-    const int64_t key = kw + c32;
+    const int kw = k0 + wave * 32;
+    const int key = kw + c32;
+    const int S = (int)a.S, S_pad = (int)a.S_pad;
+    const int64_t hS = (int64_t)h * S_pad;
 
-    // Issue the loads of the stage whose first query is q0 into buffer `buf`.
-    auto issue = [&](int64_t q0, int buf) {
-        const uint4 *base = lds_dkdv + buf * St::SIZE;
+    // Per-lane element offsets of this thread's chunks inside a stage's tiles
+    // (the same for every stage; the stage only moves the uniform base).
+    uint32_t roff[RU], toff[TU];
 #pragma unroll
-        for (int u = 0; u < St::LS / 256; ++u) {
-            const int c = 256 * u + tid;
-            const uint4 *wb = base + 256 * u + 64 * wave;
-            const void *src;
-            if (c < St::QT) { // row-major tiles
-                const int t = c / St::ROWS, cc = c % St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
-                const uint16_t *arr = t == 0 ? a.qhi : t == 1 ? a.qlo : t == 2 ? a.dohi : a.dolo;
-                src = arr + (hS + q0 + r) * D + ch * 8;
-            } else { // transposed tiles
-                const int t = (c - St::QT) / St::COLS, cc = (c - St::QT) % St::COLS, dim = cc / TCH;
-                const int ch = swzg<TCH>(dim, cc % TCH);
-                const uint16_t *arr = t == 0 ? a.qhi_t : a.dohi_t;
-                src = arr + ((int64_t)h * D + dim) * a.S_pad + q0 + ch * 8;
-            }
-            async16(src, wb);
+    for (int u = 0; u < RU; ++u) {
+        const int c = 256 * u + tid, r = c / RCH;
+        roff[u] = (uint32_t)(r * D + swzg<RCH>(r, c % RCH) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+        const int c = 256 * u + tid, dim = c / TCH;
+        toff[u] = (uint32_t)dim * (uint32_t)S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8);
+    }
+    const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
+    const uint16_t *const cols[2] = {a.qhi_t, a.dohi_t};
+
+    auto issue = [&](int q0, int buf) {
+        const uint4 *base = lds_dkdv + buf * St::SIZE + 64 * wave;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint16_t *rb = rows[t] + (hS + q0) * D;
+#pragma unroll
+            for (int u = 0; u < RU; ++u)
+                async16(rb + roff[u], base + t * St::ROWS + 256 * u);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+                async16(cb + toff[u], base + St::QT + t * St::COLS + 256 * u);
         }
         if (tid < BQ / 2) { // 8 chunks of lse, 8 of delta (wave 0)
             const float *arr = tid < BQ / 4 ? a.lse : a.delta;
-            async16(arr + hS + q0 + 4 * (tid % (BQ / 4)), base + St::LS);
+            async16(arr + hS + q0 + 4 * (tid % (BQ / 4)), lds_dkdv + buf * St::SIZE + St::LS);
         }
     };
 
-    uint4 kh[NS], kl[NS], vf[NS];
+    // K hi and V fragments of this lane's key stay in registers; the K lo rows
+    // of the block go to LDS (registers are the limit: keeping all three there
+    // makes the compiler shuttle values through accumulation registers).
+    uint4 kh[NS], vf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t off = (hS + key) * D + 16 * s + 8 * g;
         kh[s] = ld16(a.khi + off);
-        kl[s] = ld16(a.klo + off);
         vf[s] = ld16(a.v + off);
     }
+    uint4 *sKl = lds_dkdv + St::KLO;
+    for (int c = tid; c < 128 * RCH; c += 256) {
+        const int r = c / RCH, ch = c % RCH;
+        sKl[r * RCH + swzg<RCH>(r, ch)] = ld16(a.klo + (hS + k0 + r) * D + ch * 8);
+    }
+    const int krow = wave * 32 + c32; // this lane's key row in sKl
     f32x16_t dvT[NT], dkT[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -343,17 +367,17 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
         dkT[t] = zero16();
     }
     const int ql = kappa(c32);
-    const int nst = (int)((a.S - k0 + BQ - 1) / BQ);
+    const int nst = (S - k0 + BQ - 1) / BQ;
 
     issue(k0, 0);
     for (int it = 0; it < nst; ++it) {
-        const int64_t q0 = k0 + (int64_t)it * BQ;
+        const int q0 = k0 + it * BQ;
         wait_async();
         __syncthreads(); // this stage landed everywhere; the other buffer is free
         if (it + 1 < nst)
             issue(q0 + BQ, (it + 1) & 1);
-        if (q0 + 31 < kw)
-            continue; // every query of the stage precedes this wave's keys
+        // (near the diagonal a wave may find every query of the stage before its
+        // keys; the mask below zeroes that stage rather than branching around it)
         const uint4 *base = lds_dkdv + (it & 1) * St::SIZE;
         const float *sL = reinterpret_cast<const float *>(base + St::LS);
         const float *sDel = sL + BQ;
@@ -364,18 +388,19 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
             const uint4 q_h = base[St::QH + at];
             st = mfma32(q_h, kh[s], st);
             st = mfma32(base[St::QL + at], kh[s], st);
-            st = mfma32(q_h, kl[s], st);
+            st = mfma32(q_h, sKl[krow * RCH + swzg<RCH>(krow, 2 * s + g)], st);
             dp = mfma32(base[St::DH + at], vf[s], dp);
             dp = mfma32(base[St::DL + at], vf[s], dp);
         }
         float pr[16], ds[16];
+        const int rel = q0 - key; // query - key of register 0's query
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
-            const int64_t q = q0 + qi;
-            const bool ok = q >= key && q < a.S;
-            const float pv = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - sL[qi]) : 0.0f;
-            ds[v] = ok ? pv * (dp[v] - sDel[qi]) : 0.0f;
+            const float lq = sL[qi], dq = sDel[qi]; // read unconditionally: the selects stay branch-free
+            const bool ok = rel + qi >= 0 && q0 + qi < S;
+            const float pv = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lq : -INFINITY);
+            ds[v] = ok ? pv * (dp[v] - dq) : 0.0f;
             pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
         }
         const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
@@ -410,7 +435,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkdv(AttnBwdArgs a)
 template <int D>
 static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
 {
-    const size_t lds = 2 * (size_t)DkdvStage<D>::SIZE * sizeof(uint4);
+    const size_t lds = (size_t)DkdvStage<D>::TOTAL * sizeof(uint4);
     if (lds > 65536)
         (void)hipFuncSetAttribute((const void *)k_attn_bwd_dkdv<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
@@ -443,7 +468,7 @@ struct DqStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     typedef DqStage<D> St;
     constexpr int BM = 128, BN = St::BN, RCH = St::RCH, TCH = St::TCH;
@@ -506,11 +531,11 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
         if (kb + 1 < nkb)
             issue(k0 + BN, (kb + 1) & 1);
         const uint4 *base = lds_dq + (kb & 1) * St::SIZE;
+        // (in the diagonal block a wave may find a subtile entirely after its
+        // queries; the mask below zeroes it rather than branching around it)
 #pragma unroll
         for (int j = 0; j < BN / 32; ++j) {
             const int64_t kt0 = k0 + 32 * j;
-            if (kt0 > qw + 31)
-                break;
             const int kl = 32 * j + kap;
             f32x16_t st = zero16(), dpt = zero16();
 #pragma unroll
@@ -525,11 +550,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq(AttnBwdArgs a)
                 dpt = mfma32(vv, dl[s], dpt);
             }
             float ds[16];
+            const int rel = (int)(query - kt0); // query - key of register 0's key
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t kk = kt0 + 16 * (v >> 3) + 8 * g + (v & 7);
-                const bool ok = qok && kk <= query;
-                const float pr = ok ? __builtin_amdgcn_exp2f(st[v] * a.scale_log2 - lse2) : 0.0f;
+                const int ki = 16 * (v >> 3) + 8 * g + (v & 7);
+                const bool ok = qok && ki <= rel;
+                const float pr = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lse2 : -INFINITY);
                 ds[v] = ok ? pr * (dpt[v] - del) : 0.0f;
             }
             const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
