@@ -41,7 +41,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
         if ((L - 1) * log2p > 27)
             return LH_EUNSUPPORTED;
     }
-    if (N > kMaxN)
+    if (N > kMaxN || H > kMaxHeads)
         return LH_EUNSUPPORTED;
     const int top_shift = (L - 1) * log2p;
     if (L > 1 && (N & ((int64_t(1) << top_shift) - 1)) != 0)

@@ -16,6 +16,7 @@ constexpr int kStratum = 2048;      // entries per top-K stratum
 constexpr int kMaxSelTotal = 16384; // (L-1)*k held in LDS by the index kernel
 constexpr int kSubseqAlign = 256;   // S is padded to this for the attention tiles
 constexpr int64_t kMaxN = int64_t(1) << 27;
+constexpr int kMaxHeads = 65535; // heads run along the grid's y dimension
 
 // Extra workspace regions that are not exposed through lh_region.
 enum InternalRegion {

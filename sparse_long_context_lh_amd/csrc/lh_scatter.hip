@@ -16,69 +16,197 @@
 // Adjoint of gather(pool(.)): token j receives p^-l times the gradient of
 // gathered entry (l, floor(j/p^l)) from every level where that entry was
 // gathered (pull again, ascending l).
+#include <string.h>
+
 #include "lh_device.h"
 #include "lh_internal.h"
 
 namespace lh {
 
-constexpr int kRowsPerGroup = 4;
 constexpr int kPrepTile = 64;
 
-// ---------------------------------------------------------------- scatter-back
-template <int D, lh_dtype DT>
-__global__ __launch_bounds__(256) void k_scatter(ScatterArgs a)
+// ---------------------------------------------------------------- pull kernels
+// Scatter-back and the adjoint of gather(pool(.)) have one shape: token t
+// receives sum over levels l of w_l * src[slot_l(e_l)] with e_l = (x >> l*log2p)
+// - OFF, x = t + OFF, over the levels whose entry e_l exists and was gathered.
+// Scatter-back: OFF = 1 (x = u = j + 1), w_l = 1, one tensor. Pool adjoint:
+// OFF = 0, w_l = p^-l, three tensors (Q, K, V).
+//
+// A workgroup owns a tile of T = NLG * R consecutive positions x of one head,
+// R = p^NC per lane group. It first copies the slot entries every level needs
+// for the tile into LDS (coalesced loads, no dependent index chains). A lane
+// group then sums the levels >= NC once for its R positions (they share those
+// entries), and walks the positions keeping the partial sums of levels >= l
+// (l = NC-1 .. 1) in registers, refreshed when x crosses a p^l boundary; each
+// position adds its own level-0 row (if gathered) and is stored.
+struct PullArgs {
+    const float *src[3];  // [H][S_pad][d]
+    void *dst[3];         // [H][N][d] in the input dtype
+    const int32_t *slot;  // [H][lvl_total]
+    int64_t N, lvl_total, S_pad;
+    int64_t lvl_off[kMaxLevels];
+    int L, log2p, weighted;
+};
+
+constexpr int kPullMaxTile = 512; // positions per workgroup: 32 lane groups x 16
+
+template <int NT>
+__device__ __forceinline__ void pull_add(float (&acc)[NT][8], const PullArgs &a, int64_t off, float w)
 {
-    typedef typename Elem<DT>::T T;
-    constexpr int LANES = D / 8, NLG = 256 / LANES;
-    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
-    const int64_t rows = (int64_t)a.H * a.N;
-    const int64_t r0 = ((int64_t)blockIdx.x * NLG + lg) * kRowsPerGroup;
-    for (int rr = 0; rr < kRowsPerGroup; ++rr) {
-        const int64_t row = r0 + rr;
-        if (row >= rows)
-            return;
-        const int h = (int)(row / a.N);
-        const int64_t j = row - (int64_t)h * a.N;
-        const int32_t *slot = a.slot + (int64_t)h * a.lvl_total;
-        const float *osub = a.osub + (int64_t)h * a.S_pad * D + lane * 8;
-        float acc[8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float x[8];
+        load8(a.src[t] + off, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            acc[e] = 0.0f;
-        for (int l = 0; l < a.L; ++l) {
-            const int64_t i = ((j + 1) >> (l * a.log2p)) - 1;
-            if (i < 0)
-                continue;
-            const int32_t sl = slot[a.lvl_off[l] + i];
-            if ((uint32_t)sl >= (uint32_t)a.S_pad)
-                continue; // -1: not gathered
-            float x[8];
-            load8(osub + (int64_t)sl * D, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[e] += x[e];
-        }
-        store8(reinterpret_cast<T *>(a.out) + row * D + lane * 8, acc);
+            acc[t][e] = __builtin_fmaf(x[e], w, acc[t][e]);
     }
 }
 
-hipError_t launch_scatter(const Plan &pl, const ScatterArgs &a, hipStream_t s)
+__device__ __forceinline__ int pull_count(int64_t x0, int64_t T, int sh)
 {
-    const int nlg = 256 / (pl.d / 8);
-    const int64_t groups = ((int64_t)pl.H * pl.N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const dim3 grid((unsigned)((groups + nlg - 1) / nlg));
-    if (pl.d == 128) {
-        if (pl.dt == LH_BF16)
-            hipLaunchKernelGGL((k_scatter<128, LH_BF16>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_scatter<128, LH_F32>), grid, dim3(256), 0, s, a);
+    return (int)(((x0 + T - 1) >> sh) - (x0 >> sh) + 1);
+}
+
+template <int D, lh_dtype DT, int NT, int OFF, int NC>
+__global__ __launch_bounds__(256) void k_pull(PullArgs a)
+{
+    typedef typename Elem<DT>::T T;
+    constexpr int LANES = D / 8, NLG = 256 / LANES;
+    // level l holds at most T / p^l + 2 entries, so all levels together < 2T + 2L
+    __shared__ int32_t s_slot[2 * kPullMaxTile + 2 * kMaxLevels];
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
+    const int h = blockIdx.y;
+    const int lp = a.log2p;
+    const int R = 1 << (NC * lp);
+    const int64_t tile = (int64_t)NLG * R;
+    const int64_t x0 = (int64_t)blockIdx.x * tile;
+    const int32_t *slot = a.slot + (int64_t)h * a.lvl_total;
+
+    int b = 0;
+    for (int l = 0; l < a.L; ++l) {
+        const int sh = l * lp;
+        const int cnt = pull_count(x0, tile, sh);
+        const int64_t e0 = (x0 >> sh) - OFF, nl = a.N >> sh;
+        for (int e = threadIdx.x; e < cnt; e += 256) {
+            const int64_t i = e0 + e;
+            s_slot[b + e] = (i >= 0 && i < nl) ? slot[a.lvl_off[l] + i] : -1;
+        }
+        b += cnt;
+    }
+    __syncthreads();
+
+    const int64_t xg = x0 + (int64_t)lg * R;
+    const int64_t rowbase = (int64_t)h * a.S_pad;
+    const int col = lane * 8;
+    int base[NC > 0 ? NC : 1];
+    b = 0;
+#pragma unroll
+    for (int l = 0; l < NC; ++l) {
+        base[l] = b;
+        b += pull_count(x0, tile, l * lp);
+    }
+    float acc[NC + 1][NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[NC][t][e] = 0.0f;
+    for (int l = NC; l < a.L; ++l) { // levels shared by the lane group's R positions
+        const int sh = l * lp;
+        const int sl = s_slot[b + (int)((xg >> sh) - (x0 >> sh))];
+        b += pull_count(x0, tile, sh);
+        if ((uint32_t)sl < (uint32_t)a.S_pad)
+            pull_add<NT>(acc[NC], a, (rowbase + sl) * D + col, a.weighted ? 1.0f / (float)(1 << sh) : 1.0f);
+    }
+    if constexpr (NC == 0) { // L = 1: one position per lane group, level 0 already summed
+        const int64_t t = xg - OFF;
+        if (t >= 0 && t < a.N)
+#pragma unroll
+            for (int u = 0; u < NT; ++u)
+                store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, acc[0][u]);
     } else {
-        if (pl.dt == LH_BF16)
-            hipLaunchKernelGGL((k_scatter<64, LH_BF16>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_scatter<64, LH_F32>), grid, dim3(256), 0, s, a);
+        for (int r = 0; r < R; ++r) {
+            const int64_t x = xg + r;
+#pragma unroll
+            for (int l = NC - 1; l >= 1; --l) {
+                const int sh = l * lp;
+                if ((r & ((1 << sh) - 1)) == 0) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[l][t][e] = acc[l + 1][t][e];
+                    const int sl = s_slot[base[l] + (int)((x >> sh) - (x0 >> sh))];
+                    if ((uint32_t)sl < (uint32_t)a.S_pad)
+                        pull_add<NT>(acc[l], a, (rowbase + sl) * D + col, a.weighted ? 1.0f / (float)(1 << sh) : 1.0f);
+                }
+            }
+            float o[NT][8];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[t][e] = acc[1][t][e];
+            const int sl = s_slot[base[0] + (int)(x - x0)];
+            if ((uint32_t)sl < (uint32_t)a.S_pad)
+                pull_add<NT>(o, a, (rowbase + sl) * D + col, 1.0f);
+            const int64_t t = x - OFF;
+            if (t >= 0 && t < a.N)
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, o[u]);
+        }
+    }
+}
+
+// Levels shared per lane group: a run of R = p^NC positions, 8 or 16.
+static int pull_levels(const Plan &pl)
+{
+    const int want = pl.log2p == 1 ? 3 : (pl.log2p == 2 ? 2 : 1);
+    return want < pl.L - 1 ? want : pl.L - 1;
+}
+
+template <int D, lh_dtype DT, int NT, int OFF>
+static hipError_t launch_pull_t(const Plan &pl, const PullArgs &a, hipStream_t s)
+{
+    constexpr int NLG = 256 / (D / 8);
+    const int nc = pull_levels(pl);
+    const int64_t tile = (int64_t)NLG << (nc * pl.log2p);
+    if (tile > kPullMaxTile)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((pl.N + OFF + tile - 1) / tile), (unsigned)pl.H);
+    switch (nc) {
+    case 0: hipLaunchKernelGGL((k_pull<D, DT, NT, OFF, 0>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_pull<D, DT, NT, OFF, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_pull<D, DT, NT, OFF, 2>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_pull<D, DT, NT, OFF, 3>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+template <int NT, int OFF>
+static hipError_t launch_pull(const Plan &pl, const PullArgs &a, hipStream_t s)
+{
+    if (pl.d == 128)
+        return pl.dt == LH_BF16 ? launch_pull_t<128, LH_BF16, NT, OFF>(pl, a, s)
+                                : launch_pull_t<128, LH_F32, NT, OFF>(pl, a, s);
+    return pl.dt == LH_BF16 ? launch_pull_t<64, LH_BF16, NT, OFF>(pl, a, s)
+                            : launch_pull_t<64, LH_F32, NT, OFF>(pl, a, s);
+}
+
+hipError_t launch_scatter(const Plan &pl, const ScatterArgs &sa, hipStream_t s)
+{
+    PullArgs a;
+    memset(&a, 0, sizeof(a));
+    a.src[0] = sa.osub;
+    a.dst[0] = sa.out;
+    a.slot = sa.slot;
+    a.N = sa.N; a.lvl_total = sa.lvl_total; a.S_pad = sa.S_pad;
+    for (int l = 0; l < kMaxLevels; ++l)
+        a.lvl_off[l] = sa.lvl_off[l];
+    a.L = sa.L; a.log2p = sa.log2p; a.weighted = 0;
+    return launch_pull<1, 1>(pl, a, s);
 }
 
 // ---------------------------------------------------------------- adjoint of scatter-back
@@ -262,66 +390,20 @@ hipError_t launch_bwd_prep(const Plan &pl, const BwdPrepArgs &a, hipStream_t s)
 }
 
 // ---------------------------------------------------------------- adjoint of gather(pool(.))
-template <int D, lh_dtype DT>
-__global__ __launch_bounds__(256) void k_pool_bwd(PoolBwdArgs a)
+hipError_t launch_pool_bwd(const Plan &pl, const PoolBwdArgs &pa, hipStream_t s)
 {
-    typedef typename Elem<DT>::T T;
-    constexpr int LANES = D / 8, NLG = 256 / LANES;
-    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
-    const int64_t rows = (int64_t)a.H * a.N;
-    const int64_t r0 = ((int64_t)blockIdx.x * NLG + lg) * kRowsPerGroup;
-    for (int rr = 0; rr < kRowsPerGroup; ++rr) {
-        const int64_t row = r0 + rr;
-        if (row >= rows)
-            return;
-        const int h = (int)(row / a.N);
-        const int64_t j = row - (int64_t)h * a.N;
-        const int32_t *slot = a.slot + (int64_t)h * a.lvl_total;
-        float acc[3][8];
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[t][e] = 0.0f;
-        for (int l = 0; l < a.L; ++l) {
-            const int sh = l * a.log2p;
-            const int32_t sl = slot[a.lvl_off[l] + (j >> sh)];
-            if ((uint32_t)sl >= (uint32_t)a.S_pad)
-                continue; // -1: not gathered
-            const float w = 1.0f / (float)(int64_t(1) << sh); // exact: power of two
-            const int64_t off = ((int64_t)h * a.S_pad + sl) * D + lane * 8;
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                float x[8];
-                load8(a.dsub[t] + off, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[t][e] += x[e] * w;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-            store8(reinterpret_cast<T *>(a.dx[t]) + row * D + lane * 8, acc[t]);
+    PullArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int t = 0; t < 3; ++t) {
+        a.src[t] = pa.dsub[t];
+        a.dst[t] = pa.dx[t];
     }
-}
-
-hipError_t launch_pool_bwd(const Plan &pl, const PoolBwdArgs &a, hipStream_t s)
-{
-    const int nlg = 256 / (pl.d / 8);
-    const int64_t groups = ((int64_t)pl.H * pl.N + kRowsPerGroup - 1) / kRowsPerGroup;
-    const dim3 grid((unsigned)((groups + nlg - 1) / nlg));
-    if (pl.d == 128) {
-        if (pl.dt == LH_BF16)
-            hipLaunchKernelGGL((k_pool_bwd<128, LH_BF16>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_pool_bwd<128, LH_F32>), grid, dim3(256), 0, s, a);
-    } else {
-        if (pl.dt == LH_BF16)
-            hipLaunchKernelGGL((k_pool_bwd<64, LH_BF16>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_pool_bwd<64, LH_F32>), grid, dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
+    a.slot = pa.slot;
+    a.N = pa.N; a.lvl_total = pa.lvl_total; a.S_pad = pa.S_pad;
+    for (int l = 0; l < kMaxLevels; ++l)
+        a.lvl_off[l] = pa.lvl_off[l];
+    a.L = pa.L; a.log2p = pa.log2p; a.weighted = 1;
+    return launch_pull<3, 0>(pl, a, s);
 }
 
 } // namespace lh
