@@ -92,12 +92,26 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
             }
         }
     }
-    // Rows one lane group streams: a whole number of top-level windows, up to 64 rows.
-    const int64_t P = int64_t(1) << top_shift;
-    int64_t w = 1;
-    while (P * w * 2 <= 64 && (pl->n[L - 1] % (w * 2)) == 0)
-        w *= 2;
-    pl->run = (int)(P * w);
+    // Levels finished inside the row tiles; coarser ones keep window sums in
+    // IR_FPART (front, entries i of level l) and IR_SPART (scatter-back
+    // adjoint, u-space windows m = i + 1, the last tile's tail included).
+    pl->LT = L > 1 ? (tile_levels(d, log2p) < L - 1 ? tile_levels(d, log2p) : L - 1) : 0;
+    for (int l = 0; l < kMaxLevels; ++l)
+        pl->fpart_off[l] = pl->spart_off[l] = pl->spart_n[l] = -1;
+    pl->fpart_rows = pl->spart_rows = 0;
+    {
+        const int64_t T = tile_rows(d, log2p);
+        int64_t m = (N + 1 + T - 1) / T * T; // u-space positions the tiles cover
+        m >>= pl->LT * log2p;
+        for (int l = pl->LT; l <= L - 2; ++l) {
+            pl->fpart_off[l] = pl->fpart_rows;
+            pl->fpart_rows += pl->n[l];
+            pl->spart_n[l] = m;
+            pl->spart_off[l] = pl->spart_rows;
+            pl->spart_rows += m;
+            m = (m + p - 1) / p;
+        }
+    }
 
     const size_t Hs = (size_t)H, Sp = (size_t)pl->S_pad, D = (size_t)d;
     size_t b[IR_COUNT];
@@ -114,6 +128,8 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_POOLED] = 4 * 3 * Hs * (size_t)pl->mat_rows * D;
     b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
+    b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
+    b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
     size_t off = 0;
     for (int r = 0; r < IR_COUNT; ++r) {
         pl->off[r] = off;
@@ -177,7 +193,11 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
             fa.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
             fa.mat_off[l] = pl.mat_off[l];
         }
-        fa.H = H; fa.L = L; fa.log2p = pl.log2p; fa.run = pl.run; fa.runs_per_head = (int)(N / pl.run);
+        fa.part = at<float>(ws, pl, IR_FPART);
+        fa.part_rows = pl.fpart_rows;
+        for (int l = 0; l < kMaxLevels; ++l)
+            fa.part_off[l] = pl.fpart_off[l];
+        fa.H = H; fa.L = L; fa.log2p = pl.log2p; fa.LT = pl.LT;
         if (launch_front(pl, fa, s) != hipSuccess)
             return LH_EHIP;
     }
@@ -289,10 +309,13 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         a.N = N; a.lvl_total = pl.lvl_total; a.S_pad = pl.S_pad;
         for (int l = 0; l < kMaxLevels; ++l)
             a.lvl_off[l] = l < L ? pl.lvl_off[l] : 0;
-        a.H = H; a.L = L; a.log2p = pl.log2p; a.run = pl.run;
-        // u = j + 1 runs over [0, N + p^(L-1)): every top-level u-window, the last one partial.
-        const int64_t P = int64_t(1) << ((L - 1) * pl.log2p);
-        a.tiles_per_head = (int)((N + P + pl.run - 1) / pl.run);
+        a.part = at<float>(ws, pl, IR_SPART);
+        a.part_rows = pl.spart_rows;
+        for (int l = 0; l < kMaxLevels; ++l) {
+            a.part_off[l] = pl.spart_off[l];
+            a.part_n[l] = pl.spart_n[l];
+        }
+        a.H = H; a.L = L; a.log2p = pl.log2p; a.LT = pl.LT;
         if (launch_scatter_bwd(pl, a, s) != hipSuccess)
             return LH_EHIP;
     }

@@ -100,6 +100,38 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8])
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// A piece kept in its storage format until it is summed (fewer registers
+// while many rows are in flight).
+template <lh_dtype DT> struct Raw8;
+template <> struct Raw8<LH_BF16> { uint4 u; };
+template <> struct Raw8<LH_F32> { float4 a, b; };
+
+__device__ __forceinline__ void ld_raw(const uint16_t *p, Raw8<LH_BF16> &r) { r.u = *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void ld_raw(const float *p, Raw8<LH_F32> &r)
+{
+    r.a = reinterpret_cast<const float4 *>(p)[0];
+    r.b = reinterpret_cast<const float4 *>(p)[1];
+}
+__device__ __forceinline__ void zero_raw(Raw8<LH_BF16> &r) { r.u = make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ void zero_raw(Raw8<LH_F32> &r)
+{
+    r.a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    r.b = r.a;
+}
+__device__ __forceinline__ void unraw(const Raw8<LH_BF16> &r, float (&x)[8])
+{
+    const uint4 u = r.u;
+    x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+    x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+    x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+__device__ __forceinline__ void unraw(const Raw8<LH_F32> &r, float (&x)[8])
+{
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
 // Element type tags for the layer's inputs / outputs.
 template <lh_dtype DT> struct Elem;
 template <> struct Elem<LH_BF16> { typedef uint16_t T; };

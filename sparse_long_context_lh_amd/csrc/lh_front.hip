@@ -9,12 +9,16 @@
 //     materialise, as fp32 means of an fp32 sum (no rounding to 16 bits, so
 //     the attention sees pooled rows at full precision).
 //
-// Work split: a "lane group" of d/8 lanes owns one row at a time, each lane
-// holding 8 consecutive elements (16 B of bf16 or 32 B of fp32). A lane group
-// streams a contiguous run of rows that starts on a top-level window
-// boundary, so every level's window sum is built in registers by a cascade
-// (the level-l sum is pushed into level l+1 when its window ends). No LDS, no
-// atomics; each input byte is read once.
+// Work split: a "lane group" of d/8 lanes owns a row, each lane holding 8
+// consecutive elements (16 B of bf16 or 32 B of fp32). A lane group loads a
+// run of R = p^c rows at once (all loads in flight together), computes their
+// scores, and sums its run level by level in registers: a level-l window sum
+// is the sum of its p level-(l-1) window sums in ascending order, starting
+// from 0 (the same tree at every level, so the pooled values do not depend on
+// the tiling). Run totals meet in LDS, where the workgroup finishes the levels
+// whose windows fit its tile; each coarser level is one small kernel over the
+// window sums the previous level left in the workspace. No atomics; each
+// input byte is read once.
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -37,132 +41,308 @@ __device__ __forceinline__ float row_norm2(const float (&x)[8])
     return a;
 }
 
-template <int D, lh_dtype DT, int NL>
+// v[lane], for an array every lane of the lane group holds identically.
+template <int N>
+__device__ __forceinline__ float pick(const float (&v)[N], int lane)
+{
+    float r = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        r = lane == i ? v[i] : r;
+    return r;
+}
+
+constexpr int ipow(int b, int e) { return e == 0 ? 1 : b * ipow(b, e - 1); }
+
+template <int D, lh_dtype DT, int LP>
 __global__ __launch_bounds__(256) void k_front(FrontArgs a)
 {
     typedef typename Elem<DT>::T T;
-    constexpr int LANES = D / 8;
-    constexpr int NLG = 256 / LANES;
-    constexpr int NA = NL > 1 ? NL - 1 : 1; // accumulators for levels 1..NL-1
-    const int lane = threadIdx.x % LANES;
-    const int lg = threadIdx.x / LANES;
-    const int64_t run_id = (int64_t)blockIdx.x * NLG + lg;
-    if (run_id >= (int64_t)a.H * a.runs_per_head)
-        return;
-    const int h = (int)(run_id / a.runs_per_head);
-    const int64_t t0 = (run_id % a.runs_per_head) * a.run;
-    const int64_t row0 = ((int64_t)h * a.N + t0) * D + lane * 8;
-    const T *qp = reinterpret_cast<const T *>(a.q) + row0;
-    const T *kp = reinterpret_cast<const T *>(a.k) + row0;
-    const T *vp = reinterpret_cast<const T *>(a.v) + row0;
+    typedef TileShape<D, LP> Sh;
+    constexpr int LANES = Sh::LANES, NLG = Sh::NLG, NC = Sh::NC, R = Sh::R, P = 1 << LP;
+    __shared__ __attribute__((aligned(16))) float s_sum[3][NLG][D];
+    __shared__ float s_max[NLG];
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES, col = lane * 8;
+    const int h = blockIdx.y;
+    const int64_t x0 = (int64_t)blockIdx.x * Sh::T;
+    const int64_t j0 = x0 + (int64_t)lg * R;
+    const int LT = a.LT;
+    const bool keep = LT < a.L - 1; // level LT's window sums feed the next level's kernel
     float *sc = a.scores + (int64_t)h * a.lvl_total;
-    float *pooled = a.pooled + (int64_t)h * a.mat_rows * D + lane * 8;
+    float *pooled = a.pooled + (int64_t)h * a.mat_rows * D + col;
+    const int64_t pstride = (int64_t)a.H * a.part_rows * D;
+    float *part = a.part + (int64_t)h * a.part_rows * D + col;
+    float *pmax = a.part + 3 * pstride + (int64_t)h * a.part_rows;
 
-    float acc[3][NA][8];
-    float smax[NA];
-#pragma unroll
-    for (int l = 0; l < NA; ++l) {
-        smax[l] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
+    // A finished level-l window i (i < n_l, l <= LT): the pooled mean of a
+    // materialised level, and the sum itself when level LT feeds coarser ones.
+    auto put_sum = [&](int t, int l, int64_t i, const float (&acc)[8]) {
+        if (a.mat_off[l] >= 0) {
+            const float w = 1.0f / (float)(1 << (l * LP)); // exact: power of two
+            float m8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                acc[t][l][e] = 0.0f;
+                m8[e] = acc[e] * w;
+            store8(pooled + t * a.tensor_stride + (a.mat_off[l] + i) * D, m8);
+        }
+        if (keep && l == LT)
+            store8(part + t * pstride + (a.part_off[l] + i) * D, acc);
+    };
+    auto put_max = [&](int l, int64_t i, float m) {
+        sc[a.lvl_off[l] + i] = m;
+        if (keep && l == LT)
+            pmax[a.part_off[l] + i] = m;
+    };
+
+    const int64_t in_off = ((int64_t)h * a.N + j0) * D + col;
+    const T *qp = reinterpret_cast<const T *>(a.q) + in_off;
+    const T *kp = reinterpret_cast<const T *>(a.k) + in_off;
+    const T *vp = reinterpret_cast<const T *>(a.v) + in_off;
+    Raw8<DT> rq[R], rk[R], rv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (j0 + r < a.N) {
+            ld_raw(qp + r * D, rq[r]);
+            ld_raw(kp + r * D, rk[r]);
+        } else {
+            zero_raw(rq[r]);
+            zero_raw(rk[r]);
+        }
     }
 
-    for (int r = 0; r < a.run; r += 4) {
-        float xq[4][8], xk[4][8], xv[4][8];
+    // token scores, then their maxima over the run's windows
+    float s[R];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (r + u < a.run) {
-                load8(qp + (int64_t)(r + u) * D, xq[u]);
-                load8(kp + (int64_t)(r + u) * D, xk[u]);
-                if (NL > 1)
-                    load8(vp + (int64_t)(r + u) * D, xv[u]);
+    for (int r = 0; r < R; ++r) {
+        float x[8];
+        unraw(rq[r], x);
+        const float nq = row_norm2<LANES>(x);
+        unraw(rk[r], x);
+        const float nk = row_norm2<LANES>(x);
+        s[r] = sqrtf(nq) + sqrtf(nk);
+    }
+#pragma unroll
+    for (int r0 = 0; r0 < R; r0 += LANES) {
+        constexpr int W = R < LANES ? R : LANES;
+        float v[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            v[i] = s[r0 + i];
+        const float mine = pick<W>(v, lane);
+        if (lane < W && j0 + r0 + lane < a.N)
+            sc[j0 + r0 + lane] = mine;
+    }
+    float mx[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        mx[r] = s[r];
+#pragma unroll
+    for (int l = 1; l <= NC; ++l) {
+        const int cnt = R / ipow(P, l);
+#pragma unroll
+        for (int w = 0; w < R; ++w) {
+            if (w < cnt) {
+                float m = mx[w * P];
+#pragma unroll
+                for (int c = 1; c < P; ++c)
+                    m = fmaxf(m, mx[w * P + c]);
+                mx[w] = m;
             }
         }
+        const int64_t i = (j0 >> (l * LP)) + lane;
+        const float mine = pick<R>(mx, lane);
+        if (l <= LT && lane < cnt && i < (a.N >> (l * LP)))
+            put_max(l, i, mine);
+    }
+    const float run_max = mx[0];
+
+    // window sums of the run, tensor after tensor
+    float tot[3][8];
+    auto cascade = [&](int t, const Raw8<DT> (&rows)[R]) {
+        float acc[NC][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (r + u >= a.run)
-                break;
-            const int64_t t = t0 + r + u;
-            const float s = sqrtf(row_norm2<LANES>(xq[u])) + sqrtf(row_norm2<LANES>(xk[u]));
-            if (lane == 0)
-                sc[t] = s;
-            if constexpr (NL > 1) {
+        for (int l = 0; l < NC; ++l)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    acc[0][0][e] += xq[u][e];
-                    acc[1][0][e] += xk[u][e];
-                    acc[2][0][e] += xv[u][e];
-                }
-                smax[0] = fmaxf(smax[0], s);
-                // A level-l window ends on token t when p^l divides t+1; the
-                // conditions nest, so levels are closed in ascending order.
+            for (int e = 0; e < 8; ++e)
+                acc[l][e] = 0.0f;
 #pragma unroll
-                for (int l = 1; l < NL; ++l) {
-                    const int sh = l * a.log2p;
-                    if (((t + 1) & ((int64_t(1) << sh) - 1)) == 0) {
-                        const int64_t i = t >> sh;
-                        if (lane == 0)
-                            sc[a.lvl_off[l] + i] = smax[l - 1];
-                        if (a.mat_off[l] >= 0) {
-                            const float w = 1.0f / (float)(int64_t(1) << sh); // exact: power of two
-                            float *dst = pooled + (a.mat_off[l] + i) * D;
+        for (int r = 0; r < R; ++r) {
+            float x[8];
+            unraw(rows[r], x);
 #pragma unroll
-                            for (int t3 = 0; t3 < 3; ++t3) {
-                                float m8[8];
+            for (int e = 0; e < 8; ++e)
+                acc[0][e] += x[e];
 #pragma unroll
-                                for (int e = 0; e < 8; ++e)
-                                    m8[e] = acc[t3][l - 1][e] * w;
-                                store8(dst + t3 * a.tensor_stride, m8);
-                            }
-                        }
-                        if (l + 1 < NL) {
+            for (int l = 1; l <= NC; ++l) {
+                if ((r + 1) % ipow(P, l) == 0) {
+                    const int64_t i = (j0 >> (l * LP)) + (r + 1) / ipow(P, l) - 1;
+                    if (l <= LT && i < (a.N >> (l * LP)))
+                        put_sum(t, l, i, acc[l - 1]);
 #pragma unroll
-                            for (int t3 = 0; t3 < 3; ++t3)
-#pragma unroll
-                                for (int e = 0; e < 8; ++e)
-                                    acc[t3][l][e] += acc[t3][l - 1][e];
-                            smax[l] = fmaxf(smax[l], smax[l - 1]);
-                        }
-#pragma unroll
-                        for (int t3 = 0; t3 < 3; ++t3)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                acc[t3][l - 1][e] = 0.0f;
-                        smax[l - 1] = 0.0f;
+                    for (int e = 0; e < 8; ++e) {
+                        if (l < NC)
+                            acc[l < NC ? l : 0][e] += acc[l - 1][e];
+                        else
+                            tot[t][e] = acc[l - 1][e];
+                        acc[l - 1][e] = 0.0f;
                     }
                 }
             }
         }
+    };
+    cascade(0, rq);
+    // V is loaded only now (into the registers Q used): keeps two tensors in flight, not three
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (j0 + r < a.N)
+            ld_raw(vp + r * D, rv[r]);
+        else
+            zero_raw(rv[r]);
+    }
+    cascade(1, rk);
+    cascade(2, rv);
+
+    // levels NC+1 .. LT from the run totals, in LDS
+    if (LT > NC) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            *reinterpret_cast<float4 *>(&s_sum[t][lg][col]) = make_float4(tot[t][0], tot[t][1], tot[t][2], tot[t][3]);
+            *reinterpret_cast<float4 *>(&s_sum[t][lg][col + 4]) = make_float4(tot[t][4], tot[t][5], tot[t][6], tot[t][7]);
+        }
+        if (lane == 0)
+            s_max[lg] = run_max;
+        __syncthreads();
+        int W = NLG;
+        for (int l = NC + 1; l <= LT; ++l) {
+            W /= P;
+            const int64_t nl = a.N >> (l * LP);
+            float res[2][8], rmx = 0.0f;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int task = lg + n * NLG;
+                if (task < 3 * W) {
+                    const int t = task / W, w = task - t * W;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        res[n][e] = 0.0f;
+                    for (int c = 0; c < P; ++c) {
+                        const float4 lo = *reinterpret_cast<const float4 *>(&s_sum[t][w * P + c][col]);
+                        const float4 hi = *reinterpret_cast<const float4 *>(&s_sum[t][w * P + c][col + 4]);
+                        res[n][0] += lo.x; res[n][1] += lo.y; res[n][2] += lo.z; res[n][3] += lo.w;
+                        res[n][4] += hi.x; res[n][5] += hi.y; res[n][6] += hi.z; res[n][7] += hi.w;
+                    }
+                    const int64_t i = (x0 >> (l * LP)) + w;
+                    if (i < nl)
+                        put_sum(t, l, i, res[n]);
+                    if (t == 0) {
+                        float m = s_max[w * P];
+                        for (int c = 1; c < P; ++c)
+                            m = fmaxf(m, s_max[w * P + c]);
+                        rmx = m;
+                        if (lane == 0 && i < nl)
+                            put_max(l, i, m);
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int task = lg + n * NLG;
+                if (task < 3 * W) {
+                    const int t = task / W, w = task - t * W;
+                    *reinterpret_cast<float4 *>(&s_sum[t][w][col]) = make_float4(res[n][0], res[n][1], res[n][2], res[n][3]);
+                    *reinterpret_cast<float4 *>(&s_sum[t][w][col + 4]) = make_float4(res[n][4], res[n][5], res[n][6], res[n][7]);
+                    if (t == 0 && lane == 0)
+                        s_max[w] = rmx;
+                }
+            }
+            __syncthreads();
+        }
     }
 }
 
-template <int D, lh_dtype DT>
+// Level l > LT: window i sums the p windows i*p .. i*p+p-1 of level l-1 kept
+// in the workspace (ascending, from 0), one lane group per (head, window).
+template <int D>
+__global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
+{
+    constexpr int LANES = D / 8, NLG = 256 / LANES;
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES, col = lane * 8;
+    const int64_t nl = a.N >> (l * a.log2p);
+    const int64_t item = (int64_t)blockIdx.x * NLG + lg;
+    if (item >= (int64_t)a.H * nl)
+        return;
+    const int h = (int)(item / nl);
+    const int64_t i = item - (int64_t)h * nl;
+    const int P = 1 << a.log2p;
+    const bool keep = l < a.L - 1;
+    const int64_t pstride = (int64_t)a.H * a.part_rows * D;
+    const float *src = a.part + ((int64_t)h * a.part_rows + a.part_off[l - 1] + i * P) * D + col;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = 0.0f;
+        for (int c = 0; c < P; ++c) {
+            float x[8];
+            load8(src + t * pstride + c * D, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] += x[e];
+        }
+        if (a.mat_off[l] >= 0) {
+            const float w = 1.0f / (float)(1 << (l * a.log2p)); // exact: power of two
+            float m8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                m8[e] = acc[e] * w;
+            store8(a.pooled + t * a.tensor_stride + ((int64_t)h * a.mat_rows + a.mat_off[l] + i) * D + col, m8);
+        }
+        if (keep)
+            store8(a.part + t * pstride + ((int64_t)h * a.part_rows + a.part_off[l] + i) * D + col, acc);
+    }
+    if (lane == 0) {
+        const float *pm = a.part + 3 * pstride + (int64_t)h * a.part_rows + a.part_off[l - 1] + i * P;
+        float m = pm[0];
+        for (int c = 1; c < P; ++c)
+            m = fmaxf(m, pm[c]);
+        a.scores[(int64_t)h * a.lvl_total + a.lvl_off[l] + i] = m;
+        if (keep)
+            a.part[3 * pstride + (int64_t)h * a.part_rows + a.part_off[l] + i] = m;
+    }
+}
+
+template <int D, lh_dtype DT, int LP>
 static hipError_t launch_front_t(const Plan &pl, const FrontArgs &a, hipStream_t s)
 {
+    constexpr int T = TileShape<D, LP>::T;
+    const dim3 grid((unsigned)((pl.N + T - 1) / T), (unsigned)pl.H);
+    hipLaunchKernelGGL((k_front<D, DT, LP>), grid, dim3(256), 0, s, a);
     constexpr int NLG = 256 / (D / 8);
-    const int64_t runs = (int64_t)a.H * a.runs_per_head;
-    const dim3 grid((unsigned)((runs + NLG - 1) / NLG));
-    switch (pl.L) {
-    case 1: hipLaunchKernelGGL((k_front<D, DT, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_front<D, DT, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_front<D, DT, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_front<D, DT, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_front<D, DT, 5>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_front<D, DT, 6>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((k_front<D, DT, 7>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_front<D, DT, 8>), grid, dim3(256), 0, s, a); break;
+    for (int l = pl.LT + 1; l < pl.L; ++l) {
+        const int64_t items = (int64_t)pl.H * pl.n[l];
+        hipLaunchKernelGGL((k_front_up<D>), dim3((unsigned)((items + NLG - 1) / NLG)), dim3(256), 0, s, a, l);
     }
     return hipGetLastError();
+}
+
+template <int D, lh_dtype DT>
+static hipError_t launch_front_p(const Plan &pl, const FrontArgs &a, hipStream_t s)
+{
+    switch (pl.log2p) {
+    case 1: return launch_front_t<D, DT, 1>(pl, a, s);
+    case 2: return launch_front_t<D, DT, 2>(pl, a, s);
+    default: return launch_front_t<D, DT, 3>(pl, a, s);
+    }
 }
 
 hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s)
 {
     if (pl.d == 128)
-        return pl.dt == LH_BF16 ? launch_front_t<128, LH_BF16>(pl, a, s) : launch_front_t<128, LH_F32>(pl, a, s);
-    return pl.dt == LH_BF16 ? launch_front_t<64, LH_BF16>(pl, a, s) : launch_front_t<64, LH_F32>(pl, a, s);
+        return pl.dt == LH_BF16 ? launch_front_p<128, LH_BF16>(pl, a, s) : launch_front_p<128, LH_F32>(pl, a, s);
+    return pl.dt == LH_BF16 ? launch_front_p<64, LH_BF16>(pl, a, s) : launch_front_p<64, LH_F32>(pl, a, s);
 }
 
 // ---------------------------------------------------------------- sqrt self-test

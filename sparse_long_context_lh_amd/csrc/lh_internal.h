@@ -25,8 +25,30 @@ enum InternalRegion {
     IR_DOLO,                // fp16 [H][S_pad][d]: lo part of dO_sub
     IR_DOHI_T,              // fp16 [H][d][S_pad]: transpose of the hi part
     IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub)
+    IR_FPART,               // fp32 window sums [3][H][fpart_rows][d], then maxima [H][fpart_rows]
+    IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
     IR_COUNT
 };
+
+// Row tiles of the front pass and of the scatter-back adjoint. A lane group
+// (d/8 lanes, 8 elements each) owns R = p^NC consecutive rows; a workgroup of
+// 256 threads owns NLG * R rows. Levels whose windows fit a tile (p^l divides
+// it) are finished inside the tile kernel; coarser ones by one small kernel
+// per level over the tile kernel's window sums.
+constexpr int clog2(int x) { return x <= 1 ? 0 : 1 + clog2(x / 2); }
+template <int D, int LP> struct TileShape {
+    static constexpr int LANES = D / 8, NLG = 256 / LANES;
+    static constexpr int NC = LP == 1 ? 2 : 1;
+    static constexpr int R = 1 << (NC * LP); // 4 (p = 2), 4 (p = 4), 8 (p = 8)
+    static constexpr int T = NLG * R;
+    static constexpr int LMAX = clog2(T) / LP;
+};
+inline int tile_rows(int d, int log2p)
+{
+    const int nlg = 256 / (d / 8), nc = log2p == 1 ? 2 : 1;
+    return nlg << (nc * log2p);
+}
+inline int tile_levels(int d, int log2p) { return clog2(tile_rows(d, log2p)) / log2p; }
 
 struct Plan {
     int64_t N;
@@ -41,7 +63,12 @@ struct Plan {
     uint32_t mat_mask;           // bit l set: level l pooled rows are written by the front kernel
     int64_t mat_off[kMaxLevels]; // row offset of a materialized level inside one head's pooled block
     int64_t mat_rows;
-    int run;                     // rows streamed by one lane group in the front / scatter kernels
+    int LT;                      // levels 1..LT are finished inside the row-tile kernels
+    int64_t fpart_off[kMaxLevels]; // row offset of level l's window sums in a head's IR_FPART block
+    int64_t fpart_rows;
+    int64_t spart_n[kMaxLevels];   // u-space windows of level l kept in IR_SPART (l >= LT)
+    int64_t spart_off[kMaxLevels];
+    int64_t spart_rows;
     size_t off[IR_COUNT], bytes[IR_COUNT];
     size_t total;
 };
@@ -57,7 +84,10 @@ struct FrontArgs {
     int64_t N, lvl_total, mat_rows, tensor_stride; // tensor_stride = H*mat_rows*d
     int64_t lvl_off[kMaxLevels];
     int64_t mat_off[kMaxLevels]; // -1: level not materialized
-    int H, L, log2p, run, runs_per_head;
+    float *part;                 // IR_FPART: window sums of levels LT .. L-2, then their maxima
+    int64_t part_rows;
+    int64_t part_off[kMaxLevels];
+    int H, L, log2p, LT;
 };
 
 struct TopkArgs {
@@ -131,7 +161,10 @@ struct ScatterBwdArgs {
     float *dosub;        // [H][S_pad][d]
     int64_t N, lvl_total, S_pad;
     int64_t lvl_off[kMaxLevels];
-    int H, L, log2p, run, tiles_per_head;
+    float *part;         // IR_SPART: u-space window sums of levels LT .. L-2
+    int64_t part_rows;   // rows of one head's IR_SPART block
+    int64_t part_off[kMaxLevels], part_n[kMaxLevels];
+    int H, L, log2p, LT;
 };
 
 struct BwdPrepArgs {

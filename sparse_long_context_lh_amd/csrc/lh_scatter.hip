@@ -210,114 +210,200 @@ hipError_t launch_scatter(const Plan &pl, const ScatterArgs &sa, hipStream_t s)
 }
 
 // ---------------------------------------------------------------- adjoint of scatter-back
-template <int D, lh_dtype DT, int NL>
+// Row tiles in u-space (u = j + 1; TileShape): a lane group loads R rows of
+// dO at once, stores the rows whose level-0 entry was gathered, and sums its
+// run level by level (window sums of p child sums in ascending order, from
+// 0); run totals meet in LDS for the levels whose windows fit the tile, and
+// each coarser level is one small kernel over the window sums of the level
+// below. Window m of level l is entry i = m - 1 (window 0 has no entry).
+constexpr int cpow(int b, int e) { return e == 0 ? 1 : b * cpow(b, e - 1); }
+
+template <int D, lh_dtype DT, int LP>
 __global__ __launch_bounds__(256) void k_scatter_bwd(ScatterBwdArgs a)
 {
     typedef typename Elem<DT>::T T;
-    constexpr int LANES = D / 8, NLG = 256 / LANES;
-    constexpr int NA = NL > 1 ? NL - 1 : 1;
-    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
-    const int64_t run_id = (int64_t)blockIdx.x * NLG + lg;
-    if (run_id >= (int64_t)a.H * a.tiles_per_head)
-        return;
-    const int h = (int)(run_id / a.tiles_per_head);
-    const int64_t u0 = (run_id % a.tiles_per_head) * a.run;
-    const T *dout = reinterpret_cast<const T *>(a.dout) + (int64_t)h * a.N * D + lane * 8;
+    typedef TileShape<D, LP> Sh;
+    constexpr int LANES = Sh::LANES, NLG = Sh::NLG, NC = Sh::NC, R = Sh::R, P = 1 << LP;
+    __shared__ __attribute__((aligned(16))) float s_sum[NLG][D];
+    __shared__ int32_t s_slot[2 * Sh::T]; // levels 0..LT: T/p^l windows each
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES, col = lane * 8;
+    const int h = blockIdx.y;
+    const int64_t x0 = (int64_t)blockIdx.x * Sh::T;
+    const int64_t ug = x0 + (int64_t)lg * R;
+    const int LT = a.LT;
+    const bool keep = LT < a.L - 1;
     const int32_t *slot = a.slot + (int64_t)h * a.lvl_total;
-    float *dosub = a.dosub + (int64_t)h * a.S_pad * D + lane * 8;
+    float *dosub = a.dosub + (int64_t)h * a.S_pad * D + col;
+    float *part = a.part + (int64_t)h * a.part_rows * D + col;
 
-    float acc[NA][8];
+    {
+        int b = 0;
+        for (int l = 0; l <= LT; ++l) {
+            const int sh = l * LP, cnt = Sh::T >> sh;
+            const int64_t nl = a.N >> sh, e0 = (x0 >> sh) - 1;
+            for (int e = threadIdx.x; e < cnt; e += 256) {
+                const int64_t i = e0 + e;
+                s_slot[b + e] = (i >= 0 && i < nl) ? slot[a.lvl_off[l] + i] : -1;
+            }
+            b += cnt;
+        }
+    }
+    const T *dout = reinterpret_cast<const T *>(a.dout) + (int64_t)h * a.N * D + col;
+    Raw8<DT> rows[R];
 #pragma unroll
-    for (int l = 0; l < NA; ++l)
+    for (int r = 0; r < R; ++r) {
+        const int64_t u = ug + r;
+        if (u >= 1 && u <= a.N)
+            ld_raw(dout + (u - 1) * D, rows[r]);
+        else
+            zero_raw(rows[r]);
+    }
+    __syncthreads();
+
+    // finished window m of level l (l <= LT): to dO_sub if its entry was
+    // gathered, and kept for the next level if l is LT and coarser ones exist
+    auto put = [&](int l, int64_t m, const float (&acc)[8]) {
+        int b = 0;
+        for (int q = 0; q < l; ++q)
+            b += Sh::T >> (q * LP);
+        const int32_t sl = s_slot[b + (int)(m - (x0 >> (l * LP)))];
+        if ((uint32_t)sl < (uint32_t)a.S_pad)
+            store8(dosub + (int64_t)sl * D, acc);
+        if (keep && l == LT)
+            store8(part + (a.part_off[l] + m) * D, acc);
+    };
+
+    float acc[NC][8], tot[8];
+#pragma unroll
+    for (int l = 0; l < NC; ++l)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc[l][e] = 0.0f;
-
-    for (int r = 0; r < a.run; r += 4) {
-        float x[4][8];
 #pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-            const int64_t j = u0 + r + uu - 1;
-            if (r + uu < a.run && j >= 0 && j < a.N) {
-                load8(dout + j * D, x[uu]);
-            } else {
+    for (int r = 0; r < R; ++r) {
+        float x[8];
+        unraw(rows[r], x);
+        put(0, ug + r, x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    x[uu][e] = 0.0f;
-            }
-        }
+        for (int e = 0; e < 8; ++e)
+            acc[0][e] += x[e];
 #pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-            if (r + uu >= a.run)
-                break;
-            const int64_t u = u0 + r + uu;
-            const int64_t j = u - 1;
-            if (j >= 0 && j < a.N) { // level 0: R(0, j) = {j}
-                const int32_t sl = slot[a.lvl_off[0] + j];
-                if ((uint32_t)sl < (uint32_t)a.S_pad)
-                    store8(dosub + (int64_t)sl * D, x[uu]);
-            }
-            if constexpr (NL > 1) {
+        for (int l = 1; l <= NC; ++l) {
+            if ((r + 1) % cpow(P, l) == 0) {
+                if (l <= LT)
+                    put(l, (ug >> (l * LP)) + (r + 1) / cpow(P, l) - 1, acc[l - 1]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[0][e] += x[uu][e];
-#pragma unroll
-                for (int l = 1; l < NL; ++l) {
-                    const int sh = l * a.log2p;
-                    if (((u + 1) & ((int64_t(1) << sh) - 1)) == 0) {
-                        const int64_t i = (u >> sh) - 1;
-                        if (i >= 0 && i < (a.N >> sh)) {
-                            const int32_t sl = slot[a.lvl_off[l] + i];
-                            if ((uint32_t)sl < (uint32_t)a.S_pad)
-                                store8(dosub + (int64_t)sl * D, acc[l - 1]);
-                        }
-                        if (l + 1 < NL) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                acc[l][e] += acc[l - 1][e];
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[l - 1][e] = 0.0f;
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    if (l < NC)
+                        acc[l < NC ? l : 0][e] += acc[l - 1][e];
+                    else
+                        tot[e] = acc[l - 1][e];
+                    acc[l - 1][e] = 0.0f;
                 }
             }
         }
     }
+
+    if (LT > NC) {
+        *reinterpret_cast<float4 *>(&s_sum[lg][col]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+        *reinterpret_cast<float4 *>(&s_sum[lg][col + 4]) = make_float4(tot[4], tot[5], tot[6], tot[7]);
+        __syncthreads();
+        int W = NLG;
+        for (int l = NC + 1; l <= LT; ++l) {
+            W /= P;
+            float res[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                res[e] = 0.0f;
+            if (lg < W) {
+                for (int c = 0; c < P; ++c) {
+                    const float4 lo = *reinterpret_cast<const float4 *>(&s_sum[lg * P + c][col]);
+                    const float4 hi = *reinterpret_cast<const float4 *>(&s_sum[lg * P + c][col + 4]);
+                    res[0] += lo.x; res[1] += lo.y; res[2] += lo.z; res[3] += lo.w;
+                    res[4] += hi.x; res[5] += hi.y; res[6] += hi.z; res[7] += hi.w;
+                }
+                put(l, (x0 >> (l * LP)) + lg, res);
+            }
+            __syncthreads();
+            if (lg < W) {
+                *reinterpret_cast<float4 *>(&s_sum[lg][col]) = make_float4(res[0], res[1], res[2], res[3]);
+                *reinterpret_cast<float4 *>(&s_sum[lg][col + 4]) = make_float4(res[4], res[5], res[6], res[7]);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Level l > LT: window m sums windows m*p .. m*p+p-1 of level l-1 (those the
+// level below holds; the rest cover no row), one lane group per (head, window).
+template <int D>
+__global__ __launch_bounds__(256) void k_scatter_bwd_up(ScatterBwdArgs a, int l)
+{
+    constexpr int LANES = D / 8, NLG = 256 / LANES;
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES, col = lane * 8;
+    const int P = 1 << a.log2p;
+    const int64_t below = a.part_n[l - 1], ml = (below + P - 1) / P;
+    const int64_t item = (int64_t)blockIdx.x * NLG + lg;
+    if (item >= (int64_t)a.H * ml)
+        return;
+    const int h = (int)(item / ml);
+    const int64_t m = item - (int64_t)h * ml;
+    const float *src = a.part + ((int64_t)h * a.part_rows + a.part_off[l - 1]) * D + col;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.0f;
+    for (int c = 0; c < P; ++c) {
+        const int64_t mc = m * P + c;
+        if (mc < below) {
+            float x[8];
+            load8(src + mc * D, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] += x[e];
+        }
+    }
+    const int64_t i = m - 1;
+    if (i >= 0 && i < (a.N >> (l * a.log2p))) {
+        const int32_t sl = a.slot[(int64_t)h * a.lvl_total + a.lvl_off[l] + i];
+        if ((uint32_t)sl < (uint32_t)a.S_pad)
+            store8(a.dosub + ((int64_t)h * a.S_pad + sl) * D + col, acc);
+    }
+    if (l < a.L - 1)
+        store8(a.part + ((int64_t)h * a.part_rows + a.part_off[l] + m) * D + col, acc);
+}
+
+template <int D, lh_dtype DT, int LP>
+static hipError_t launch_scatter_bwd_t(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s)
+{
+    constexpr int T = TileShape<D, LP>::T, NLG = 256 / (D / 8);
+    const dim3 grid((unsigned)((pl.N + 1 + T - 1) / T), (unsigned)pl.H);
+    hipLaunchKernelGGL((k_scatter_bwd<D, DT, LP>), grid, dim3(256), 0, s, a);
+    for (int l = pl.LT + 1; l < pl.L; ++l) {
+        const int64_t ml = (pl.spart_n[l - 1] + pl.p - 1) / pl.p;
+        const int64_t items = (int64_t)pl.H * ml;
+        hipLaunchKernelGGL((k_scatter_bwd_up<D>), dim3((unsigned)((items + NLG - 1) / NLG)), dim3(256), 0, s, a, l);
+    }
+    return hipGetLastError();
 }
 
 template <int D, lh_dtype DT>
-static void launch_scatter_bwd_t(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s)
+static hipError_t launch_scatter_bwd_p(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s)
 {
-    constexpr int NLG = 256 / (D / 8);
-    const int64_t runs = (int64_t)a.H * a.tiles_per_head;
-    const dim3 grid((unsigned)((runs + NLG - 1) / NLG));
-    switch (pl.L) {
-    case 1: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 5>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 6>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 7>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_scatter_bwd<D, DT, 8>), grid, dim3(256), 0, s, a); break;
+    switch (pl.log2p) {
+    case 1: return launch_scatter_bwd_t<D, DT, 1>(pl, a, s);
+    case 2: return launch_scatter_bwd_t<D, DT, 2>(pl, a, s);
+    default: return launch_scatter_bwd_t<D, DT, 3>(pl, a, s);
     }
 }
 
 hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s)
 {
-    if (pl.d == 128) {
-        if (pl.dt == LH_BF16)
-            launch_scatter_bwd_t<128, LH_BF16>(pl, a, s);
-        else
-            launch_scatter_bwd_t<128, LH_F32>(pl, a, s);
-    } else {
-        if (pl.dt == LH_BF16)
-            launch_scatter_bwd_t<64, LH_BF16>(pl, a, s);
-        else
-            launch_scatter_bwd_t<64, LH_F32>(pl, a, s);
-    }
-    return hipGetLastError();
+    if (pl.d == 128)
+        return pl.dt == LH_BF16 ? launch_scatter_bwd_p<128, LH_BF16>(pl, a, s)
+                                : launch_scatter_bwd_p<128, LH_F32>(pl, a, s);
+    return pl.dt == LH_BF16 ? launch_scatter_bwd_p<64, LH_BF16>(pl, a, s)
+                            : launch_scatter_bwd_p<64, LH_F32>(pl, a, s);
 }
 
 // ---------------------------------------------------------------- backward prep

@@ -59,6 +59,20 @@ def test_backward_L5_p4_shape_of_512k():
     _case(32768, 2, 128, 5, 4, 32, n_plant=32, bwd=True, tag="bwd-L5")
 
 
+def test_upper_levels_p4_L6():
+    # levels 4 and 5 lie above the row tiles of the front pass and of the
+    # scatter-back adjoint: they are built from the window sums of the level below
+    _case(8192, 2, 128, 6, 4, 4, n_plant=4, bwd=True, tag="up-p4-L6")
+
+
+def test_upper_levels_p8_L4_d64():
+    _case(8192, 2, 64, 4, 8, 8, n_plant=4, bwd=True, tag="up-p8-L4")
+
+
+def test_upper_levels_p2_L8():
+    _case(8192, 2, 128, 8, 2, 16, n_plant=4, bwd=True, tag="up-p2-L8")
+
+
 def test_dense_L1_fwd_bwd_ragged():
     # L = 1: S = N, dense causal attention; N = 1000 is not a multiple of any tile
     _case(1000, 2, 64, 1, 2, 0, bwd=True, tag="L1")
