@@ -1,6 +1,9 @@
 """Throughput of the Lighthouse layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--copy-calibration]
+    python bench.py --summarize-stats DIR              (rocprofv3 --stats output -> markdown)
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR [--workload NAME]
 
 A step is one lh_forward + lh_backward over the whole workload (every stage
 of the path, all heads), inputs resident in HBM. The default workload is the
@@ -12,6 +15,15 @@ Per-kernel timing: the library records caller-created HIP events between its
 stages on the launch stream (lh_forward_timed / lh_backward_timed), so every
 stage's average launch duration is measured inside the timed region. The
 roofline object describes the stage with the largest share of the step.
+
+HBM traffic: two rocprofv3 counter runs of this script with
+--copy-calibration (one with --pmc FETCH_SIZE, one with --pmc WRITE_SIZE)
+see, besides the layer's kernels, one elementwise kernel that reads and
+writes exactly 1 GiB; the ratio of those bytes to what the counters report
+for it scales the layer's kernels. --summarize-traffic writes the scaled
+bytes per launch of every stage to profiles/traffic_<stage>_<workload>.json,
+tagged with the digest of the kernel sources, and the "traffic" field of
+the roofline object is read from there only while the sources still match.
 """
 from __future__ import annotations
 
@@ -30,6 +42,31 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, datasheet
 MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16 / bf16 matrix, datasheet
 
 MFMA_STAGES = {"attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"}
+
+# rocprofv3 kernel names -> stages of the path
+KERNEL_STAGES = [
+    (r"lh::k_front(_up)?<", "front"),
+    (r"lh::k_topk\(", "topk"),
+    (r"lh::k_index\(", "index"),
+    (r"lh::k_gather<", "gather"),
+    (r"lh::k_attn_fwd<", "attn_fwd"),
+    (r"lh::k_pull<\d+, [^,]+, 1, 1,", "scatter"),
+    (r"lh::k_scatter_bwd(_up)?<", "scatter_bwd"),
+    (r"lh::k_bwd_prep<", "bwd_prep"),
+    (r"lh::k_attn_bwd_dkdv<", "attn_bwd_dkdv"),
+    (r"lh::k_attn_bwd_dq<", "attn_bwd_dq"),
+    (r"lh::k_pull<\d+, [^,]+, 3, 0,", "pool_bwd"),
+]
+CALIB_BYTES = 1 << 30        # the calibration kernel reads and writes this many bytes
+CALIB_PATTERN = r"neg_kernel"
+
+
+def stage_of(kernel_name: str):
+    import re
+    for pat, stage in KERNEL_STAGES:
+        if re.search(pat, kernel_name):
+            return stage
+    return None
 
 
 def algorithmic(stage: str, w, S: int) -> float:
@@ -129,6 +166,70 @@ def load_traffic(stage: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def summarize_stats(d: str) -> None:
+    """Markdown table of a rocprofv3 --stats run: per stage of the path, the
+    kernels, their launches and average duration."""
+    import csv
+    path = os.path.join(d, "run_kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    print("| stage | kernel | calls | avg us | total ms |")
+    print("|---|---|---:|---:|---:|")
+    for r in rows:
+        st = stage_of(r["Name"])
+        if st is None:
+            continue
+        print("| %s | `%s` | %s | %.1f | %.2f |" % (st, r["Name"].replace("void ", "")[:70], r["Calls"],
+                                                 float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
+    """Per-stage HBM bytes per step from two counter runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), scaled by the calibration kernel's known
+    1 GiB read and write; writes profiles/traffic_<stage>_<workload>.json."""
+    import csv
+    import re
+    from collections import defaultdict
+    from sparse_long_context_lh_amd.build import source_digest
+
+    def per_stage(d, counter):
+        tot, calls, calib = defaultdict(float), defaultdict(set), []
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if re.search(CALIB_PATTERN, r["Kernel_Name"]):
+                calib.append(v)
+                continue
+            st = stage_of(r["Kernel_Name"])
+            if st is not None:
+                tot[st] += v
+                calls[(st, r["Kernel_Name"])].add(r["Dispatch_Id"])
+        if not calib:
+            raise SystemExit("no calibration kernel in %s (run bench.py with --copy-calibration)" % d)
+        # launches of each stage = launches of any one of its kernels
+        n = {}
+        for (st, _), ids in calls.items():
+            n[st] = max(n.get(st, 0), len(ids))
+        scale = CALIB_BYTES / (sum(calib) / len(calib))
+        return {st: tot[st] / n[st] * scale for st in tot}, scale
+
+    fetch, fs = per_stage(fetch_dir, "FETCH_SIZE")
+    write, wsc = per_stage(write_dir, "WRITE_SIZE")
+    digest = source_digest()
+    print("calibration: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (fs, wsc))
+    print("| stage | read MB / step | written MB / step | total MB |")
+    print("|---|---:|---:|---:|")
+    for st in sorted(fetch, key=lambda x: -(fetch[x] + write.get(x, 0.0))):
+        total = fetch[st] + write.get(st, 0.0)
+        print("| %s | %.1f | %.1f | %.1f |" % (st, fetch[st] / 1e6, write.get(st, 0.0) / 1e6, total / 1e6))
+        rec = {"stage": st, "workload": workload, "bytes_per_launch": round(total), "read_bytes": round(fetch[st]),
+               "written_bytes": round(write.get(st, 0.0)), "fetch_scale": fs, "write_scale": wsc,
+               "source_digest": digest}
+        with open(os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (st, workload)), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +237,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lh-fwdbwd-512k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB read + 1 GiB write elementwise kernel before the warmup")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, workload=args.workload)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer here has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -167,6 +278,13 @@ def main():
         lh.forward(q, k, v, w.L, w.p, w.k, ws=ws, out=out, stream=stream, events=evf)
         lh.backward(dout, w.L, w.p, w.k, ws, dq, dk, dv, stream=stream, events=evb)
 
+    if args.copy_calibration:
+        src = torch.full((CALIB_BYTES // 4,), 7, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

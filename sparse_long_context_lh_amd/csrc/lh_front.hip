@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
     typedef TileShape<D, LP> Sh;
     constexpr int LANES = Sh::LANES, NLG = Sh::NLG, NC = Sh::NC, R = Sh::R, P = 1 << LP;
     __shared__ __attribute__((aligned(16))) float s_sum[3][NLG][D];
-    __shared__ float s_max[NLG];
+    // scores of the tile, level after level (T / p^l each): written to memory
+    // at the end as whole lines
+    __shared__ float s_sc[2 * Sh::T];
     const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES, col = lane * 8;
     const int h = blockIdx.y;
     const int64_t x0 = (int64_t)blockIdx.x * Sh::T;
@@ -87,11 +89,6 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         }
         if (keep && l == LT)
             store8(part + t * pstride + (a.part_off[l] + i) * D, acc);
-    };
-    auto put_max = [&](int l, int64_t i, float m) {
-        sc[a.lvl_off[l] + i] = m;
-        if (keep && l == LT)
-            pmax[a.part_off[l] + i] = m;
     };
 
     const int64_t in_off = ((int64_t)h * a.N + j0) * D + col;
@@ -121,40 +118,12 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         const float nk = row_norm2<LANES>(x);
         s[r] = sqrtf(nq) + sqrtf(nk);
     }
-#pragma unroll
-    for (int r0 = 0; r0 < R; r0 += LANES) {
-        constexpr int W = R < LANES ? R : LANES;
-        float v[W];
-#pragma unroll
-        for (int i = 0; i < W; ++i)
-            v[i] = s[r0 + i];
-        const float mine = pick<W>(v, lane);
-        if (lane < W && j0 + r0 + lane < a.N)
-            sc[j0 + r0 + lane] = mine;
+    static_assert(R <= LANES, "a lane group stages its run's scores with one store");
+    {
+        const float mine = pick<R>(s, lane);
+        if (lane < R)
+            s_sc[lg * R + lane] = mine;
     }
-    float mx[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        mx[r] = s[r];
-#pragma unroll
-    for (int l = 1; l <= NC; ++l) {
-        const int cnt = R / ipow(P, l);
-#pragma unroll
-        for (int w = 0; w < R; ++w) {
-            if (w < cnt) {
-                float m = mx[w * P];
-#pragma unroll
-                for (int c = 1; c < P; ++c)
-                    m = fmaxf(m, mx[w * P + c]);
-                mx[w] = m;
-            }
-        }
-        const int64_t i = (j0 >> (l * LP)) + lane;
-        const float mine = pick<R>(mx, lane);
-        if (l <= LT && lane < cnt && i < (a.N >> (l * LP)))
-            put_max(l, i, mine);
-    }
-    const float run_max = mx[0];
 
     // window sums of the run, tensor after tensor
     float tot[3][8];
@@ -210,14 +179,12 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
             *reinterpret_cast<float4 *>(&s_sum[t][lg][col]) = make_float4(tot[t][0], tot[t][1], tot[t][2], tot[t][3]);
             *reinterpret_cast<float4 *>(&s_sum[t][lg][col + 4]) = make_float4(tot[t][4], tot[t][5], tot[t][6], tot[t][7]);
         }
-        if (lane == 0)
-            s_max[lg] = run_max;
         __syncthreads();
         int W = NLG;
         for (int l = NC + 1; l <= LT; ++l) {
             W /= P;
             const int64_t nl = a.N >> (l * LP);
-            float res[2][8], rmx = 0.0f;
+            float res[2][8];
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int task = lg + n * NLG;
@@ -235,14 +202,6 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
                     const int64_t i = (x0 >> (l * LP)) + w;
                     if (i < nl)
                         put_sum(t, l, i, res[n]);
-                    if (t == 0) {
-                        float m = s_max[w * P];
-                        for (int c = 1; c < P; ++c)
-                            m = fmaxf(m, s_max[w * P + c]);
-                        rmx = m;
-                        if (lane == 0 && i < nl)
-                            put_max(l, i, m);
-                    }
                 }
             }
             __syncthreads();
@@ -253,12 +212,40 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
                     const int t = task / W, w = task - t * W;
                     *reinterpret_cast<float4 *>(&s_sum[t][w][col]) = make_float4(res[n][0], res[n][1], res[n][2], res[n][3]);
                     *reinterpret_cast<float4 *>(&s_sum[t][w][col + 4]) = make_float4(res[n][4], res[n][5], res[n][6], res[n][7]);
-                    if (t == 0 && lane == 0)
-                        s_max[w] = rmx;
                 }
             }
             __syncthreads();
         }
+    }
+
+    // score maxima of levels 1..LT over the tile, then every level's scores
+    // to memory with consecutive threads on consecutive entries
+    __syncthreads();
+    int b = 0;
+    for (int l = 1; l <= LT; ++l) {
+        const int below = Sh::T >> ((l - 1) * LP), cnt = below / P;
+        for (int e = threadIdx.x; e < cnt; e += 256) {
+            float m = s_sc[b + e * P];
+#pragma unroll
+            for (int c = 1; c < P; ++c)
+                m = fmaxf(m, s_sc[b + e * P + c]);
+            s_sc[b + below + e] = m;
+        }
+        b += below;
+        __syncthreads();
+    }
+    b = 0;
+    for (int l = 0; l <= LT; ++l) {
+        const int cnt = Sh::T >> (l * LP);
+        const int64_t i0 = x0 >> (l * LP), nl = a.N >> (l * LP);
+        for (int e = threadIdx.x; e < cnt; e += 256) {
+            if (i0 + e < nl) {
+                sc[a.lvl_off[l] + i0 + e] = s_sc[b + e];
+                if (keep && l == LT)
+                    pmax[a.part_off[l] + i0 + e] = s_sc[b + e];
+            }
+        }
+        b += cnt;
     }
 }
 

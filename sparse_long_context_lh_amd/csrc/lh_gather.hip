@@ -25,58 +25,72 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     constexpr int LANES = D / 8;
     constexpr int NLG = 256 / LANES;
     constexpr int LD = D + 8; // LDS row pitch in bf16 (16 B pad)
+    constexpr int CHUNK = 4;  // window rows in flight per tensor
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
+    __shared__ int32_t s_ent[kGatherTile];
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
     const int lane = threadIdx.x % LANES;
     const int lg = threadIdx.x / LANES;
     const T *src[3] = {reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
                        reinterpret_cast<const T *>(a.v)};
+    if (threadIdx.x < kGatherTile)
+        s_ent[threadIdx.x] = a.ent[(int64_t)h * a.S_pad + s0 + threadIdx.x];
+    __syncthreads();
 
     for (int r = lg; r < kGatherTile; r += NLG) {
         const int64_t s = s0 + r;
-        const int32_t en = a.ent[(int64_t)h * a.S_pad + s];
+        const int32_t en = s_ent[r];
         float x[3][8];
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x[t][e] = 0.0f;
         // an entry outside the pyramid (never produced by the index kernel) reads as zeros
-        if (en < 0 || (en & 7) >= a.L || (int64_t)(en >> 3) >= a.n[en & 7]) {
+        const bool valid = en >= 0 && (en & 7) < a.L && (int64_t)(en >> 3) < a.n[en & 7];
+        const int l = en & 7;
+        const int64_t i = (int64_t)(en >> 3);
+        if (valid && l > 0 && a.mat_off[l] >= 0) {
 #pragma unroll
             for (int t = 0; t < 3; ++t)
+                load8(a.pooled + t * a.tensor_stride + ((int64_t)h * a.mat_rows + a.mat_off[l] + i) * D + lane * 8,
+                      x[t]);
+        } else if (valid) {
+            // level 0: the input row; other levels: the mean of the p^l input
+            // rows, summed in ascending order from 0 (CHUNK rows per round trip)
+            const int sh = l * a.log2p;
+            const int w = 1 << sh;
+            const int64_t row0 = ((int64_t)h * a.N + (i << sh)) * D + lane * 8;
+            for (int j = 0; j < w; j += CHUNK) {
+                Raw8<DT> y[3][CHUNK];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    x[t][e] = 0.0f;
-        } else {
-            const int l = en & 7;
-            const int64_t i = (int64_t)(en >> 3);
-            if (l == 0) {
+                for (int u = 0; u < CHUNK; ++u)
 #pragma unroll
-                for (int t = 0; t < 3; ++t)
-                    load8(src[t] + ((int64_t)h * a.N + i) * D + lane * 8, x[t]);
-            } else if (a.mat_off[l] >= 0) {
+                    for (int t = 0; t < 3; ++t) {
+                        if (j + u < w)
+                            ld_raw(src[t] + row0 + (int64_t)(j + u) * D, y[t][u]);
+                        else
+                            zero_raw(y[t][u]);
+                    }
 #pragma unroll
-                for (int t = 0; t < 3; ++t)
-                    load8(a.pooled + t * a.tensor_stride + ((int64_t)h * a.mat_rows + a.mat_off[l] + i) * D + lane * 8,
-                          x[t]);
-            } else {
-                const int sh = l * a.log2p;
-                const int64_t w = int64_t(1) << sh;
+                for (int u = 0; u < CHUNK; ++u)
 #pragma unroll
-                for (int t = 0; t < 3; ++t) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[t][e] = 0.0f;
-                    const T *p0 = src[t] + ((int64_t)h * a.N + (i << sh)) * D + lane * 8;
-                    for (int64_t j = 0; j < w; ++j) {
-                        float y[8];
-                        load8(p0 + j * D, y);
+                    for (int t = 0; t < 3; ++t) {
+                        float z[8];
+                        unraw(y[t][u], z);
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            x[t][e] += y[e];
+                            x[t][e] += z[e];
                     }
-                    const float inv = 1.0f / (float)w; // exact: power of two
+            }
+            if (l > 0) {
+                const float inv = 1.0f / (float)w; // exact: power of two
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         x[t][e] *= inv;
-                }
             }
         }
         const int64_t off = ((int64_t)h * a.S_pad + s) * D + lane * 8;
