@@ -40,6 +40,8 @@
 // resulting O_sub error is amplified by delta); the scale cancels against the
 // normaliser (forward) or is divided out of dV (backward). The log-sum-exp is
 // kept in the log2 domain of the scaled logits, as the backward uses it.
+#include <type_traits>
+
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -260,6 +262,27 @@ __device__ __forceinline__ void async16(const void *g, const uint4 *lds_wave_bas
 
 __device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same transfer issued from inline assembly, for the multi-stage rings of
+// the backward kernels: the compiler then does not track these LDS writes, so
+// it inserts no wait for them before reading other stages of the ring (its
+// own tracking of LDS DMA is coarse and would wait for every transfer in
+// flight). The kernels wait themselves (s_waitcnt vmcnt(n), then an LDS
+// barrier) before reading a stage. M0 takes the wave's LDS base; one wait
+// state separates its write from the transfer that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm" // M0 is reserved: nothing else in these kernels keeps it live
+__device__ __forceinline__ void async16_nc(const void *g, const uint4 *lds_wave_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier without a memory fence (the fence of __syncthreads would
+// wait for every transfer in flight); LDS reads of this wave are complete.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Generic swizzle for NCH chunks per row: rows per 256-byte bank window are
 // 16/NCH; XOR the chunk with the window index so 16 consecutive rows map the
 // same logical chunk to 16 distinct bank groups.
@@ -270,8 +293,10 @@ __device__ __forceinline__ int swzg(int row, int ch)
 }
 
 // ============================================================== backward: dK, dV
-// One workgroup per 128 keys (32 per wave, K/V rows in registers); queries
-// stream through LDS 32 at a time from the key block onwards, double-buffered.
+// One workgroup per 128 keys (32 per wave; K hi, K lo and V rows of the
+// lane's key in registers); queries stream through LDS 32 at a time from the
+// key block onwards, in a three-deep ring of stages filled asynchronously
+// (two stages are in flight while one is used).
 // S = Q K^T with queries as (permuted) rows, so a lane owns one key:
 //   dV^T += dO^T P,  dP = dO V^T,  dS = P * (dP - delta),  dK^T += Q^T dS.
 template <int D>
@@ -284,9 +309,20 @@ struct DkdvStage {
     static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS, QT = 4 * ROWS, DT = 4 * ROWS + COLS;
     static constexpr int LS = 4 * ROWS + 2 * COLS; // lse (BQ floats), then delta (BQ floats)
     static constexpr int SIZE = LS + BQ / 2;        // in 16-byte chunks
-    static constexpr int KLO = 2 * SIZE;            // after the two stages: the block's K lo rows [128][RCH]
-    static constexpr int TOTAL = KLO + 128 * RCH;
+    static constexpr int NBUF = 3;
+    // global_load_lds instructions one wave issues per stage
+    static constexpr int LOADS = 4 * (ROWS / 256) + 2 * (COLS / 256) + 1;
 };
+
+// Keeps the compiler from moving instructions across this point: used to
+// interleave each matrix product with the LDS read of a later operand.
+#define LH_FENCE __builtin_amdgcn_sched_barrier(0)
+
+template <int N>
+__device__ __forceinline__ void wait_async_n()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
@@ -295,7 +331,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
     constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
-    extern __shared__ uint4 lds_dkdv[]; // two stages
+    // The ring is three separate arrays and every access names its array at
+    // compile time: the compiler then knows that reads of the current stage do
+    // not alias the asynchronous writes of a later one, and does not wait for
+    // those writes before the reads.
+    __shared__ uint4 sb0[St::SIZE], sb1[St::SIZE], sb2[St::SIZE];
 
     const int h = blockIdx.x % a.H;
     const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
@@ -321,45 +361,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
     const uint16_t *const cols[2] = {a.qhi_t, a.dohi_t};
+    // lanes 0..3 of every wave fetch 4 of the 16 lse / delta chunks, so each
+    // wave issues the same number of loads per stage (St::LOADS)
+    const float *stat = wave < 2 ? a.lse : a.delta;
+    const int stat_off = 4 * ((4 * wave + (lane & 3)) & 7);
 
-    auto issue = [&](int q0, int buf) {
-        const uint4 *base = lds_dkdv + buf * St::SIZE + 64 * wave;
+    auto issue = [&](int q0, const uint4 *base) {
+        if (lane < 4) // lanes 0..3 write chunks LS + 4 * wave + lane
+            async16_nc(stat + hS + q0 + stat_off, base + St::LS + 4 * wave);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint16_t *rb = rows[t] + (hS + q0) * D;
 #pragma unroll
             for (int u = 0; u < RU; ++u)
-                async16(rb + roff[u], base + t * St::ROWS + 256 * u);
+                async16_nc(rb + roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
 #pragma unroll
             for (int u = 0; u < TU; ++u)
-                async16(cb + toff[u], base + St::QT + t * St::COLS + 256 * u);
-        }
-        if (tid < BQ / 2) { // 8 chunks of lse, 8 of delta (wave 0)
-            const float *arr = tid < BQ / 4 ? a.lse : a.delta;
-            async16(arr + hS + q0 + 4 * (tid % (BQ / 4)), lds_dkdv + buf * St::SIZE + St::LS);
+                async16_nc(cb + toff[u], base + 64 * wave + St::QT + t * St::COLS + 256 * u);
         }
     };
 
-    // K hi and V fragments of this lane's key stay in registers; the K lo rows
-    // of the block go to LDS (registers are the limit: keeping all three there
-    // makes the compiler shuttle values through accumulation registers).
-    uint4 kh[NS], vf[NS];
+    uint4 kh[NS], klf[NS], vf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t off = (hS + key) * D + 16 * s + 8 * g;
         kh[s] = ld16(a.khi + off);
+        klf[s] = ld16(a.klo + off);
         vf[s] = ld16(a.v + off);
     }
-    uint4 *sKl = lds_dkdv + St::KLO;
-    for (int c = tid; c < 128 * RCH; c += 256) {
-        const int r = c / RCH, ch = c % RCH;
-        sKl[r * RCH + swzg<RCH>(r, ch)] = ld16(a.klo + (hS + k0 + r) * D + ch * 8);
-    }
-    const int krow = wave * 32 + c32; // this lane's key row in sKl
     f32x16_t dvT[NT], dkT[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -369,52 +402,129 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int ql = kappa(c32);
     const int nst = (S - k0 + BQ - 1) / BQ;
 
-    issue(k0, 0);
-    for (int it = 0; it < nst; ++it) {
+    auto stage = [&](auto bidx, int it) __attribute__((always_inline)) {
+        constexpr int B = decltype(bidx)::value;
+        const uint4 *base = B == 0 ? sb0 : (B == 1 ? sb1 : sb2);
+        const uint4 *ahead = B == 0 ? sb2 : (B == 1 ? sb0 : sb1); // ring slot of stage it + 2
         const int q0 = k0 + it * BQ;
-        wait_async();
-        __syncthreads(); // this stage landed everywhere; the other buffer is free
+        // stage it has landed once at most one stage's loads are outstanding
         if (it + 1 < nst)
-            issue(q0 + BQ, (it + 1) & 1);
+            wait_async_n<St::LOADS>();
+        else
+            wait_async();
+        lds_barrier(); // stage it is visible to all waves; stage it-1's slot is free
+        if (it + 2 < nst)
+            issue(q0 + 2 * BQ, ahead);
         // (near the diagonal a wave may find every query of the stage before its
         // keys; the mask below zeroes that stage rather than branching around it)
-        const uint4 *base = lds_dkdv + (it & 1) * St::SIZE;
         const float *sL = reinterpret_cast<const float *>(base + St::LS);
         const float *sDel = sL + BQ;
+
+        // S and dP. The operands of k-step s+1 are read while the products of
+        // step s run (one LDS read between consecutive products).
         f32x16_t st = zero16(), dp = zero16();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        uint4 fa[4], fb[4];
+        auto rd = [&](int s, int i) {
             const int at = ql * RCH + swzg<RCH>(ql, 2 * s + g);
-            const uint4 q_h = base[St::QH + at];
-            st = mfma32(q_h, kh[s], st);
-            st = mfma32(base[St::QL + at], kh[s], st);
-            st = mfma32(q_h, sKl[krow * RCH + swzg<RCH>(krow, 2 * s + g)], st);
-            dp = mfma32(base[St::DH + at], vf[s], dp);
-            dp = mfma32(base[St::DL + at], vf[s], dp);
+            return base[(i == 0 ? St::QH : i == 1 ? St::QL : i == 2 ? St::DH : St::DL) + at];
+        };
+        auto step = [&](int s, const uint4 (&f)[4], uint4 (&nx)[4], bool pre) {
+            if (pre) nx[0] = rd(s + 1, 0);
+            LH_FENCE;
+            st = mfma32(f[0], kh[s], st);
+            LH_FENCE;
+            if (pre) nx[1] = rd(s + 1, 1);
+            LH_FENCE;
+            st = mfma32(f[1], kh[s], st);
+            LH_FENCE;
+            if (pre) nx[2] = rd(s + 1, 2);
+            LH_FENCE;
+            st = mfma32(f[0], klf[s], st);
+            LH_FENCE;
+            if (pre) nx[3] = rd(s + 1, 3);
+            LH_FENCE;
+            dp = mfma32(f[2], vf[s], dp);
+            LH_FENCE;
+            dp = mfma32(f[3], vf[s], dp);
+            LH_FENCE;
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[i] = rd(0, i);
+#pragma unroll
+        for (int s = 0; s < NS; s += 2) {
+            step(s, fa, fb, true);
+            step(s + 1, fb, fa, s + 2 < NS);
+        }
+
+        // the first dV / dK operands and the row statistics load while the
+        // last products drain
+        auto gfrag = [&](int t, int i) {
+            const int dim = 32 * t + c32;
+            const int c = dim * TCH + swzg<TCH>(dim, (i & 1) * 2 + g);
+            return base[(i < 2 ? St::DT : St::QT) + c];
+        };
+        uint4 ga[4], gb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ga[i] = gfrag(0, i);
+        float lq[16], dlt[16];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float4 l0 = *reinterpret_cast<const float4 *>(sL + 16 * hh + 8 * g);
+            const float4 l1 = *reinterpret_cast<const float4 *>(sL + 16 * hh + 8 * g + 4);
+            const float4 d0 = *reinterpret_cast<const float4 *>(sDel + 16 * hh + 8 * g);
+            const float4 d1 = *reinterpret_cast<const float4 *>(sDel + 16 * hh + 8 * g + 4);
+            lq[8 * hh + 0] = l0.x; lq[8 * hh + 1] = l0.y; lq[8 * hh + 2] = l0.z; lq[8 * hh + 3] = l0.w;
+            lq[8 * hh + 4] = l1.x; lq[8 * hh + 5] = l1.y; lq[8 * hh + 6] = l1.z; lq[8 * hh + 7] = l1.w;
+            dlt[8 * hh + 0] = d0.x; dlt[8 * hh + 1] = d0.y; dlt[8 * hh + 2] = d0.z; dlt[8 * hh + 3] = d0.w;
+            dlt[8 * hh + 4] = d1.x; dlt[8 * hh + 5] = d1.y; dlt[8 * hh + 6] = d1.z; dlt[8 * hh + 7] = d1.w;
         }
         float pr[16], ds[16];
         const int rel = q0 - key; // query - key of register 0's query
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
-            const float lq = sL[qi], dq = sDel[qi]; // read unconditionally: the selects stay branch-free
             const bool ok = rel + qi >= 0 && q0 + qi < S;
-            const float pv = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lq : -INFINITY);
-            ds[v] = ok ? pv * (dp[v] - dq) : 0.0f;
+            const float pv = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lq[v] : -INFINITY);
+            ds[v] = ok ? pv * (dp[v] - dlt[v]) : 0.0f;
             pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
         }
         const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+        auto gstep = [&](int t, const uint4 (&f)[4], uint4 (&nx)[4], bool pre) {
+            if (pre) nx[0] = gfrag(t + 1, 0);
+            LH_FENCE;
+            dvT[t] = mfma32(f[0], pb0, dvT[t]);
+            LH_FENCE;
+            if (pre) nx[1] = gfrag(t + 1, 1);
+            LH_FENCE;
+            dvT[t] = mfma32(f[1], pb1, dvT[t]);
+            LH_FENCE;
+            if (pre) nx[2] = gfrag(t + 1, 2);
+            LH_FENCE;
+            dkT[t] = mfma32(f[2], db0, dkT[t]);
+            LH_FENCE;
+            if (pre) nx[3] = gfrag(t + 1, 3);
+            LH_FENCE;
+            dkT[t] = mfma32(f[3], db1, dkT[t]);
+            LH_FENCE;
+        };
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int dim = 32 * t + c32;
-            const int c0 = dim * TCH + swzg<TCH>(dim, g);
-            const int c1 = dim * TCH + swzg<TCH>(dim, 2 + g);
-            dvT[t] = mfma32(base[St::DT + c0], pb0, dvT[t]);
-            dvT[t] = mfma32(base[St::DT + c1], pb1, dvT[t]);
-            dkT[t] = mfma32(base[St::QT + c0], db0, dkT[t]);
-            dkT[t] = mfma32(base[St::QT + c1], db1, dkT[t]);
+        for (int t = 0; t < NT; t += 2) {
+            gstep(t, ga, gb, true);
+            gstep(t + 1, gb, ga, t + 2 < NT);
         }
+    };
+    issue(k0, sb0);
+    if (nst > 1)
+        issue(k0 + BQ, sb1);
+    for (int it = 0; it < nst; it += 3) {
+        stage(std::integral_constant<int, 0>(), it);
+        if (it + 1 < nst)
+            stage(std::integral_constant<int, 1>(), it + 1);
+        if (it + 2 < nst)
+            stage(std::integral_constant<int, 2>(), it + 2);
     }
 
     float *dk = a.dk + (hS + key) * D;
@@ -435,11 +545,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D>
 static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
 {
-    const size_t lds = (size_t)DkdvStage<D>::TOTAL * sizeof(uint4);
-    if (lds > 65536)
-        (void)hipFuncSetAttribute((const void *)k_attn_bwd_dkdv<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds);
-    hipLaunchKernelGGL((k_attn_bwd_dkdv<D>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_attn_bwd_dkdv<D>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
@@ -473,7 +579,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     typedef DqStage<D> St;
     constexpr int BM = 128, BN = St::BN, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
-    extern __shared__ uint4 lds_dq[]; // two stages
+    // two stages, separate arrays named at compile time (see the dK/dV kernel)
+    __shared__ uint4 sq0[St::SIZE], sq1[St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -484,22 +591,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t hS = (int64_t)h * a.S_pad;
     const int64_t query = qw + c32;
 
-    auto issue = [&](int64_t k0, int buf) {
-        const uint4 *base = lds_dq + buf * St::SIZE;
+    const uint16_t *const khi = a.khi, *const klo = a.klo, *const vv = a.v, *const kht = a.khi_t;
+    auto issue = [&](int64_t k0, const uint4 *base) {
 #pragma unroll
         for (int u = 0; u < St::SIZE / 256; ++u) {
             const int c = 256 * u + tid;
             const uint4 *wb = base + 256 * u + 64 * wave;
             const void *src;
-            if (c < St::KT) {
-                const int t = c / St::ROWS, cc = c % St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
-                const uint16_t *arr = t == 0 ? a.khi : t == 1 ? a.klo : a.v;
+            if (256 * u < St::KT) { // round u lies in one row-major tile (ROWS is a multiple of 256)
+                const int t = 256 * u / St::ROWS;
+                const int cc = c - t * St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
+                const uint16_t *arr = t == 0 ? khi : (t == 1 ? klo : vv);
                 src = arr + (hS + k0 + r) * D + ch * 8;
             } else {
                 const int cc = c - St::KT, dim = cc / TCH, ch = swzg<TCH>(dim, cc % TCH);
-                src = a.khi_t + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8;
+                src = kht + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8;
             }
-            async16(src, wb);
+            async16_nc(src, wb);
         }
     };
 
@@ -523,14 +631,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
 
-    issue(0, 0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    auto stage = [&](auto bidx, int kb) __attribute__((always_inline)) {
+        constexpr int B = decltype(bidx)::value;
+        const uint4 *base = B == 0 ? sq0 : sq1;
         const int64_t k0 = (int64_t)kb * BN;
         wait_async();
-        __syncthreads();
+        lds_barrier(); // stage kb is visible to all waves; the other slot is free
         if (kb + 1 < nkb)
-            issue(k0 + BN, (kb + 1) & 1);
-        const uint4 *base = lds_dq + (kb & 1) * St::SIZE;
+            issue(k0 + BN, B == 0 ? sq1 : sq0);
         // (in the diagonal block a wave may find a subtile entirely after its
         // queries; the mask below zeroes it rather than branching around it)
 #pragma unroll
@@ -566,6 +674,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + 2 + g)], db1, dqT[t]);
             }
         }
+    };
+    issue(0, sq0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        stage(std::integral_constant<int, 0>(), kb);
+        if (kb + 1 < nkb)
+            stage(std::integral_constant<int, 1>(), kb + 1);
     }
 
     float *dq = a.dq + (hS + query) * D;
@@ -581,11 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D>
 static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
 {
-    const size_t lds = 2 * (size_t)DqStage<D>::SIZE * sizeof(uint4);
-    if (lds > 65536)
-        (void)hipFuncSetAttribute((const void *)k_attn_bwd_dq<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds);
-    hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
