@@ -128,6 +128,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_POOLED] = 4 * 3 * Hs * (size_t)pl->mat_rows * D;
     b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
+    b[IR_LSE15] = 4 * Hs * Sp;
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
     size_t off = 0;
@@ -326,6 +327,8 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         a.dohi = at<uint16_t>(ws, pl, IR_DOHI); a.dolo = at<uint16_t>(ws, pl, IR_DOLO);
         a.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
         a.delta = at<float>(ws, pl, IR_DELTA);
+        a.lse = at<float>(ws, pl, LH_R_LSE);
+        a.lse15 = at<float>(ws, pl, IR_LSE15);
         a.S = pl.S; a.S_pad = pl.S_pad; a.H = H;
         if (launch_bwd_prep(pl, a, s) != hipSuccess)
             return LH_EHIP;
@@ -342,7 +345,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);
     ab.dolo = at<uint16_t>(ws, pl, IR_DOLO);
     ab.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
-    ab.lse = at<float>(ws, pl, LH_R_LSE);
+    ab.lse = at<float>(ws, pl, IR_LSE15);
     ab.delta = at<float>(ws, pl, IR_DELTA);
     ab.dq = at<float>(ws, pl, LH_R_DQSUB);
     ab.dk = at<float>(ws, pl, LH_R_DKSUB);

@@ -90,30 +90,109 @@ __device__ __forceinline__ f32x16_t zero16()
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// ============================================================== async staging
+// global_load_lds_dwordx4: each lane fetches 16 bytes from its own global
+// address and the wave writes them to LDS at M0 + 16 * lane (M0 uniform over
+// the wave). A stage is a list of 16-byte LDS chunks; chunk c of a round is
+// handled by thread c % 256. The XOR swizzle of a tile is applied by choosing
+// which global chunk lands in each physical LDS chunk. No registers hold the
+// data, so later stages load while the current one is used.
+//
+// The transfer is issued from inline assembly: the compiler's own tracking of
+// LDS DMA is coarse (it waits for every transfer in flight before any LDS
+// read that might alias one, and so does the release fence of
+// __syncthreads), which would serialise the rings. The kernels wait
+// themselves (s_waitcnt vmcnt, then a plain s_barrier) before reading a
+// stage. The address is a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// per-lane byte offset (no 64-bit arithmetic per lane). One wait state
+// separates the write of M0 from the transfer that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm" // M0 is reserved: nothing else in these kernels keeps it live
+__device__ __forceinline__ void dma16(const void *base, uint32_t off_bytes, const uint4 *lds_wave_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)lds_wave_base);
+    // (readfirstlane yields a signed int: both halves go through uint32_t so
+    // that the low word is zero-extended, never sign-extended)
+    const uint64_t b = (uint64_t)(size_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off_bytes), "s"(sb)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without a memory fence; this wave's LDS reads are complete.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Generic swizzle for NCH chunks per row: rows per 256-byte bank window are
+// 16/NCH; XOR the chunk with the window index so 16 consecutive rows map the
+// same logical chunk to 16 distinct bank groups.
+template <int NCH>
+__device__ __forceinline__ int swzg(int row, int ch)
+{
+    return ch ^ ((row / (16 / NCH)) & (NCH - 1));
+}
+
 // ============================================================== forward
+// One workgroup per 128 queries (32 per wave, Q hi / lo fragments in
+// registers); keys stream through LDS 32 at a time in a two-stage ring
+// filled asynchronously, two workgroups per CU.
+template <int D> struct FwdStage {
+    static constexpr int BN = 32;
+    static constexpr int KCH = D / 8;  // chunks per K row
+    static constexpr int VCH = BN / 8; // chunks per V^T row
+    static constexpr int KROWS = BN * KCH, VROWS = D * VCH;
+    static constexpr int KH = 0, KL = KROWS, VT = 2 * KROWS;
+    static constexpr int SIZE = 2 * KROWS + VROWS;
+    static constexpr int KU = KROWS / 256, VU = VROWS / 256; // load rounds per tile
+};
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
 {
-    constexpr int BM = 128, BN = 64;
-    constexpr int KCH = D / 8;  // chunks per K row
-    constexpr int VCH = BN / 8; // chunks per V^T row
+    typedef FwdStage<D> St;
+    constexpr int BM = 128, BN = St::BN, KCH = St::KCH, VCH = St::VCH;
     constexpr int NS = D / 16;  // k-steps over d
     constexpr int NT = D / 32;  // 32-dim tiles of the output
-    constexpr int KPT = BN * KCH / 256;
-    constexpr int VPT = D * VCH / 256;
-    __shared__ uint4 sKh[BN * KCH];
-    __shared__ uint4 sKl[BN * KCH];
-    __shared__ uint4 sV[D * VCH];
+    __shared__ uint4 sf0[St::SIZE], sf1[St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
     const int qb = nqb - 1 - (int)(blockIdx.x / a.H); // longest rows first
     const int64_t q0 = (int64_t)qb * BM;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int64_t qw = q0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
     const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D;
     const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
+
+    // byte offsets of this thread's chunks in a stage (the stage moves the base)
+    uint32_t koff[St::KU], voff[St::VU];
+#pragma unroll
+    for (int u = 0; u < St::KU; ++u) {
+        const int c = 256 * u + tid, r = c / KCH;
+        koff[u] = 2u * (uint32_t)(r * D + swz<KCH>(r, c % KCH) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < St::VU; ++u) {
+        const int c = 256 * u + tid, dim = c / VCH;
+        voff[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swz<VCH>(dim, c % VCH) * 8));
+    }
+    auto issue = [&](int64_t k0, const uint4 *base) {
+#pragma unroll
+        for (int u = 0; u < St::KU; ++u) {
+            dma16(khi + k0 * D, koff[u], base + St::KH + 256 * u + 64 * wave);
+            dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
+        }
+#pragma unroll
+        for (int u = 0; u < St::VU; ++u)
+            dma16(vt + k0, voff[u], base + St::VT + 256 * u + 64 * wave);
+    };
 
     uint4 qh[NS], ql[NS];
 #pragma unroll
@@ -132,95 +211,94 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
     const int nkb = (int)((kend + BN - 1) / BN);
     const int kap = kappa(c32);
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int64_t k0 = (int64_t)kb * BN;
-        __syncthreads();
+    auto stage = [&](auto bidx, int kb) __attribute__((always_inline)) {
+        constexpr int B = decltype(bidx)::value;
+        const uint4 *base = B == 0 ? sf0 : sf1;
+        const int64_t kt0 = (int64_t)kb * BN;
+        wait_async();
+        lds_barrier(); // stage kb is visible to all waves; the other slot is free
+        if (kb + 1 < nkb)
+            issue(kt0 + BN, B == 0 ? sf1 : sf0);
+        if (kt0 > qw + 31)
+            return; // this wave's queries all precede these keys
+        const uint4 *sKh = base + St::KH, *sKl = base + St::KL, *sV = base + St::VT;
+        f32x16_t st = zero16();
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int c = tid + 256 * u, key = c / KCH, ch = c % KCH;
-            const int at = key * KCH + swz<KCH>(key, ch);
-            sKh[at] = ld16(khi + (k0 + key) * D + ch * 8);
-            sKl[at] = ld16(klo + (k0 + key) * D + ch * 8);
+        for (int s = 0; s < NS; ++s) {
+            const int idx = kap * KCH + swz<KCH>(kap, 2 * s + g);
+            const uint4 kh = sKh[idx];
+            st = mfma32(kh, qh[s], st);
+            st = mfma32(sKl[idx], qh[s], st);
+            st = mfma32(kh, ql[s], st);
         }
+        // scaled logits y = st * log2(e)/sqrt(d); the row maximum is taken on
+        // st (a positive scale keeps the order, and rounding is monotonic)
+        if (kt0 + 31 > qw) { // diagonal subtile: mask keys after the query
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int c = tid + 256 * u, dim = c / VCH, ch = c % VCH;
-            sV[dim * VCH + swz<VCH>(dim, ch)] = ld16(vt + (int64_t)dim * a.S_pad + k0 + ch * 8);
+            for (int v = 0; v < 16; ++v)
+                if (kt0 + 16 * (v >> 3) + 8 * g + (v & 7) > qw + c32)
+                    st[v] = -INFINITY;
         }
-        __syncthreads();
+        float mx = st[0];
 #pragma unroll
-        for (int j = 0; j < BN / 32; ++j) {
-            const int64_t kt0 = k0 + 32 * j;
-            if (kt0 > qw + 31)
-                break; // this wave's queries all precede these keys
-            f32x16_t st = zero16();
-            const int kl = 32 * j + kap;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int idx = kl * KCH + swz<KCH>(kl, 2 * s + g);
-                const uint4 kh = sKh[idx];
-                st = mfma32(kh, qh[s], st);
-                st = mfma32(sKl[idx], qh[s], st);
-                st = mfma32(kh, ql[s], st);
-            }
-            const bool diag = kt0 + 31 > qw;
-            float y[16];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                y[v] = st[v] * a.scale_log2;
-                if (diag && kt0 + 16 * (v >> 3) + 8 * g + (v & 7) > qw + c32)
-                    y[v] = -INFINITY;
-                mx = fmaxf(mx, y[v]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
+        for (int v = 1; v < 16; ++v)
+            mx = fmaxf(mx, st[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx * a.scale_log2);
+        // rescale only when some row's maximum moved (a factor of 1 changes nothing)
+        if (__ballot(mn != m) != 0) {
             const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            m = mn;
             lsum *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     o[t][v] *= alpha;
-            float pr[16];
-            const float shift = mn - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
+        }
+        m = mn;
+        float pr[16];
+        const float shift = mn - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                pr[v] = __builtin_amdgcn_exp2f(y[v] - shift);
-            // The tile's 16 probabilities are summed first (pairwise) and then
-            // added to the running sum: added one by one, probabilities far
-            // below the running sum's half-ulp would all be rounded away, a
-            // systematic loss in the normaliser that the backward's
-            // dS = P (dP - delta) amplifies.
-            float t8[8];
+        for (int v = 0; v < 16; ++v)
+            pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -shift));
+        // The tile's 16 probabilities are summed first (pairwise) and then
+        // added to the running sum: added one by one, probabilities far
+        // below the running sum's half-ulp would all be rounded away, a
+        // systematic loss in the normaliser that the backward's
+        // dS = P (dP - delta) amplifies.
+        float t8[8];
 #pragma unroll
-            for (int v = 0; v < 8; ++v)
-                t8[v] = pr[v] + pr[v + 8];
+        for (int v = 0; v < 8; ++v)
+            t8[v] = pr[v] + pr[v + 8];
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                t8[v] += t8[v + 4];
-            lsum += (t8[0] + t8[2]) + (t8[1] + t8[3]);
-            uint4 ph[2], pl[2];
+        for (int v = 0; v < 4; ++v)
+            t8[v] += t8[v + 4];
+        lsum += (t8[0] + t8[2]) + (t8[1] + t8[3]);
+        uint4 ph[2], pl[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float x8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x8[e] = pr[8 * hh + e];
+            split8_f16(x8, ph[hh], pl[hh]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int dim = 32 * t + c32;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                float x8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    x8[e] = pr[8 * hh + e];
-                split8_f16(x8, ph[hh], pl[hh]);
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int dim = 32 * t + c32;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint4 vv = sV[dim * VCH + swz<VCH>(dim, 4 * j + 2 * hh + g)];
-                    o[t] = mfma32(vv, ph[hh], o[t]);
-                    o[t] = mfma32(vv, pl[hh], o[t]);
-                }
+                const uint4 vv = sV[dim * VCH + swz<VCH>(dim, 2 * hh + g)];
+                o[t] = mfma32(vv, ph[hh], o[t]);
+                o[t] = mfma32(vv, pl[hh], o[t]);
             }
         }
+    };
+    issue(0, sf0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        stage(std::integral_constant<int, 0>(), kb);
+        if (kb + 1 < nkb)
+            stage(std::integral_constant<int, 1>(), kb + 1);
     }
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -245,51 +323,6 @@ hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
     else
         hipLaunchKernelGGL((k_attn_fwd<64>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
-}
-
-// ============================================================== async staging
-// global_load_lds_dwordx4: each lane fetches 16 bytes from its own global
-// address and the wave writes them to LDS at base + 16 * lane (base uniform
-// over the wave). A stage is a list of 16-byte LDS chunks; chunk c of a round
-// is handled by thread c % 256. The XOR swizzle of a tile is applied by
-// choosing which global chunk lands in each physical LDS chunk. No registers
-// hold the data, so the next stage's loads overlap the current stage's math.
-__device__ __forceinline__ void async16(const void *g, const uint4 *lds_wave_base)
-{
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
-                                     (void __attribute__((address_space(3))) *)lds_wave_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// The same transfer issued from inline assembly, for the multi-stage rings of
-// the backward kernels: the compiler then does not track these LDS writes, so
-// it inserts no wait for them before reading other stages of the ring (its
-// own tracking of LDS DMA is coarse and would wait for every transfer in
-// flight). The kernels wait themselves (s_waitcnt vmcnt(n), then an LDS
-// barrier) before reading a stage. M0 takes the wave's LDS base; one wait
-// state separates its write from the transfer that reads it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm" // M0 is reserved: nothing else in these kernels keeps it live
-__device__ __forceinline__ void async16_nc(const void *g, const uint4 *lds_wave_base)
-{
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Workgroup barrier without a memory fence (the fence of __syncthreads would
-// wait for every transfer in flight); LDS reads of this wave are complete.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Generic swizzle for NCH chunks per row: rows per 256-byte bank window are
-// 16/NCH; XOR the chunk with the window index so 16 consecutive rows map the
-// same logical chunk to 16 distinct bank groups.
-template <int NCH>
-__device__ __forceinline__ int swzg(int row, int ch)
-{
-    return ch ^ ((row / (16 / NCH)) & (NCH - 1));
 }
 
 // ============================================================== backward: dK, dV
@@ -340,48 +373,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int h = blockIdx.x % a.H;
     const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
     const int k0 = kb * BK;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int kw = k0 + wave * 32;
     const int key = kw + c32;
     const int S = (int)a.S, S_pad = (int)a.S_pad;
     const int64_t hS = (int64_t)h * S_pad;
 
-    // Per-lane element offsets of this thread's chunks inside a stage's tiles
+    // Per-lane byte offsets of this thread's chunks inside a stage's tiles
     // (the same for every stage; the stage only moves the uniform base).
     uint32_t roff[RU], toff[TU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int c = 256 * u + tid, r = c / RCH;
-        roff[u] = (uint32_t)(r * D + swzg<RCH>(r, c % RCH) * 8);
+        roff[u] = 2u * (uint32_t)(r * D + swzg<RCH>(r, c % RCH) * 8);
     }
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
         const int c = 256 * u + tid, dim = c / TCH;
-        toff[u] = (uint32_t)dim * (uint32_t)S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8);
+        toff[u] = 2u * ((uint32_t)dim * (uint32_t)S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8));
     }
     const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
     const uint16_t *const cols[2] = {a.qhi_t, a.dohi_t};
     // lanes 0..3 of every wave fetch 4 of the 16 lse / delta chunks, so each
     // wave issues the same number of loads per stage (St::LOADS)
     const float *stat = wave < 2 ? a.lse : a.delta;
-    const int stat_off = 4 * ((4 * wave + (lane & 3)) & 7);
+    const uint32_t stat_off = 16u * (uint32_t)((4 * wave + (lane & 3)) & 7);
 
     auto issue = [&](int q0, const uint4 *base) {
         if (lane < 4) // lanes 0..3 write chunks LS + 4 * wave + lane
-            async16_nc(stat + hS + q0 + stat_off, base + St::LS + 4 * wave);
+            dma16(stat + hS + q0, stat_off, base + St::LS + 4 * wave);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint16_t *rb = rows[t] + (hS + q0) * D;
 #pragma unroll
             for (int u = 0; u < RU; ++u)
-                async16_nc(rb + roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
+                dma16(rb, roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
 #pragma unroll
             for (int u = 0; u < TU; ++u)
-                async16_nc(cb + toff[u], base + 64 * wave + St::QT + t * St::COLS + 256 * u);
+                dma16(cb, toff[u], base + 64 * wave + St::QT + t * St::COLS + 256 * u);
         }
     };
 
@@ -480,15 +514,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dlt[8 * hh + 0] = d0.x; dlt[8 * hh + 1] = d0.y; dlt[8 * hh + 2] = d0.z; dlt[8 * hh + 3] = d0.w;
             dlt[8 * hh + 4] = d1.x; dlt[8 * hh + 5] = d1.y; dlt[8 * hh + 6] = d1.z; dlt[8 * hh + 7] = d1.w;
         }
+        // pr = P * 2^15 (keeps small P out of the fp16 underflow range; the
+        // statistics arrive as LSE - 15 and delta * 2^-15), dS = P (dP - delta).
+        // Only stages that cross the diagonal or the end of S need the mask.
         float pr[16], ds[16];
-        const int rel = q0 - key; // query - key of register 0's query
+        if (q0 >= kw + 31 && q0 + BQ <= S) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
-            const bool ok = rel + qi >= 0 && q0 + qi < S;
-            const float pv = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lq[v] : -INFINITY);
-            ds[v] = ok ? pv * (dp[v] - dlt[v]) : 0.0f;
-            pr[v] = pv * 32768.0f; // 2^15: keeps small P out of the fp16 underflow range
+            for (int v = 0; v < 16; ++v) {
+                pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lq[v]));
+                ds[v] = pr[v] * __builtin_fmaf(dp[v], kPScaleInv, -dlt[v]);
+            }
+        } else {
+            const int rel = q0 - key; // query - key of register 0's query
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
+                const bool ok = rel + qi >= 0 && q0 + qi < S;
+                pr[v] = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(st[v], a.scale_log2, -lq[v]) : -INFINITY);
+                ds[v] = ok ? pr[v] * __builtin_fmaf(dp[v], kPScaleInv, -dlt[v]) : 0.0f;
+            }
         }
         const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
@@ -586,28 +630,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int h = blockIdx.x % a.H;
     const int qb = nqb - 1 - (int)(blockIdx.x / a.H);
     const int64_t q0 = (int64_t)qb * BM;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int64_t qw = q0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
     const int64_t query = qw + c32;
 
-    const uint16_t *const khi = a.khi, *const klo = a.klo, *const vv = a.v, *const kht = a.khi_t;
+    // byte offsets of this thread's chunks inside a stage (the stage moves the
+    // uniform bases): each 256-chunk round lies in one tile (ROWS is a
+    // multiple of 256)
+    constexpr int NU = St::SIZE / 256;
+    uint32_t off[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int c = 256 * u + tid;
+        if (256 * u < St::KT) {
+            const int cc = c - (256 * u / St::ROWS) * St::ROWS, r = cc / RCH;
+            off[u] = 2u * (uint32_t)(r * D + swzg<RCH>(r, cc % RCH) * 8);
+        } else {
+            const int cc = c - St::KT, dim = cc / TCH;
+            off[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swzg<TCH>(dim, cc % TCH) * 8));
+        }
+    }
+    const uint16_t *const khi = a.khi + hS * D, *const klo = a.klo + hS * D, *const vv = a.v + hS * D;
+    const uint16_t *const kht = a.khi_t + (int64_t)h * D * a.S_pad;
     auto issue = [&](int64_t k0, const uint4 *base) {
 #pragma unroll
-        for (int u = 0; u < St::SIZE / 256; ++u) {
-            const int c = 256 * u + tid;
+        for (int u = 0; u < NU; ++u) {
             const uint4 *wb = base + 256 * u + 64 * wave;
-            const void *src;
-            if (256 * u < St::KT) { // round u lies in one row-major tile (ROWS is a multiple of 256)
+            if (256 * u < St::KT) {
                 const int t = 256 * u / St::ROWS;
-                const int cc = c - t * St::ROWS, r = cc / RCH, ch = swzg<RCH>(r, cc % RCH);
                 const uint16_t *arr = t == 0 ? khi : (t == 1 ? klo : vv);
-                src = arr + (hS + k0 + r) * D + ch * 8;
+                dma16(arr + k0 * D, off[u], wb);
             } else {
-                const int cc = c - St::KT, dim = cc / TCH, ch = swzg<TCH>(dim, cc % TCH);
-                src = kht + ((int64_t)h * D + dim) * a.S_pad + k0 + ch * 8;
+                dma16(kht + k0, off[u], wb);
             }
-            async16_nc(src, wb);
         }
     };
 
@@ -621,8 +678,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dl[s] = ld16(a.dolo + off);
     }
     const bool qok = query < a.S;
-    const float lse2 = qok ? a.lse[hS + query] : 0.0f;
-    const float del = qok ? a.delta[hS + query] : 0.0f;
+    const float lse15 = qok ? a.lse[hS + query] : 0.0f; // log2 LSE - 15
+    const float del15 = qok ? a.delta[hS + query] : 0.0f; // delta * 2^-15
     f32x16_t dqT[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -657,14 +714,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dpt = mfma32(vv, dh[s], dpt);
                 dpt = mfma32(vv, dl[s], dpt);
             }
+            // dS = P (dP - delta) from P * 2^15 and (dP - delta) * 2^-15; only
+            // subtiles that cross the diagonal or the end of S need the mask
             float ds[16];
-            const int rel = (int)(query - kt0); // query - key of register 0's key
+            if (kt0 + 31 <= qw && qw + 31 < a.S) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int ki = 16 * (v >> 3) + 8 * g + (v & 7);
-                const bool ok = qok && ki <= rel;
-                const float pr = __builtin_amdgcn_exp2f(ok ? st[v] * a.scale_log2 - lse2 : -INFINITY);
-                ds[v] = ok ? pr * (dpt[v] - del) : 0.0f;
+                for (int v = 0; v < 16; ++v)
+                    ds[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lse15)) *
+                            __builtin_fmaf(dpt[v], kPScaleInv, -del15);
+            } else {
+                const int rel = (int)(query - kt0); // query - key of register 0's key
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int ki = 16 * (v >> 3) + 8 * g + (v & 7);
+                    const bool ok = qok && ki <= rel;
+                    const float pr = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(st[v], a.scale_log2, -lse15) : -INFINITY);
+                    ds[v] = ok ? pr * __builtin_fmaf(dpt[v], kPScaleInv, -del15) : 0.0f;
+                }
             }
             const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
 #pragma unroll

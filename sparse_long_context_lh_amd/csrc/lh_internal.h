@@ -24,7 +24,8 @@ enum InternalRegion {
     IR_DOHI,                // fp16 [H][S_pad][d]: hi part of dO_sub
     IR_DOLO,                // fp16 [H][S_pad][d]: lo part of dO_sub
     IR_DOHI_T,              // fp16 [H][d][S_pad]: transpose of the hi part
-    IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub)
+    IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub) * 2^-15
+    IR_LSE15,               // fp32 [H][S_pad]: log2-domain LSE - 15
     IR_FPART,               // fp32 window sums [3][H][fpart_rows][d], then maxima [H][fpart_rows]
     IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
     IR_COUNT
@@ -138,7 +139,7 @@ struct AttnBwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
     const uint16_t *qhi_t, *khi_t;              // fp16 [H][d][S_pad]
     const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
-    const float *lse, *delta;                        // [H][S_pad]
+    const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
     float *dq, *dk, *dv;                             // [H][S_pad][d]
     int64_t S, S_pad;
     int H;
@@ -170,7 +171,9 @@ struct ScatterBwdArgs {
 struct BwdPrepArgs {
     const float *dosub, *osub;       // [H][S_pad][d]
     uint16_t *dohi, *dolo, *dohi_t;  // fp16 pair, and the hi transpose
-    float *delta;              // [H][S_pad]
+    float *delta;              // [H][S_pad]: rowsum * 2^-15
+    const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
+    float *lse15;              // [H][S_pad]: lse - 15
     int64_t S, S_pad;
     int H;
 };

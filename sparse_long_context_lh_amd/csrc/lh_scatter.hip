@@ -411,6 +411,9 @@ hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream
 // transposed (MFMA operands of the attention backward), and
 // delta_s = sum_d (hi + lo)[s][d] * O_sub[s][d], the row term of the softmax
 // gradient, from the same values the dP products see. Rows past S are zero.
+// The attention backward works with probabilities scaled by 2^15 (kept out of
+// the fp16 underflow range): it reads delta_s * 2^-15 (an exact scaling) and
+// the log2-domain LSE minus 15, so that one fma gives the scaled exponent.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
 {
@@ -443,8 +446,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
 #pragma unroll
         for (int off2 = LANES / 2; off2 >= 1; off2 >>= 1)
             dot += __shfl_xor(dot, off2, LANES);
-        if (lane == 0)
-            a.delta[(int64_t)h * a.S_pad + s] = dot;
+        if (lane == 0) {
+            a.delta[(int64_t)h * a.S_pad + s] = dot * (1.0f / 32768.0f);
+            a.lse15[(int64_t)h * a.S_pad + s] = s < a.S ? a.lse[(int64_t)h * a.S_pad + s] - 15.0f : 0.0f;
+        }
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
         *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
         *reinterpret_cast<uint4 *>(&tile[r * LD + lane * 8]) = hi;
