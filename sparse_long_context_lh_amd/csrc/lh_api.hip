@@ -129,6 +129,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
     b[IR_LSE15] = 4 * Hs * Sp;
+    b[IR_DST] = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
     size_t off = 0;
@@ -350,6 +351,8 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.dq = at<float>(ws, pl, LH_R_DQSUB);
     ab.dk = at<float>(ws, pl, LH_R_DKSUB);
     ab.dv = at<float>(ws, pl, LH_R_DVSUB);
+    ab.dst = at<uint16_t>(ws, pl, IR_DST);
+    ab.dst_head = dst_tiles(pl.S_pad) * 1024;
     ab.S = pl.S; ab.S_pad = pl.S_pad; ab.H = H;
     ab.scale = (float)(1.0 / sqrt((double)d));
     ab.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));

@@ -376,7 +376,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int kw = k0 + wave * 32;
-    const int key = kw + c32;
+    // lane c32 owns key kw + kappa(c32): then the transposed dS tile (below)
+    // leaves the MFMA as runs of 8 consecutive keys per lane
+    const int key = kw + kappa(c32);
     const int S = (int)a.S, S_pad = (int)a.S_pad;
     const int64_t hS = (int64_t)h * S_pad;
 
@@ -434,6 +436,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dkT[t] = zero16();
     }
     const int ql = kappa(c32);
+    // fp16 identity columns: lane (c32, g) holds 1.0 at k-value e when query
+    // 8g + e (first half of the stage) or 16 + 8g + e (second half) is c32
+    uint4 eye0, eye1;
+    {
+        uint32_t w0[4], w1[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int qa = 8 * g + 2 * e2;
+            w0[e2] = (c32 == qa ? 0x3c00u : 0u) | (c32 == qa + 1 ? 0x3c000000u : 0u);
+            w1[e2] = (c32 == qa + 16 ? 0x3c00u : 0u) | (c32 == qa + 17 ? 0x3c000000u : 0u);
+        }
+        eye0 = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        eye1 = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+    }
+    uint16_t *const dst_head = a.dst + (int64_t)h * a.dst_head;
+    const int kt = kw / 32; // this wave's key tile
     const int nst = (S - k0 + BQ - 1) / BQ;
 
     auto stage = [&](auto bidx, int it) __attribute__((always_inline)) {
@@ -442,6 +460,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint4 *ahead = B == 0 ? sb2 : (B == 1 ? sb0 : sb1); // ring slot of stage it + 2
         const int q0 = k0 + it * BQ;
         // stage it has landed once at most one stage's loads are outstanding
+        // (this also waits for the previous stage's dS stores, issued after them:
+        // vector memory operations complete in issue order)
         if (it + 1 < nst)
             wait_async_n<St::LOADS>();
         else
@@ -536,6 +556,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+        // dS of the tile (queries q0.., keys kw..) for the dQ kernel, query-major:
+        // C = dS^T(as rows keys) x identity puts query c32 in lane c32 with keys
+        // 16(v/8) + 8g + v%8 in register v (exact: fp16 times 1, fp32 sums of one term)
+        if (q0 >= kw) {
+            f32x16_t tr = mfma32(db0, eye0, zero16());
+            tr = mfma32(db1, eye1, tr);
+            const int qt = q0 / 32;
+            uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
+            float t8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                t8[e] = tr[e];
+            *reinterpret_cast<uint4 *>(row) = pack8h(t8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                t8[e] = tr[8 + e];
+            *reinterpret_cast<uint4 *>(row + 16) = pack8h(t8);
+        }
         auto gstep = [&](int t, const uint4 (&f)[4], uint4 (&nx)[4], bool pre) {
             if (pre) nx[0] = gfrag(t + 1, 0);
             LH_FENCE;
@@ -604,87 +642,77 @@ hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_
 }
 
 // ============================================================== backward: dQ
-// One workgroup per 128 queries (32 per wave, Q and dO_sub in registers); keys
-// stream through LDS 64 at a time up to the diagonal, double-buffered.
-// S^T = K Q^T as in the forward, so a lane owns one query:
-//   dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
+// dQ = scale * dS K from the dS tiles the dK/dV kernel stored (query-major,
+// fp16: the values it used itself), so S and dP are not recomputed. One
+// workgroup per 128 queries (32 per wave), two workgroups per CU; K^T of 64
+// keys per stage (shared) and each wave's own dS tiles of the stage go
+// through a two-stage LDS ring. Per 32x32 tile: dQ^T += K^T dS^T, 8 MFMAs.
 template <int D>
 struct DqStage {
     static constexpr int BN = 64;
-    static constexpr int RCH = D / 8, TCH = BN / 8;
-    static constexpr int ROWS = BN * RCH, COLS = D * TCH;
-    static constexpr int KH = 0, KL = ROWS, VV = 2 * ROWS, KT = 3 * ROWS;
-    static constexpr int SIZE = 3 * ROWS + COLS;
+    static constexpr int TCH = BN / 8;          // chunks per K^T row
+    static constexpr int KT = 0, KSIZE = D * TCH; // K^T [D][BN]
+    static constexpr int DS = KSIZE;            // dS: [wave][subtile][32 queries][4 chunks]
+    static constexpr int DSW = 2 * 32 * 4;      // chunks per wave
+    static constexpr int SIZE = KSIZE + 4 * DSW;
+    static constexpr int KU = KSIZE / 256;      // K^T load rounds
 };
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dq(AttnBwdArgs a)
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     typedef DqStage<D> St;
-    constexpr int BM = 128, BN = St::BN, RCH = St::RCH, TCH = St::TCH;
-    constexpr int NS = D / 16, NT = D / 32;
-    // two stages, separate arrays named at compile time (see the dK/dV kernel)
+    constexpr int BM = 128, BN = St::BN, TCH = St::TCH;
+    constexpr int NT = D / 32;
     __shared__ uint4 sq0[St::SIZE], sq1[St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
-    const int qb = nqb - 1 - (int)(blockIdx.x / a.H);
+    const int qb = nqb - 1 - (int)(blockIdx.x / a.H); // longest rows first
     const int64_t q0 = (int64_t)qb * BM;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int64_t qw = q0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
-    const int64_t query = qw + c32;
+    const int qt = (int)(qw / 32); // this wave's query tile: key tiles 0..qt
+    const bool live = qw < a.S;
 
-    // byte offsets of this thread's chunks inside a stage (the stage moves the
-    // uniform bases): each 256-chunk round lies in one tile (ROWS is a
-    // multiple of 256)
-    constexpr int NU = St::SIZE / 256;
-    uint32_t off[NU];
+    // K^T chunk byte offsets (the stage moves the uniform base)
+    uint32_t koff[St::KU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int c = 256 * u + tid;
-        if (256 * u < St::KT) {
-            const int cc = c - (256 * u / St::ROWS) * St::ROWS, r = cc / RCH;
-            off[u] = 2u * (uint32_t)(r * D + swzg<RCH>(r, cc % RCH) * 8);
-        } else {
-            const int cc = c - St::KT, dim = cc / TCH;
-            off[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swzg<TCH>(dim, cc % TCH) * 8));
-        }
+    for (int u = 0; u < St::KU; ++u) {
+        const int c = 256 * u + tid, dim = c / TCH;
+        koff[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8));
     }
-    const uint16_t *const khi = a.khi + hS * D, *const klo = a.klo + hS * D, *const vv = a.v + hS * D;
     const uint16_t *const kht = a.khi_t + (int64_t)h * D * a.S_pad;
+    // this wave's dS tiles (qt, kt) are contiguous in kt; lane chunk = 16 B
+    const uint16_t *const dsrow = a.dst + (int64_t)h * a.dst_head + (int64_t)qt * (qt + 1) / 2 * 1024;
+    // a 32x32 tile is 128 chunks (32 query rows of 4): two DMA rounds, the
+    // physical chunk of (row, c) XOR-swizzled so lane reads avoid bank conflicts
+    const uint32_t doff0 = 16u * (uint32_t)((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3)));
+    const uint32_t doff1 = doff0 + 16u * 64u;
+
     auto issue = [&](int64_t k0, const uint4 *base) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const uint4 *wb = base + 256 * u + 64 * wave;
-            if (256 * u < St::KT) {
-                const int t = 256 * u / St::ROWS;
-                const uint16_t *arr = t == 0 ? khi : (t == 1 ? klo : vv);
-                dma16(arr + k0 * D, off[u], wb);
-            } else {
-                dma16(kht + k0, off[u], wb);
+        for (int u = 0; u < St::KU; ++u)
+            dma16(kht + k0, koff[u], base + St::KT + 256 * u + 64 * wave);
+        // own dS tiles of the stage: key tiles k0/32 and k0/32 + 1, if at or before qt
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ktile = (int)(k0 / 32) + j;
+            if (live && ktile <= qt) {
+                const uint16_t *tb = dsrow + (int64_t)ktile * 1024;
+                const uint4 *lb = base + St::DS + wave * St::DSW + j * 128;
+                dma16(tb, doff0, lb);
+                dma16(tb, doff1, lb + 64);
             }
         }
     };
 
-    uint4 qh[NS], ql[NS], dh[NS], dl[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int64_t off = (hS + query) * D + 16 * s + 8 * g;
-        qh[s] = ld16(a.qhi + off);
-        ql[s] = ld16(a.qlo + off);
-        dh[s] = ld16(a.dohi + off);
-        dl[s] = ld16(a.dolo + off);
-    }
-    const bool qok = query < a.S;
-    const float lse15 = qok ? a.lse[hS + query] : 0.0f; // log2 LSE - 15
-    const float del15 = qok ? a.delta[hS + query] : 0.0f; // delta * 2^-15
     f32x16_t dqT[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         dqT[t] = zero16();
-    const int kap = kappa(c32);
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
 
@@ -696,48 +724,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         lds_barrier(); // stage kb is visible to all waves; the other slot is free
         if (kb + 1 < nkb)
             issue(k0 + BN, B == 0 ? sq1 : sq0);
-        // (in the diagonal block a wave may find a subtile entirely after its
-        // queries; the mask below zeroes it rather than branching around it)
 #pragma unroll
-        for (int j = 0; j < BN / 32; ++j) {
-            const int64_t kt0 = k0 + 32 * j;
-            const int kl = 32 * j + kap;
-            f32x16_t st = zero16(), dpt = zero16();
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int at = kl * RCH + swzg<RCH>(kl, 2 * s + g);
-                const uint4 k_h = base[St::KH + at];
-                st = mfma32(k_h, qh[s], st);
-                st = mfma32(base[St::KL + at], qh[s], st);
-                st = mfma32(k_h, ql[s], st);
-                const uint4 vv = base[St::VV + at];
-                dpt = mfma32(vv, dh[s], dpt);
-                dpt = mfma32(vv, dl[s], dpt);
-            }
-            // dS = P (dP - delta) from P * 2^15 and (dP - delta) * 2^-15; only
-            // subtiles that cross the diagonal or the end of S need the mask
-            float ds[16];
-            if (kt0 + 31 <= qw && qw + 31 < a.S) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    ds[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lse15)) *
-                            __builtin_fmaf(dpt[v], kPScaleInv, -del15);
-            } else {
-                const int rel = (int)(query - kt0); // query - key of register 0's key
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int ki = 16 * (v >> 3) + 8 * g + (v & 7);
-                    const bool ok = qok && ki <= rel;
-                    const float pr = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(st[v], a.scale_log2, -lse15) : -INFINITY);
-                    ds[v] = ok ? pr * __builtin_fmaf(dpt[v], kPScaleInv, -del15) : 0.0f;
-                }
-            }
-            const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+        for (int j = 0; j < 2; ++j) {
+            const int ktile = (int)(k0 / 32) + j;
+            if (!live || ktile > qt)
+                break;
+            // dS^T operand: query c32, keys 8g.. and 16 + 8g.. of the tile
+            const uint4 *dt = base + St::DS + wave * St::DSW + j * 128 + c32 * 4;
+            const int sw = (c32 >> 1) & 3;
+            const uint4 ds0 = dt[g ^ sw], ds1 = dt[(2 + g) ^ sw];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int dim = 32 * t + c32;
-                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + g)], db0, dqT[t]);
-                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + 2 + g)], db1, dqT[t]);
+                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + g)], ds0, dqT[t]);
+                dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + 2 + g)], ds1, dqT[t]);
             }
         }
     };
@@ -748,6 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             stage(std::integral_constant<int, 1>(), kb + 1);
     }
 
+    const int64_t query = qw + c32;
     float *dq = a.dq + (hS + query) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)

@@ -26,6 +26,7 @@ enum InternalRegion {
     IR_DOHI_T,              // fp16 [H][d][S_pad]: transpose of the hi part
     IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub) * 2^-15
     IR_LSE15,               // fp32 [H][S_pad]: log2-domain LSE - 15
+    IR_DST,                 // fp16 [H][T(T+1)/2][32][32], T = S_pad/32: dS tiles (query-major), causal half
     IR_FPART,               // fp32 window sums [3][H][fpart_rows][d], then maxima [H][fpart_rows]
     IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
     IR_COUNT
@@ -73,6 +74,13 @@ struct Plan {
     size_t off[IR_COUNT], bytes[IR_COUNT];
     size_t total;
 };
+
+// 32x32 tiles of the causal half of the S_pad x S_pad score matrix (kt <= qt).
+inline int64_t dst_tiles(int64_t S_pad)
+{
+    const int64_t t = S_pad / 32;
+    return t * (t + 1) / 2;
+}
 
 // Fills `pl` and returns LH_OK, or the validation error.
 lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, Plan *pl);
@@ -141,6 +149,8 @@ struct AttnBwdArgs {
     const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
     const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
     float *dq, *dk, *dv;                             // [H][S_pad][d]
+    uint16_t *dst;     // IR_DST: tile (qt, kt), kt <= qt, at (qt(qt+1)/2 + kt) * 1024 in a head's block
+    int64_t dst_head;  // elements per head of IR_DST
     int64_t S, S_pad;
     int H;
     float scale_log2; // log2(e) / sqrt(d)
