@@ -40,8 +40,6 @@
 // resulting O_sub error is amplified by delta); the scale cancels against the
 // normaliser (forward) or is divided out of dV (backward). The log-sum-exp is
 // kept in the log2 domain of the scaled logits, as the backward uses it.
-#include <type_traits>
-
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -103,15 +101,16 @@ __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_c
 // read that might alias one, and so does the release fence of
 // __syncthreads), which would serialise the rings. The kernels wait
 // themselves (s_waitcnt vmcnt, then a plain s_barrier) before reading a
-// stage. The address is a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// stage, so a ring can be one LDS array indexed at run time. The address is a wave-uniform 64-bit base in SGPRs plus a 32-bit
 // per-lane byte offset (no 64-bit arithmetic per lane). One wait state
 // separates the write of M0 from the transfer that reads it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm" // M0 is reserved: nothing else in these kernels keeps it live
 __device__ __forceinline__ void dma16(const void *base, uint32_t off_bytes, const uint4 *lds_wave_base)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)lds_wave_base);
+    // the low 32 bits of a generic LDS address are the LDS offset (the shared
+    // aperture is 4 GiB aligned); this avoids the null check of an address-space cast
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds_wave_base);
     // (readfirstlane yields a signed int: both halves go through uint32_t so
     // that the low word is zero-extended, never sign-extended)
     const uint64_t b = (uint64_t)(size_t)base;
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
     constexpr int BM = 128, BN = St::BN, KCH = St::KCH, VCH = St::VCH;
     constexpr int NS = D / 16;  // k-steps over d
     constexpr int NT = D / 32;  // 32-dim tiles of the output
-    __shared__ uint4 sf0[St::SIZE], sf1[St::SIZE];
+    __shared__ uint4 ring[2 * St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -211,14 +210,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
     const int nkb = (int)((kend + BN - 1) / BN);
     const int kap = kappa(c32);
 
-    auto stage = [&](auto bidx, int kb) __attribute__((always_inline)) {
-        constexpr int B = decltype(bidx)::value;
-        const uint4 *base = B == 0 ? sf0 : sf1;
+    auto stage = [&](int kb) __attribute__((always_inline)) {
+        const uint4 *base = ring + (kb & 1) * St::SIZE;
         const int64_t kt0 = (int64_t)kb * BN;
         wait_async();
         lds_barrier(); // stage kb is visible to all waves; the other slot is free
         if (kb + 1 < nkb)
-            issue(kt0 + BN, B == 0 ? sf1 : sf0);
+            issue(kt0 + BN, ring + ((kb + 1) & 1) * St::SIZE);
         if (kt0 > qw + 31)
             return; // this wave's queries all precede these keys
         const uint4 *sKh = base + St::KH, *sKl = base + St::KL, *sV = base + St::VT;
@@ -294,12 +292,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
             }
         }
     };
-    issue(0, sf0);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        stage(std::integral_constant<int, 0>(), kb);
-        if (kb + 1 < nkb)
-            stage(std::integral_constant<int, 1>(), kb + 1);
-    }
+    issue(0, ring);
+    for (int kb = 0; kb < nkb; ++kb)
+        stage(kb);
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float inv = 1.0f / ltot;
@@ -364,11 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
     constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
-    // The ring is three separate arrays and every access names its array at
-    // compile time: the compiler then knows that reads of the current stage do
-    // not alias the asynchronous writes of a later one, and does not wait for
-    // those writes before the reads.
-    __shared__ uint4 sb0[St::SIZE], sb1[St::SIZE], sb2[St::SIZE];
+    __shared__ uint4 ring[St::NBUF * St::SIZE];
 
     const int h = blockIdx.x % a.H;
     const int kb = (int)(blockIdx.x / a.H); // early keys see the most queries: run them first
@@ -402,16 +393,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float *stat = wave < 2 ? a.lse : a.delta;
     const uint32_t stat_off = 16u * (uint32_t)((4 * wave + (lane & 3)) & 7);
 
-    auto issue = [&](int q0, const uint4 *base) {
+    // A stage's transfers in five parts (the four row-major tiles, then the
+    // two transposed tiles and the statistics), issued at spread-out points
+    // of the previous stage's math: issued in one burst, their LDS writes
+    // stall the operand reads of the products.
+    auto issue_rows = [&](int q0, const uint4 *base, int t) {
+        const uint16_t *rb = rows[t] + (hS + q0) * D;
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            dma16(rb, roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
+    };
+    auto issue_cols = [&](int q0, const uint4 *base) {
         if (lane < 4) // lanes 0..3 write chunks LS + 4 * wave + lane
             dma16(stat + hS + q0, stat_off, base + St::LS + 4 * wave);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint16_t *rb = rows[t] + (hS + q0) * D;
-#pragma unroll
-            for (int u = 0; u < RU; ++u)
-                dma16(rb, roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
-        }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
@@ -419,6 +413,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int u = 0; u < TU; ++u)
                 dma16(cb, toff[u], base + 64 * wave + St::QT + t * St::COLS + 256 * u);
         }
+    };
+    auto issue = [&](int q0, const uint4 *base) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            issue_rows(q0, base, t);
+        issue_cols(q0, base);
     };
 
     uint4 kh[NS], klf[NS], vf[NS];
@@ -454,10 +454,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int kt = kw / 32; // this wave's key tile
     const int nst = (S - k0 + BQ - 1) / BQ;
 
-    auto stage = [&](auto bidx, int it) __attribute__((always_inline)) {
-        constexpr int B = decltype(bidx)::value;
-        const uint4 *base = B == 0 ? sb0 : (B == 1 ? sb1 : sb2);
-        const uint4 *ahead = B == 0 ? sb2 : (B == 1 ? sb0 : sb1); // ring slot of stage it + 2
+    int slot = 0; // ring slot of stage it
+    auto stage = [&](int it) __attribute__((always_inline)) {
+        const uint4 *base = ring + slot * St::SIZE;
+        const uint4 *ahead = ring + (slot == 0 ? 2 : slot - 1) * St::SIZE; // slot of stage it + 2
         const int q0 = k0 + it * BQ;
         // stage it has landed once at most one stage's loads are outstanding
         // (this also waits for the previous stage's dS stores, issued after them:
@@ -467,8 +467,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else
             wait_async();
         lds_barrier(); // stage it is visible to all waves; stage it-1's slot is free
-        if (it + 2 < nst)
-            issue(q0 + 2 * BQ, ahead);
+        const bool pre2 = it + 2 < nst; // stage it + 2 is loaded during this one
         // (near the diagonal a wave may find every query of the stage before its
         // keys; the mask below zeroes that stage rather than branching around it)
         const float *sL = reinterpret_cast<const float *>(base + St::LS);
@@ -507,6 +506,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             fa[i] = rd(0, i);
 #pragma unroll
         for (int s = 0; s < NS; s += 2) {
+            if (pre2) { // row tiles of stage it + 2, spread over the k-step pairs
+                constexpr int PER = 8 / NS; // tiles per pair: 4 tiles over NS/2 pairs
+#pragma unroll
+                for (int t = 0; t < PER; ++t)
+                    issue_rows(q0 + 2 * BQ, ahead, (s / 2) * PER + t);
+            }
             step(s, fa, fb, true);
             step(s + 1, fb, fa, s + 2 < NS);
         }
@@ -594,19 +599,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         };
 #pragma unroll
         for (int t = 0; t < NT; t += 2) {
+            if (pre2 && t == 0)
+                issue_cols(q0 + 2 * BQ, ahead);
             gstep(t, ga, gb, true);
             gstep(t + 1, gb, ga, t + 2 < NT);
         }
     };
-    issue(k0, sb0);
+    issue(k0, ring);
     if (nst > 1)
-        issue(k0 + BQ, sb1);
-    for (int it = 0; it < nst; it += 3) {
-        stage(std::integral_constant<int, 0>(), it);
-        if (it + 1 < nst)
-            stage(std::integral_constant<int, 1>(), it + 1);
-        if (it + 2 < nst)
-            stage(std::integral_constant<int, 2>(), it + 2);
+        issue(k0 + BQ, ring + St::SIZE);
+    for (int it = 0; it < nst; ++it) {
+        stage(it);
+        slot = slot == 2 ? 0 : slot + 1;
     }
 
     float *dk = a.dk + (hS + key) * D;
@@ -664,7 +668,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     typedef DqStage<D> St;
     constexpr int BM = 128, BN = St::BN, TCH = St::TCH;
     constexpr int NT = D / 32;
-    __shared__ uint4 sq0[St::SIZE], sq1[St::SIZE];
+    __shared__ uint4 ring[2 * St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -716,14 +720,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
 
-    auto stage = [&](auto bidx, int kb) __attribute__((always_inline)) {
-        constexpr int B = decltype(bidx)::value;
-        const uint4 *base = B == 0 ? sq0 : sq1;
+    auto stage = [&](int kb) __attribute__((always_inline)) {
+        const uint4 *base = ring + (kb & 1) * St::SIZE;
         const int64_t k0 = (int64_t)kb * BN;
         wait_async();
         lds_barrier(); // stage kb is visible to all waves; the other slot is free
         if (kb + 1 < nkb)
-            issue(k0 + BN, B == 0 ? sq1 : sq0);
+            issue(k0 + BN, ring + ((kb + 1) & 1) * St::SIZE);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int ktile = (int)(k0 / 32) + j;
@@ -741,12 +744,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
             }
         }
     };
-    issue(0, sq0);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        stage(std::integral_constant<int, 0>(), kb);
-        if (kb + 1 < nkb)
-            stage(std::integral_constant<int, 1>(), kb + 1);
-    }
+    issue(0, ring);
+    for (int kb = 0; kb < nkb; ++kb)
+        stage(kb);
 
     const int64_t query = qw + c32;
     float *dq = a.dq + (hS + query) * D;
