@@ -41,17 +41,6 @@ __device__ __forceinline__ float row_norm2(const float (&x)[8])
     return a;
 }
 
-// v[lane], for an array every lane of the lane group holds identically.
-template <int N>
-__device__ __forceinline__ float pick(const float (&v)[N], int lane)
-{
-    float r = v[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i)
-        r = lane == i ? v[i] : r;
-    return r;
-}
-
 constexpr int ipow(int b, int e) { return e == 0 ? 1 : b * ipow(b, e - 1); }
 
 template <int D, lh_dtype DT, int LP>
@@ -101,9 +90,11 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         if (j0 + r < a.N) {
             ld_raw(qp + r * D, rq[r]);
             ld_raw(kp + r * D, rk[r]);
+            ld_raw(vp + r * D, rv[r]);
         } else {
             zero_raw(rq[r]);
             zero_raw(rk[r]);
+            zero_raw(rv[r]);
         }
     }
 
@@ -118,12 +109,12 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         const float nk = row_norm2<LANES>(x);
         s[r] = sqrtf(nq) + sqrtf(nk);
     }
-    static_assert(R <= LANES, "a lane group stages its run's scores with one store");
-    {
-        const float mine = pick<R>(s, lane);
-        if (lane < R)
-            s_sc[lg * R + lane] = mine;
-    }
+    // every lane holds the run's scores; lane r stages score r (masked
+    // stores: selecting s[lane] by index would put s in scratch memory)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (lane == r)
+            s_sc[lg * R + r] = s[r];
 
     // window sums of the run, tensor after tensor
     float tot[3][8];
@@ -160,15 +151,6 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         }
     };
     cascade(0, rq);
-    // V is loaded only now (into the registers Q used): keeps two tensors in flight, not three
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (j0 + r < a.N)
-            ld_raw(vp + r * D, rv[r]);
-        else
-            zero_raw(rv[r]);
-    }
     cascade(1, rk);
     cascade(2, rv);
 
