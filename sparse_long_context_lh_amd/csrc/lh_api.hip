@@ -95,17 +95,23 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     // Levels finished inside the row tiles; coarser ones keep window sums in
     // IR_FPART (front, entries i of level l) and IR_SPART (scatter-back
     // adjoint, u-space windows m = i + 1, the last tile's tail included).
-    pl->LT = L > 1 ? (tile_levels(d, log2p) < L - 1 ? tile_levels(d, log2p) : L - 1) : 0;
+    {
+        const int ltf = tile_levels(d, log2p, front_nc(log2p)), lts = tile_levels(d, log2p, sbwd_nc(log2p));
+        pl->LT = L > 1 ? (ltf < L - 1 ? ltf : L - 1) : 0;
+        pl->LTs = L > 1 ? (lts < L - 1 ? lts : L - 1) : 0;
+    }
     for (int l = 0; l < kMaxLevels; ++l)
         pl->fpart_off[l] = pl->spart_off[l] = pl->spart_n[l] = -1;
     pl->fpart_rows = pl->spart_rows = 0;
+    for (int l = pl->LT; l <= L - 2; ++l) {
+        pl->fpart_off[l] = pl->fpart_rows;
+        pl->fpart_rows += pl->n[l];
+    }
     {
-        const int64_t T = tile_rows(d, log2p);
+        const int64_t T = tile_rows(d, log2p, sbwd_nc(log2p));
         int64_t m = (N + 1 + T - 1) / T * T; // u-space positions the tiles cover
-        m >>= pl->LT * log2p;
-        for (int l = pl->LT; l <= L - 2; ++l) {
-            pl->fpart_off[l] = pl->fpart_rows;
-            pl->fpart_rows += pl->n[l];
+        m >>= pl->LTs * log2p;
+        for (int l = pl->LTs; l <= L - 2; ++l) {
             pl->spart_n[l] = m;
             pl->spart_off[l] = pl->spart_rows;
             pl->spart_rows += m;
@@ -317,7 +323,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
             a.part_off[l] = pl.spart_off[l];
             a.part_n[l] = pl.spart_n[l];
         }
-        a.H = H; a.L = L; a.log2p = pl.log2p; a.LT = pl.LT;
+        a.H = H; a.L = L; a.log2p = pl.log2p; a.LT = pl.LTs;
         if (launch_scatter_bwd(pl, a, s) != hipSuccess)
             return LH_EHIP;
     }

@@ -47,7 +47,7 @@ template <int D, lh_dtype DT, int LP>
 __global__ __launch_bounds__(256) void k_front(FrontArgs a)
 {
     typedef typename Elem<DT>::T T;
-    typedef TileShape<D, LP> Sh;
+    typedef TileShape<D, LP, front_nc(LP)> Sh;
     constexpr int LANES = Sh::LANES, NLG = Sh::NLG, NC = Sh::NC, R = Sh::R, P = 1 << LP;
     __shared__ __attribute__((aligned(16))) float s_sum[3][NLG][D];
     // scores of the tile, level after level (T / p^l each): written to memory
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
 template <int D, lh_dtype DT, int LP>
 static hipError_t launch_front_t(const Plan &pl, const FrontArgs &a, hipStream_t s)
 {
-    constexpr int T = TileShape<D, LP>::T;
+    constexpr int T = TileShape<D, LP, front_nc(LP)>::T;
     const dim3 grid((unsigned)((pl.N + T - 1) / T), (unsigned)pl.H);
     hipLaunchKernelGGL((k_front<D, DT, LP>), grid, dim3(256), 0, s, a);
     constexpr int NLG = 256 / (D / 8);

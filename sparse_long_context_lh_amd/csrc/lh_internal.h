@@ -36,21 +36,21 @@ enum InternalRegion {
 // (d/8 lanes, 8 elements each) owns R = p^NC consecutive rows; a workgroup of
 // 256 threads owns NLG * R rows. Levels whose windows fit a tile (p^l divides
 // it) are finished inside the tile kernel; coarser ones by one small kernel
-// per level over the tile kernel's window sums.
+// per level over the tile kernel's window sums. The front pass (three
+// tensors) runs 4 rows per lane group (8 for p = 8); the scatter-back adjoint
+// (one tensor) 16 (8 for p = 8).
 constexpr int clog2(int x) { return x <= 1 ? 0 : 1 + clog2(x / 2); }
-template <int D, int LP> struct TileShape {
+constexpr int front_nc(int lp) { return lp == 1 ? 2 : 1; }
+constexpr int sbwd_nc(int lp) { return lp == 1 ? 4 : (lp == 2 ? 2 : 1); }
+template <int D, int LP, int NC_> struct TileShape {
     static constexpr int LANES = D / 8, NLG = 256 / LANES;
-    static constexpr int NC = LP == 1 ? 2 : 1;
-    static constexpr int R = 1 << (NC * LP); // 4 (p = 2), 4 (p = 4), 8 (p = 8)
+    static constexpr int NC = NC_;
+    static constexpr int R = 1 << (NC * LP);
     static constexpr int T = NLG * R;
     static constexpr int LMAX = clog2(T) / LP;
 };
-inline int tile_rows(int d, int log2p)
-{
-    const int nlg = 256 / (d / 8), nc = log2p == 1 ? 2 : 1;
-    return nlg << (nc * log2p);
-}
-inline int tile_levels(int d, int log2p) { return clog2(tile_rows(d, log2p)) / log2p; }
+inline int tile_rows(int d, int log2p, int nc) { return (256 / (d / 8)) << (nc * log2p); }
+inline int tile_levels(int d, int log2p, int nc) { return clog2(tile_rows(d, log2p, nc)) / log2p; }
 
 struct Plan {
     int64_t N;
@@ -65,7 +65,8 @@ struct Plan {
     uint32_t mat_mask;           // bit l set: level l pooled rows are written by the front kernel
     int64_t mat_off[kMaxLevels]; // row offset of a materialized level inside one head's pooled block
     int64_t mat_rows;
-    int LT;                      // levels 1..LT are finished inside the row-tile kernels
+    int LT;                      // levels 1..LT are finished inside the front pass's row tiles
+    int LTs;                     // the same for the scatter-back adjoint's row tiles
     int64_t fpart_off[kMaxLevels]; // row offset of level l's window sums in a head's IR_FPART block
     int64_t fpart_rows;
     int64_t spart_n[kMaxLevels];   // u-space windows of level l kept in IR_SPART (l >= LT)

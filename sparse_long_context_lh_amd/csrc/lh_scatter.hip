@@ -222,7 +222,7 @@ template <int D, lh_dtype DT, int LP>
 __global__ __launch_bounds__(256) void k_scatter_bwd(ScatterBwdArgs a)
 {
     typedef typename Elem<DT>::T T;
-    typedef TileShape<D, LP> Sh;
+    typedef TileShape<D, LP, sbwd_nc(LP)> Sh;
     constexpr int LANES = Sh::LANES, NLG = Sh::NLG, NC = Sh::NC, R = Sh::R, P = 1 << LP;
     __shared__ __attribute__((aligned(16))) float s_sum[NLG][D];
     __shared__ int32_t s_slot[2 * Sh::T]; // levels 0..LT: T/p^l windows each
@@ -376,10 +376,10 @@ __global__ __launch_bounds__(256) void k_scatter_bwd_up(ScatterBwdArgs a, int l)
 template <int D, lh_dtype DT, int LP>
 static hipError_t launch_scatter_bwd_t(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s)
 {
-    constexpr int T = TileShape<D, LP>::T, NLG = 256 / (D / 8);
+    constexpr int T = TileShape<D, LP, sbwd_nc(LP)>::T, NLG = 256 / (D / 8);
     const dim3 grid((unsigned)((pl.N + 1 + T - 1) / T), (unsigned)pl.H);
     hipLaunchKernelGGL((k_scatter_bwd<D, DT, LP>), grid, dim3(256), 0, s, a);
-    for (int l = pl.LT + 1; l < pl.L; ++l) {
+    for (int l = pl.LTs + 1; l < pl.L; ++l) {
         const int64_t ml = (pl.spart_n[l - 1] + pl.p - 1) / pl.p;
         const int64_t items = (int64_t)pl.H * ml;
         hipLaunchKernelGGL((k_scatter_bwd_up<D>), dim3((unsigned)((items + NLG - 1) / NLG)), dim3(256), 0, s, a, l);
