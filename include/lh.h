@@ -54,9 +54,10 @@
  *
  * Precision. Scores are fp32 in the stated order (bit-exact by design).
  * Pooling sums in fp32. The attention runs on fp16 matrix cores with fp32
- * accumulation: the logits use an fp16 hi/lo pair for both the query and the
- * key rows (three products, about 22 significant bits, so pooled rows are not
- * truncated before the softmax); P, V, dS and the fp16 hi/lo pair of dO_sub
+ * accumulation: the logits use an fp16 hi/lo pair for the query rows (about
+ * 22 significant bits, so pooled rows are not truncated before the softmax)
+ * and fp16 key rows, plus the key's lo part for fp32 inputs; P, V, dS and the
+ * fp16 hi/lo pair of dO_sub
  * feed the other products; row statistics, Delta = rowsum(dO_sub * O_sub) and
  * all sums are fp32. Consequently every input, pooled row, scattered-back
  * gradient sum and attention intermediate must stay within the fp16 range

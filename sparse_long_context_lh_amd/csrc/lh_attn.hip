@@ -21,8 +21,13 @@
 // swizzle on 16-byte chunks so that the 32 rows one MFMA operand read touches
 // fall in distinct banks.
 //
-// Precision: a logit is the sum of three products, q_hi.k_hi + q_hi.k_lo +
-// q_lo.k_hi, over fp16 pairs x = hi + lo of the gathered rows; dP uses the
+// Precision: a logit is q_hi.k_hi + q_lo.k_hi over the fp16 pair q = hi + lo
+// of the gathered query row, plus q_hi.k_lo when the inputs are fp32. A
+// query's rounding error shifts every logit of its row coherently, so its lo
+// part is needed; keys' rounding errors are independent and average out over
+// a row, except on the level-0 keys the selection concentrates attention on,
+// and those are the bf16 inputs themselves, exact in fp16. The forward and the
+// backward form the same logits, so both see the same P. dP uses the
 // fp16 pair of dO_sub (two products); the forward's P.V uses an fp16 pair of
 // P (two products), so O_sub, and with it delta = rowsum(dO_sub * O_sub),
 // agree with the P the backward recomputes (dS = P (dP - delta) cancels
@@ -140,20 +145,20 @@ __device__ __forceinline__ int swzg(int row, int ch)
 // One workgroup per 128 queries (32 per wave, Q hi / lo fragments in
 // registers); keys stream through LDS 32 at a time in a two-stage ring
 // filled asynchronously, two workgroups per CU.
-template <int D> struct FwdStage {
+template <int D, bool KLO> struct FwdStage {
     static constexpr int BN = 32;
     static constexpr int KCH = D / 8;  // chunks per K row
     static constexpr int VCH = BN / 8; // chunks per V^T row
     static constexpr int KROWS = BN * KCH, VROWS = D * VCH;
-    static constexpr int KH = 0, KL = KROWS, VT = 2 * KROWS;
-    static constexpr int SIZE = 2 * KROWS + VROWS;
+    static constexpr int KH = 0, KL = KROWS, VT = (KLO ? 2 : 1) * KROWS;
+    static constexpr int SIZE = VT + VROWS;
     static constexpr int KU = KROWS / 256, VU = VROWS / 256; // load rounds per tile
 };
 
-template <int D>
+template <int D, bool KLO>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
 {
-    typedef FwdStage<D> St;
+    typedef FwdStage<D, KLO> St;
     constexpr int BM = 128, BN = St::BN, KCH = St::KCH, VCH = St::VCH;
     constexpr int NS = D / 16;  // k-steps over d
     constexpr int NT = D / 32;  // 32-dim tiles of the output
@@ -186,7 +191,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
 #pragma unroll
         for (int u = 0; u < St::KU; ++u) {
             dma16(khi + k0 * D, koff[u], base + St::KH + 256 * u + 64 * wave);
-            dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
+            if constexpr (KLO)
+                dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
         }
 #pragma unroll
         for (int u = 0; u < St::VU; ++u)
@@ -219,14 +225,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
             issue(kt0 + BN, ring + ((kb + 1) & 1) * St::SIZE);
         if (kt0 > qw + 31)
             return; // this wave's queries all precede these keys
-        const uint4 *sKh = base + St::KH, *sKl = base + St::KL, *sV = base + St::VT;
+        const uint4 *sKh = base + St::KH, *sV = base + St::VT;
         f32x16_t st = zero16();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int idx = kap * KCH + swz<KCH>(kap, 2 * s + g);
             const uint4 kh = sKh[idx];
             st = mfma32(kh, qh[s], st);
-            st = mfma32(sKl[idx], qh[s], st);
+            if constexpr (KLO)
+                st = mfma32(base[St::KL + idx], qh[s], st);
             st = mfma32(kh, ql[s], st);
         }
         // scaled logits y = st * log2(e)/sqrt(d); the row maximum is taken on
@@ -313,10 +320,18 @@ hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
 {
     const unsigned nqb = (unsigned)((pl.S + 127) / 128);
     const dim3 grid(nqb * pl.H);
-    if (pl.d == 128)
-        hipLaunchKernelGGL((k_attn_fwd<128>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_attn_fwd<64>), grid, dim3(256), 0, s, a);
+    const bool klo = pl.dt == LH_F32; // see the precision note at the top of this file
+    if (pl.d == 128) {
+        if (klo)
+            hipLaunchKernelGGL((k_attn_fwd<128, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_attn_fwd<128, false>), grid, dim3(256), 0, s, a);
+    } else {
+        if (klo)
+            hipLaunchKernelGGL((k_attn_fwd<64, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_attn_fwd<64, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -352,7 +367,7 @@ __device__ __forceinline__ void wait_async_n()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D>
+template <int D, bool KLO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     typedef DkdvStage<D> St;
@@ -421,12 +436,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         issue_cols(q0, base);
     };
 
-    uint4 kh[NS], klf[NS], vf[NS];
+    uint4 kh[NS], vf[NS], klf[KLO ? NS : 1];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t off = (hS + key) * D + 16 * s + 8 * g;
         kh[s] = ld16(a.khi + off);
-        klf[s] = ld16(a.klo + off);
+        if constexpr (KLO)
+            klf[s] = ld16(a.klo + off);
         vf[s] = ld16(a.v + off);
     }
     f32x16_t dvT[NT], dkT[NT];
@@ -490,13 +506,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             LH_FENCE;
             st = mfma32(f[1], kh[s], st);
             LH_FENCE;
+            if constexpr (KLO) {
+                st = mfma32(f[0], klf[s], st);
+                LH_FENCE;
+            }
             if (pre) nx[2] = rd(s + 1, 2);
             LH_FENCE;
-            st = mfma32(f[0], klf[s], st);
+            dp = mfma32(f[2], vf[s], dp);
             LH_FENCE;
             if (pre) nx[3] = rd(s + 1, 3);
-            LH_FENCE;
-            dp = mfma32(f[2], vf[s], dp);
             LH_FENCE;
             dp = mfma32(f[3], vf[s], dp);
             LH_FENCE;
@@ -629,19 +647,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 template <int D>
-static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
+static void launch_dkdv_t(const dim3 grid, const AttnBwdArgs &a, bool klo, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_attn_bwd_dkdv<D>), grid, dim3(256), 0, s, a);
+    if (klo)
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<D, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<D, false>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
 {
     const unsigned nkb = (unsigned)((pl.S + 127) / 128);
     const dim3 grid(nkb * pl.H);
+    const bool klo = pl.dt == LH_F32; // see the precision note at the top of this file
     if (pl.d == 128)
-        launch_dkdv_t<128>(grid, a, s);
+        launch_dkdv_t<128>(grid, a, klo, s);
     else
-        launch_dkdv_t<64>(grid, a, s);
+        launch_dkdv_t<64>(grid, a, klo, s);
     return hipGetLastError();
 }
 
