@@ -25,6 +25,10 @@ FLAGS = [
     # packed fp32 VALU ops stay off: hipcc must not emit v_pk_{add,mul,fma}_f32.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions. The attention kernels keep their MFMA accumulators in
+# ordinary VGPRs where they fit: the vector work on logits and outputs then
+# reads them directly instead of copying out of accumulation registers.
+EXTRA = {"lh_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def source_digest() -> str:
@@ -41,7 +45,7 @@ def source_digest() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))

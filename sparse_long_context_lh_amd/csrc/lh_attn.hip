@@ -143,8 +143,15 @@ __device__ __forceinline__ int swzg(int row, int ch)
 
 // ============================================================== forward
 // One workgroup per 128 queries (32 per wave, Q hi / lo fragments in
-// registers); keys stream through LDS 32 at a time in a two-stage ring
+// registers); keys stream through LDS 32 at a time in a three-stage ring
 // filled asynchronously, two workgroups per CU.
+//
+// Software pipeline: while the matrix cores form the logits of key block
+// j+1, the vector unit turns block j's logits into probabilities, and while
+// they accumulate P_j V_j it takes the row maximum of block j+1. An MFMA
+// runs in the background of the wave that issued it, so the softmax costs no
+// time as long as it is interleaved with independent MFMAs in program order;
+// the sched_group_barrier pattern below fixes that order.
 template <int D, bool KLO> struct FwdStage {
     static constexpr int BN = 32;
     static constexpr int KCH = D / 8;  // chunks per K row
@@ -153,16 +160,73 @@ template <int D, bool KLO> struct FwdStage {
     static constexpr int KH = 0, KL = KROWS, VT = (KLO ? 2 : 1) * KROWS;
     static constexpr int SIZE = VT + VROWS;
     static constexpr int KU = KROWS / 256, VU = VROWS / 256; // load rounds per tile
+    static constexpr int LOADS = (KLO ? 2 : 1) * KU + VU;    // transfers per thread per stage
+    static constexpr int NSLOT = 3;
 };
 
+// hi = fp16(x), lo = fp16(x - hi) for 8 values. The residual comes from one
+// mixed-precision fma per value (fp16 operand, fp32 operand, fp16 result):
+// x - hi is exact in fp32, so this rounds exactly as converting it would.
+__device__ __forceinline__ void split8_mix(const float *x, uint4 &hi, uint4 &lo)
+{
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = pack_f16x2(x[2 * e], x[2 * e + 1]);
+        asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l[e]) : "v"(h[e]), "v"(x[2 * e]));
+        asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "+v"(l[e])
+            : "v"(h[e]), "v"(x[2 * e + 1]));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// pairwise sum of a tile's 16 probabilities
+__device__ __forceinline__ float tile_sum(const float *pr)
+{
+    float t8[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+        t8[v] = pr[v] + pr[v + 8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        t8[v] += t8[v + 4];
+    return (t8[0] + t8[2]) + (t8[1] + t8[3]);
+}
+
+// An LDS address the compiler cannot split into a loop-invariant part per
+// access: every fragment read of a stage becomes one base register plus an
+// immediate offset instead of one precomputed register per fragment.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef const u32x4_t __attribute__((address_space(3))) *lds_cptr;
+__device__ __forceinline__ lds_cptr lane_base(const uint4 *p)
+{
+    uint32_t off = (uint32_t)(size_t)p; // low word of a generic LDS address = LDS offset
+    asm volatile("" : "+v"(off));
+    return (lds_cptr)(size_t)off;
+}
+__device__ __forceinline__ uint4 lds_ld(lds_cptr p, int i) { return __builtin_bit_cast(uint4, p[i]); }
+
+template <bool B> struct Flag {
+    static constexpr bool value = B;
+};
+
+// max over lanes l and l ^ 32 (the two lane groups holding one column)
+__device__ __forceinline__ float max_pair(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, bool KLO>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
+__global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 {
     typedef FwdStage<D, KLO> St;
-    constexpr int BM = 128, BN = St::BN, KCH = St::KCH, VCH = St::VCH;
+    constexpr int BM = 128, BN = St::BN;
     constexpr int NS = D / 16;  // k-steps over d
     constexpr int NT = D / 32;  // 32-dim tiles of the output
-    __shared__ uint4 ring[2 * St::SIZE];
+    __shared__ uint4 ring[St::NSLOT * St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -175,19 +239,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
     const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D;
     const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
 
+    const int64_t kend = min(q0 + BM, a.S);
+    const int nkb = (int)((kend + BN - 1) / BN);
+    // last key block this wave reads: its diagonal block, or the workgroup's
+    // last one for rows past S (their outputs are never read)
+    const int jl = (int)min((int64_t)(nkb - 1), qw / BN);
+
     // byte offsets of this thread's chunks in a stage (the stage moves the base)
+    // Operand-order tiles: fragment f of a tile is the 64 x 16 bytes one MFMA
+    // operand reads, lane l's chunk at f * 64 + l, so every fragment read is
+    // one linear 1 KiB LDS access. The transfer of LDS chunk c = 256u + tid
+    // fetches what lane c % 64 of fragment c / 64 needs: for K, k-step
+    // s = c / 64 of key row kappa(c % 32); for V^T, dimension row
+    // 32 t + c % 32 and keys 16 hh + 8 (c / 32 % 2) .. +7 with
+    // (hh, t) = (f / NT, f % NT).
     uint32_t koff[St::KU], voff[St::VU];
 #pragma unroll
     for (int u = 0; u < St::KU; ++u) {
-        const int c = 256 * u + tid, r = c / KCH;
-        koff[u] = 2u * (uint32_t)(r * D + swz<KCH>(r, c % KCH) * 8);
+        const int f = 4 * u + wave;
+        koff[u] = 2u * (uint32_t)(kappa(c32) * D + (2 * f + g) * 8);
     }
 #pragma unroll
     for (int u = 0; u < St::VU; ++u) {
-        const int c = 256 * u + tid, dim = c / VCH;
-        voff[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swz<VCH>(dim, c % VCH) * 8));
+        const int f = 4 * u + wave, hh = f / NT, t = f % NT;
+        voff[u] = 2u * ((uint32_t)(32 * t + c32) * (uint32_t)a.S_pad + (uint32_t)(16 * hh + 8 * g));
     }
-    auto issue = [&](int64_t k0, const uint4 *base) {
+    auto slot = [&](int kb) { return ring + (kb % St::NSLOT) * St::SIZE; };
+    auto issue = [&](int kb) {
+        if (kb >= nkb)
+            return;
+        const int64_t k0 = (int64_t)kb * BN;
+        const uint4 *base = slot(kb);
 #pragma unroll
         for (int u = 0; u < St::KU; ++u) {
             dma16(khi + k0 * D, koff[u], base + St::KH + 256 * u + 64 * wave);
@@ -199,58 +281,86 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
             dma16(vt + k0, voff[u], base + St::VT + 256 * u + 64 * wave);
     };
 
+    issue(0);
     uint4 qh[NS], ql[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         qh[s] = ld16(a.qhi + (hS + qw + c32) * D + 16 * s + 8 * g);
         ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
     }
+    // Consume the fragments here: otherwise the compiler waits for them at
+    // their first use inside the key loop, in every iteration, and those
+    // waits on the memory counter also wait for the ring's transfers in flight.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        asm volatile("" ::"v"(qh[s].x), "v"(ql[s].x));
+    wait_async(); // stage 0 (its transfers were issued before the fragments)
+    issue(1);
+    lds_barrier();
+
+    // S^T tile of key block kb (keys as rows, kappa-permuted)
+    auto logits = [&](const uint4 *base) __attribute__((always_inline)) {
+        f32x16_t st = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint4 kh = base[St::KH + 64 * s + lane];
+            st = mfma32(kh, qh[s], st);
+            if constexpr (KLO)
+                st = mfma32(base[St::KL + 64 * s + lane], qh[s], st);
+            st = mfma32(kh, ql[s], st);
+        }
+        return st;
+    };
+    auto rowmax = [&](const f32x16_t &st) __attribute__((always_inline)) {
+        float mx = st[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v)
+            mx = fmaxf(mx, st[v]);
+        return max_pair(mx);
+    };
 
     f32x16_t o[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         o[t] = zero16();
-    float m = -INFINITY, lsum = 0.0f;
+    float lsum = 0.0f;
+    // Running maximum m of the scaled logits y = st * log2(e)/sqrt(d); the
+    // maximum is taken on st (a positive scale keeps the order, and rounding
+    // is monotonic). Probabilities enter the products as 2^(y - m + 15).
+    f32x16_t st = logits(slot(0));
+    float m = jl > 0 ? rowmax(st) * a.scale_log2 : -INFINITY;
 
-    const int64_t kend = min(q0 + BM, a.S);
-    const int nkb = (int)((kend + BN - 1) / BN);
-    const int kap = kappa(c32);
-
-    auto stage = [&](int kb) __attribute__((always_inline)) {
-        const uint4 *base = ring + (kb & 1) * St::SIZE;
-        const int64_t kt0 = (int64_t)kb * BN;
-        wait_async();
-        lds_barrier(); // stage kb is visible to all waves; the other slot is free
-        if (kb + 1 < nkb)
-            issue(kt0 + BN, ring + ((kb + 1) & 1) * St::SIZE);
-        if (kt0 > qw + 31)
-            return; // this wave's queries all precede these keys
-        const uint4 *sKh = base + St::KH, *sV = base + St::VT;
-        f32x16_t st = zero16();
+    // Probabilities of block st relative to m: the fp16 pair of each run of 8
+    // keys, and their sum added to lsum. The tile's 16 probabilities are
+    // summed first (pairwise) and then added to the running sum: added one by
+    // one, probabilities far below the running sum's half-ulp would all be
+    // rounded away, a systematic loss in the normaliser that the backward's
+    // dS = P (dP - delta) amplifies.
+    auto probs = [&](const f32x16_t &sv, uint4 (&ph)[2], uint4 (&pl)[2]) __attribute__((always_inline)) {
+        const float shift = m - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
+        float pr[16];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int idx = kap * KCH + swz<KCH>(kap, 2 * s + g);
-            const uint4 kh = sKh[idx];
-            st = mfma32(kh, qh[s], st);
-            if constexpr (KLO)
-                st = mfma32(base[St::KL + idx], qh[s], st);
-            st = mfma32(kh, ql[s], st);
-        }
-        // scaled logits y = st * log2(e)/sqrt(d); the row maximum is taken on
-        // st (a positive scale keeps the order, and rounding is monotonic)
-        if (kt0 + 31 > qw) { // diagonal subtile: mask keys after the query
+        for (int v = 0; v < 16; ++v)
+            pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -shift));
+        split8_mix(pr, ph[0], pl[0]);
+        split8_mix(pr + 8, ph[1], pl[1]);
+        lsum += tile_sum(pr);
+    };
+    // O^T += V^T P^T for block kb
+    auto accumulate = [&](const uint4 *base, const uint4 (&ph)[2], const uint4 (&pl)[2]) __attribute__((always_inline)) {
+        const uint4 *sV = base + St::VT;
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                if (kt0 + 16 * (v >> 3) + 8 * g + (v & 7) > qw + c32)
-                    st[v] = -INFINITY;
-        }
-        float mx = st[0];
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int v = 1; v < 16; ++v)
-            mx = fmaxf(mx, st[v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx * a.scale_log2);
-        // rescale only when some row's maximum moved (a factor of 1 changes nothing)
+            for (int t = 0; t < NT; ++t) {
+                const uint4 vv = sV[64 * (hh * NT + t) + lane];
+                o[t] = mfma32(vv, ph[hh], o[t]);
+                o[t] = mfma32(vv, pl[hh], o[t]);
+            }
+    };
+    // rescale O and the running sum when some row's maximum moved (a factor
+    // of 1 changes nothing)
+    auto rescale = [&](float mn) __attribute__((always_inline)) {
         if (__ballot(mn != m) != 0) {
             const float alpha = __builtin_amdgcn_exp2f(m - mn);
             lsum *= alpha;
@@ -261,47 +371,133 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnFwdArgs a)
                     o[t][v] *= alpha;
         }
         m = mn;
+    };
+
+    // Block j < jl: logits of block j+1 alongside the probabilities of block
+    // j, then P_j V_j alongside the row maximum of block j+1 (skipped when
+    // block j+1 is the diagonal one: its maximum is taken after masking).
+    auto body = [&](int j, auto last) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last)::value;
+        const int dj = j % St::NSLOT - (j + 1) % St::NSLOT; // slot(j) - slot(j + 1), in stages
+        const lds_cptr kb = lane_base(slot(j + 1) + lane), vb = kb + (St::VT + dj * St::SIZE);
+        // Fragments are read a little ahead of their MFMAs (LDS reads return
+        // in order): K of block j+1 two k-steps ahead, V^T of block j during
+        // the second half of the logits.
+        uint4 kf[NS], kl[KLO ? NS : 1], vf[2 * NT];
+        auto read_k = [&](int s) __attribute__((always_inline)) {
+            kf[s] = lds_ld(kb, St::KH + 64 * s);
+            if constexpr (KLO)
+                kl[s] = lds_ld(kb, St::KL + 64 * s);
+        };
+        auto read_v = [&](int f) __attribute__((always_inline)) { vf[f] = lds_ld(vb, 64 * f); };
+        read_k(0);
+        read_k(1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Each group below is its own scheduling region (sched_barrier): the
+        // MFMAs first, then vector work that does not depend on them, so the
+        // vector unit runs while the matrix core is busy.
+        const float shift = m - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
         float pr[16];
-        const float shift = mn - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -shift));
-        // The tile's 16 probabilities are summed first (pairwise) and then
-        // added to the running sum: added one by one, probabilities far
-        // below the running sum's half-ulp would all be rounded away, a
-        // systematic loss in the normaliser that the backward's
-        // dS = P (dP - delta) amplifies.
-        float t8[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-            t8[v] = pr[v] + pr[v + 8];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            t8[v] += t8[v + 4];
-        lsum += (t8[0] + t8[2]) + (t8[1] + t8[3]);
         uint4 ph[2], pl[2];
+        auto expo = [&](int v0, int v1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            float x8[8];
+            for (int v = v0; v < v1; ++v)
+                pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -shift));
+        };
+        constexpr int HS = NS / 2;
+        f32x16_t sn = zero16();
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                x8[e] = pr[8 * hh + e];
-            split8_f16(x8, ph[hh], pl[hh]);
-        }
+        for (int s = 0; s < NS; ++s) {
+            if (s + 2 < NS)
+                read_k(s + 2);
+            // V^T fragments 0 .. NT-1 over the second half
+            if (s >= HS) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int dim = 32 * t + c32;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const uint4 vv = sV[dim * VCH + swz<VCH>(dim, 2 * hh + g)];
-                o[t] = mfma32(vv, ph[hh], o[t]);
-                o[t] = mfma32(vv, pl[hh], o[t]);
+                for (int f = (s - HS) * NT / (NS - HS); f < (s - HS + 1) * NT / (NS - HS); ++f)
+                    read_v(f);
             }
+            sn = mfma32(kf[s], qh[s], sn);
+            if constexpr (KLO)
+                sn = mfma32(kl[s], qh[s], sn);
+            sn = mfma32(kf[s], ql[s], sn);
+            if (s < HS)
+                expo(8 * s / HS, 8 * (s + 1) / HS);
+            else if (s == HS)
+                split8_mix(pr, ph[0], pl[0]);
+            else
+                expo(8 + 8 * (s - HS - 1) / (NS - HS - 1), 8 + 8 * (s - HS) / (NS - HS - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // O^T += V^T P^T: per accumulator the order hi, lo of keys 0-15, then
+        // hi, lo of keys 16-31
+#pragma unroll
+        for (int f = NT; f < 2 * NT; ++f)
+            read_v(f);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            o[t] = mfma32(vf[t], ph[0], o[t]);
+        split8_mix(pr + 8, ph[1], pl[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            o[t] = mfma32(vf[t], pl[0], o[t]);
+        lsum += tile_sum(pr);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            o[t] = mfma32(vf[NT + t], ph[1], o[t]);
+        float mn = m;
+        if constexpr (!LAST)
+            mn = fmaxf(m, rowmax(sn) * a.scale_log2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            o[t] = mfma32(vf[NT + t], pl[1], o[t]);
+        st = sn;
+        if constexpr (!LAST)
+            rescale(mn);
+    };
+    // Block jl: mask keys after the query (diagonal block), maximum,
+    // probabilities, P V.
+    auto tail = [&](int j) __attribute__((always_inline)) {
+        const int64_t kt0 = (int64_t)j * BN;
+        if (kt0 + 31 > qw) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if ((int)(kt0 - qw) + 16 * (v >> 3) + 8 * g + (v & 7) > c32)
+                    st[v] = -INFINITY;
+        }
+        rescale(fmaxf(m, rowmax(st) * a.scale_log2));
+        uint4 ph[2], pl[2];
+        probs(st, ph, pl);
+        accumulate(slot(j), ph, pl);
+    };
+
+    // Step j starts by making stage j+1 visible and refilling the slot of
+    // stage j-1. Every wave passes the same sequence of barriers; the loops
+    // below only split it by what this wave computes in each step.
+    auto sync = [&](int j) __attribute__((always_inline)) {
+        if (j + 1 < nkb) {
+            wait_async(); // stage j+1 (the only one in flight)
+            lds_barrier(); // ... visible to all waves; stage j-1's slot is free
+            issue(j + 2);
         }
     };
-    issue(0, ring);
-    for (int kb = 0; kb < nkb; ++kb)
-        stage(kb);
+    int j = 0;
+    for (; j + 1 < jl; ++j) {
+        sync(j);
+        body(j, Flag<false>());
+    }
+    if (jl > 0) {
+        sync(j);
+        body(j, Flag<true>());
+        ++j;
+    }
+    sync(j);
+    tail(j);
+    for (++j; j < nkb; ++j)
+        sync(j);
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float inv = 1.0f / ltot;
