@@ -32,8 +32,9 @@ EXTRA = {"lh_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def source_digest() -> str:
-    """SHA-256 over every source and header under csrc/ and include/ (names and bytes)."""
+    """SHA-256 over the compiler flags and every source and header under csrc/ and include/."""
     h = hashlib.sha256()
+    h.update(repr((FLAGS, EXTRA)).encode())
     inc = os.path.join(os.path.dirname(HERE), "include")
     for d in (CSRC, inc):
         for name in sorted(os.listdir(d)):
