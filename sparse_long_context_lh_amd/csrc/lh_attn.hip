@@ -208,6 +208,10 @@ __device__ __forceinline__ lds_cptr lane_base(const uint4 *p)
 }
 __device__ __forceinline__ uint4 lds_ld(lds_cptr p, int i) { return __builtin_bit_cast(uint4, p[i]); }
 
+template <int M> struct Mode {
+    static constexpr int value = M;
+};
+
 template <bool B> struct Flag {
     static constexpr bool value = B;
 };
@@ -546,8 +550,11 @@ struct DkdvStage {
     static constexpr int ROWS = BQ * RCH;
     static constexpr int COLS = D * TCH;
     static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS, QT = 4 * ROWS, DT = 4 * ROWS + COLS;
-    static constexpr int LS = 4 * ROWS + 2 * COLS; // lse (BQ floats), then delta (BQ floats)
-    static constexpr int SIZE = LS + BQ / 2;        // in 16-byte chunks
+    // row statistics: 64 chunks per wave, the first 4 of them used (wave 0:
+    // lse of queries 0-15, 1: lse 16-31, 2: delta 0-15, 3: delta 16-31); a
+    // whole wave's transfer fills them, so none is predicated
+    static constexpr int LS = 4 * ROWS + 2 * COLS;
+    static constexpr int SIZE = LS + 4 * 64; // in 16-byte chunks
     static constexpr int NBUF = 3;
     // global_load_lds instructions one wave issues per stage
     static constexpr int LOADS = 4 * (ROWS / 256) + 2 * (COLS / 256) + 1;
@@ -599,10 +606,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
     const uint16_t *const cols[2] = {a.qhi_t, a.dohi_t};
-    // lanes 0..3 of every wave fetch 4 of the 16 lse / delta chunks, so each
-    // wave issues the same number of loads per stage (St::LOADS)
+    // each wave fetches 4 of the 16 lse / delta chunks (lanes 4..63 repeat
+    // them), so every wave issues the same number of loads per stage (St::LOADS)
     const float *stat = wave < 2 ? a.lse : a.delta;
-    const uint32_t stat_off = 16u * (uint32_t)((4 * wave + (lane & 3)) & 7);
+    const uint32_t stat_off = 16u * (uint32_t)(4 * (wave & 1) + (lane & 3));
 
     // A stage's transfers in five parts (the four row-major tiles, then the
     // two transposed tiles and the statistics), issued at spread-out points
@@ -615,8 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             dma16(rb, roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
     };
     auto issue_cols = [&](int q0, const uint4 *base) {
-        if (lane < 4) // lanes 0..3 write chunks LS + 4 * wave + lane
-            dma16(stat + hS + q0, stat_off, base + St::LS + 4 * wave);
+        dma16(stat + hS + q0, stat_off, base + St::LS + 64 * wave);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
@@ -667,165 +673,183 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nst = (S - k0 + BQ - 1) / BQ;
 
     int slot = 0; // ring slot of stage it
-    auto stage = [&](int it) __attribute__((always_inline)) {
+    // One stage in four phases, each a group of MFMAs with the vector work
+    // that does not depend on them placed behind them (scheduling barriers
+    // keep the order): S; dP with P = exp2(...) of the finished S; dV with
+    // dS = P (dP - delta); the dS transposes and dK with the dS tile store.
+    // MODE 0: every query of the stage precedes this wave's keys (nothing to
+    // compute); 1: interior stage; 2: masked (diagonal, or reaching past S).
+    auto stage = [&](int it, auto mode_flag) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_flag)::value;
         const uint4 *base = ring + slot * St::SIZE;
         const uint4 *ahead = ring + (slot == 0 ? 2 : slot - 1) * St::SIZE; // slot of stage it + 2
         const int q0 = k0 + it * BQ;
         // stage it has landed once at most one stage's loads are outstanding
         // (this also waits for the previous stage's dS stores, issued after them:
         // vector memory operations complete in issue order)
-        if (it + 1 < nst)
-            wait_async_n<St::LOADS>();
-        else
-            wait_async();
+        wait_async_n<St::LOADS>();
         lds_barrier(); // stage it is visible to all waves; stage it-1's slot is free
-        const bool pre2 = it + 2 < nst; // stage it + 2 is loaded during this one
-        // (near the diagonal a wave may find every query of the stage before its
-        // keys; the mask below zeroes that stage rather than branching around it)
+        // stage it + 2 is loaded during this one; past the last stage, the last
+        // stage again (into the free slot, never read): no branch in the stage
+        const int q2 = k0 + min(it + 2, nst - 1) * BQ;
+        if constexpr (MODE == 0) {
+            issue(q2, ahead);
+            return;
+        }
         const float *sL = reinterpret_cast<const float *>(base + St::LS);
-        const float *sDel = sL + BQ;
-
-        // S and dP. The operands of k-step s+1 are read while the products of
-        // step s run (one LDS read between consecutive products).
-        f32x16_t st = zero16(), dp = zero16();
-        uint4 fa[4], fb[4];
+        const float *sDel = sL + 2 * 256; // (waves 2, 3 of the statistics area)
         auto rd = [&](int s, int i) {
             const int at = ql * RCH + swzg<RCH>(ql, 2 * s + g);
             return base[(i == 0 ? St::QH : i == 1 ? St::QL : i == 2 ? St::DH : St::DL) + at];
         };
-        auto step = [&](int s, const uint4 (&f)[4], uint4 (&nx)[4], bool pre) {
-            if (pre) nx[0] = rd(s + 1, 0);
-            LH_FENCE;
-            st = mfma32(f[0], kh[s], st);
-            LH_FENCE;
-            if (pre) nx[1] = rd(s + 1, 1);
-            LH_FENCE;
-            st = mfma32(f[1], kh[s], st);
-            LH_FENCE;
-            if constexpr (KLO) {
-                st = mfma32(f[0], klf[s], st);
-                LH_FENCE;
-            }
-            if (pre) nx[2] = rd(s + 1, 2);
-            LH_FENCE;
-            dp = mfma32(f[2], vf[s], dp);
-            LH_FENCE;
-            if (pre) nx[3] = rd(s + 1, 3);
-            LH_FENCE;
-            dp = mfma32(f[3], vf[s], dp);
-            LH_FENCE;
-        };
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[i] = rd(0, i);
-#pragma unroll
-        for (int s = 0; s < NS; s += 2) {
-            if (pre2) { // row tiles of stage it + 2, spread over the k-step pairs
-                constexpr int PER = 8 / NS; // tiles per pair: 4 tiles over NS/2 pairs
-#pragma unroll
-                for (int t = 0; t < PER; ++t)
-                    issue_rows(q0 + 2 * BQ, ahead, (s / 2) * PER + t);
-            }
-            step(s, fa, fb, true);
-            step(s + 1, fb, fa, s + 2 < NS);
-        }
-
-        // the first dV / dK operands and the row statistics load while the
-        // last products drain
         auto gfrag = [&](int t, int i) {
             const int dim = 32 * t + c32;
             const int c = dim * TCH + swzg<TCH>(dim, (i & 1) * 2 + g);
             return base[(i < 2 ? St::DT : St::QT) + c];
         };
-        uint4 ga[4], gb[4];
+        // statistics of 4 queries: register v holds query 16(v/8) + 8g + v%8
+        auto stat4 = [&](const float *p, int v0) { // queries 16(v0/8) + 8g + v0%8 .. +3
+            return *reinterpret_cast<const float4 *>(p + 256 * (v0 >> 3) + 8 * g + (v0 & 7));
+        };
+        const int rel = q0 - key; // query - key of register 0's query
+        auto ok = [&](int v) {
+            const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
+            return MODE == 1 || (rel + qi >= 0 && q0 + qi < S);
+        };
+
+        // S: the Q operands of k-step s+1 are read under the products of step s
+        f32x16_t st = zero16(), dp = zero16();
+        uint4 qa[2][2];
+        qa[0][0] = rd(0, 0);
+        qa[0][1] = rd(0, 1);
+        LH_FENCE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ga[i] = gfrag(0, i);
-        float lq[16], dlt[16];
+        for (int s = 0; s < NS; ++s) {
+            if (s % 2 == 1) { // row tiles of stage it + 2, spread over the k-steps
+                constexpr int PER = 8 / NS;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const float4 l0 = *reinterpret_cast<const float4 *>(sL + 16 * hh + 8 * g);
-            const float4 l1 = *reinterpret_cast<const float4 *>(sL + 16 * hh + 8 * g + 4);
-            const float4 d0 = *reinterpret_cast<const float4 *>(sDel + 16 * hh + 8 * g);
-            const float4 d1 = *reinterpret_cast<const float4 *>(sDel + 16 * hh + 8 * g + 4);
-            lq[8 * hh + 0] = l0.x; lq[8 * hh + 1] = l0.y; lq[8 * hh + 2] = l0.z; lq[8 * hh + 3] = l0.w;
-            lq[8 * hh + 4] = l1.x; lq[8 * hh + 5] = l1.y; lq[8 * hh + 6] = l1.z; lq[8 * hh + 7] = l1.w;
-            dlt[8 * hh + 0] = d0.x; dlt[8 * hh + 1] = d0.y; dlt[8 * hh + 2] = d0.z; dlt[8 * hh + 3] = d0.w;
-            dlt[8 * hh + 4] = d1.x; dlt[8 * hh + 5] = d1.y; dlt[8 * hh + 6] = d1.z; dlt[8 * hh + 7] = d1.w;
+                for (int t = 0; t < PER; ++t)
+                    issue_rows(q2, ahead, (s / 2) * PER + t);
+            }
+            if (s + 1 < NS) {
+                qa[(s + 1) & 1][0] = rd(s + 1, 0);
+                qa[(s + 1) & 1][1] = rd(s + 1, 1);
+            }
+            st = mfma32(qa[s & 1][0], kh[s], st);
+            st = mfma32(qa[s & 1][1], kh[s], st);
+            if constexpr (KLO)
+                st = mfma32(qa[s & 1][0], klf[s], st);
+            LH_FENCE;
         }
-        // pr = P * 2^15 (keeps small P out of the fp16 underflow range; the
-        // statistics arrive as LSE - 15 and delta * 2^-15), dS = P (dP - delta).
-        // Only stages that cross the diagonal or the end of S need the mask.
+        // dP; behind its products, pr = P * 2^15 (keeps small P out of the fp16
+        // underflow range; the statistics arrive as LSE - 15 and delta * 2^-15)
         float pr[16], ds[16];
-        if (q0 >= kw + 31 && q0 + BQ <= S) {
+        uint4 da[2][2];
+        da[0][0] = rd(0, 2);
+        da[0][1] = rd(0, 3);
+        LH_FENCE;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lq[v]));
-                ds[v] = pr[v] * __builtin_fmaf(dp[v], kPScaleInv, -dlt[v]);
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) {
+                da[(s + 1) & 1][0] = rd(s + 1, 2);
+                da[(s + 1) & 1][1] = rd(s + 1, 3);
             }
-        } else {
-            const int rel = q0 - key; // query - key of register 0's query
+            dp = mfma32(da[s & 1][0], vf[s], dp);
+            dp = mfma32(da[s & 1][1], vf[s], dp);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 16 * (v >> 3) + 8 * g + (v & 7);
-                const bool ok = rel + qi >= 0 && q0 + qi < S;
-                pr[v] = __builtin_amdgcn_exp2f(ok ? __builtin_fmaf(st[v], a.scale_log2, -lq[v]) : -INFINITY);
-                ds[v] = ok ? pr[v] * __builtin_fmaf(dp[v], kPScaleInv, -dlt[v]) : 0.0f;
+            for (int i = 4 * s / NS; i < 4 * (s + 1) / NS; ++i) { // values 4i .. 4i+3
+                const int v0 = 4 * i;
+                const float4 l4 = stat4(sL, v0);
+                const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = ok(v0 + e) ? st[v0 + e] : -INFINITY; // masked: P = 0
+                    pr[v0 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -lq[e]));
+                }
             }
+            LH_FENCE;
         }
         const uint4 pb0 = pack8h(pr), pb1 = pack8h(pr + 8);
+        // dV; behind it dS = P (dP - delta) (a masked P = 0 gives dS = 0)
+        uint4 ga[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            ga[0][i] = gfrag(0, i);
+        issue_cols(q2, ahead);
+        LH_FENCE;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t + 1 < NT) {
+                ga[(t + 1) & 1][0] = gfrag(t + 1, 0);
+                ga[(t + 1) & 1][1] = gfrag(t + 1, 1);
+            }
+            dvT[t] = mfma32(ga[t & 1][0], pb0, dvT[t]);
+            dvT[t] = mfma32(ga[t & 1][1], pb1, dvT[t]);
+#pragma unroll
+            for (int i = 4 * t / NT; i < 4 * (t + 1) / NT; ++i) {
+                const int v0 = 4 * i;
+                const float4 d4 = stat4(sDel, v0);
+                const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ds[v0 + e] = pr[v0 + e] * __builtin_fmaf(dp[v0 + e], kPScaleInv, -dl[e]);
+            }
+            LH_FENCE;
+        }
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
         // dS of the tile (queries q0.., keys kw..) for the dQ kernel, query-major:
         // C = dS^T(as rows keys) x identity puts query c32 in lane c32 with keys
-        // 16(v/8) + 8g + v%8 in register v (exact: fp16 times 1, fp32 sums of one term)
-        if (q0 >= kw) {
-            f32x16_t tr = mfma32(db0, eye0, zero16());
-            tr = mfma32(db1, eye1, tr);
-            const int qt = q0 / 32;
-            uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
-            float t8[8];
+        // 16(v/8) + 8g + v%8 in register v (exact: fp16 times 1, fp32 sums of one
+        // term); then dK, with the tile's store behind its first products
+        ga[0][2] = gfrag(0, 2);
+        ga[0][3] = gfrag(0, 3);
+        f32x16_t tr = mfma32(db0, eye0, zero16());
+        tr = mfma32(db1, eye1, tr);
+        LH_FENCE;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                t8[e] = tr[e];
-            *reinterpret_cast<uint4 *>(row) = pack8h(t8);
+        for (int t = 0; t < NT; ++t) {
+            if (t + 1 < NT) {
+                ga[(t + 1) & 1][2] = gfrag(t + 1, 2);
+                ga[(t + 1) & 1][3] = gfrag(t + 1, 3);
+            }
+            dkT[t] = mfma32(ga[t & 1][2], db0, dkT[t]);
+            dkT[t] = mfma32(ga[t & 1][3], db1, dkT[t]);
+            if (t == 0) {
+                const int qt = q0 / 32;
+                uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
+                float t8[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                t8[e] = tr[8 + e];
-            *reinterpret_cast<uint4 *>(row + 16) = pack8h(t8);
-        }
-        auto gstep = [&](int t, const uint4 (&f)[4], uint4 (&nx)[4], bool pre) {
-            if (pre) nx[0] = gfrag(t + 1, 0);
-            LH_FENCE;
-            dvT[t] = mfma32(f[0], pb0, dvT[t]);
-            LH_FENCE;
-            if (pre) nx[1] = gfrag(t + 1, 1);
-            LH_FENCE;
-            dvT[t] = mfma32(f[1], pb1, dvT[t]);
-            LH_FENCE;
-            if (pre) nx[2] = gfrag(t + 1, 2);
-            LH_FENCE;
-            dkT[t] = mfma32(f[2], db0, dkT[t]);
-            LH_FENCE;
-            if (pre) nx[3] = gfrag(t + 1, 3);
-            LH_FENCE;
-            dkT[t] = mfma32(f[3], db1, dkT[t]);
-            LH_FENCE;
-        };
+                for (int e = 0; e < 8; ++e)
+                    t8[e] = tr[e];
+                *reinterpret_cast<uint4 *>(row) = pack8h(t8);
 #pragma unroll
-        for (int t = 0; t < NT; t += 2) {
-            if (pre2 && t == 0)
-                issue_cols(q0 + 2 * BQ, ahead);
-            gstep(t, ga, gb, true);
-            gstep(t + 1, gb, ga, t + 2 < NT);
+                for (int e = 0; e < 8; ++e)
+                    t8[e] = tr[8 + e];
+                *reinterpret_cast<uint4 *>(row + 16) = pack8h(t8);
+            }
+            LH_FENCE;
         }
     };
     issue(k0, ring);
-    if (nst > 1)
-        issue(k0 + BQ, ring + St::SIZE);
-    for (int it = 0; it < nst; ++it) {
-        stage(it);
-        slot = slot == 2 ? 0 : slot + 1;
+    issue(k0 + min(1, nst - 1) * BQ, ring + St::SIZE); // (the only stage again when nst = 1)
+    auto next = [&]() { slot = slot == 2 ? 0 : slot + 1; };
+    // stages before this wave's keys; the diagonal one; interior ones; the
+    // last one when it reaches past S (one code path per loop, so the
+    // accumulators stay in place)
+    const int last_int = (k0 + nst * BQ > S) ? nst - 1 : nst; // first stage that needs the S mask
+    int it = 0;
+    for (; it < min(wave, nst); ++it, next())
+        stage(it, Mode<0>());
+    if (it < nst) {
+        stage(it, Mode<2>());
+        ++it;
+        next();
     }
+    for (; it < last_int; ++it, next())
+        stage(it, Mode<1>());
+    for (; it < nst; ++it, next())
+        stage(it, Mode<2>());
+    wait_async(); // transfers past the last stage
 
     float *dk = a.dk + (hS + key) * D;
     float *dv = a.dv + (hS + key) * D;
