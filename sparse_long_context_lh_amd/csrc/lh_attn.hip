@@ -719,6 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
         // S: the Q operands of k-step s+1 are read under the products of step s
         f32x16_t st = zero16(), dp = zero16();
+        float4 lnext;
         uint4 qa[2][2];
         qa[0][0] = rd(0, 0);
         qa[0][1] = rd(0, 1);
@@ -739,6 +740,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             st = mfma32(qa[s & 1][1], kh[s], st);
             if constexpr (KLO)
                 st = mfma32(qa[s & 1][0], klf[s], st);
+            if (s == NS - 1)
+                lnext = stat4(sL, 0); // the statistics a piece needs are read a group ahead
             LH_FENCE;
         }
         // dP; behind its products, pr = P * 2^15 (keeps small P out of the fp16
@@ -759,8 +762,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 4 * s / NS; i < 4 * (s + 1) / NS; ++i) { // values 4i .. 4i+3
                 const int v0 = 4 * i;
-                const float4 l4 = stat4(sL, v0);
-                const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float lq[4] = {lnext.x, lnext.y, lnext.z, lnext.w};
+                lnext = i < 3 ? stat4(sL, v0 + 4) : stat4(sDel, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float sv = ok(v0 + e) ? st[v0 + e] : -INFINITY; // masked: P = 0
@@ -788,8 +791,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 4 * t / NT; i < 4 * (t + 1) / NT; ++i) {
                 const int v0 = 4 * i;
-                const float4 d4 = stat4(sDel, v0);
-                const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float dl[4] = {lnext.x, lnext.y, lnext.z, lnext.w};
+                if (i < 3)
+                    lnext = stat4(sDel, v0 + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     ds[v0 + e] = pr[v0 + e] * __builtin_fmaf(dp[v0 + e], kPScaleInv, -dl[e]);
@@ -800,7 +804,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // dS of the tile (queries q0.., keys kw..) for the dQ kernel, query-major:
         // C = dS^T(as rows keys) x identity puts query c32 in lane c32 with keys
         // 16(v/8) + 8g + v%8 in register v (exact: fp16 times 1, fp32 sums of one
-        // term); then dK, with the tile's store behind its first products
+        // term); then dK, with the tile's store behind its last products
         ga[0][2] = gfrag(0, 2);
         ga[0][3] = gfrag(0, 3);
         f32x16_t tr = mfma32(db0, eye0, zero16());
@@ -814,7 +818,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             dkT[t] = mfma32(ga[t & 1][2], db0, dkT[t]);
             dkT[t] = mfma32(ga[t & 1][3], db1, dkT[t]);
-            if (t == 0) {
+            if (t == NT - 1) { // (the transposes have finished by now)
                 const int qt = q0 / 32;
                 uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
                 float t8[8];
