@@ -54,6 +54,11 @@ def test_backward_p2_d64_fp32():
     _case(4096, 2, 64, 3, 2, 200, torch.float32, n_plant=0, bwd=True, tag="bwd-fp32")
 
 
+def test_backward_fp32_d128():
+    # fp32 inputs at d = 128: the logits take the key's lo part as well
+    _case(4096, 2, 128, 3, 2, 128, torch.float32, n_plant=4, bwd=True, tag="bwd-fp32-d128")
+
+
 def test_backward_L5_p4_shape_of_512k():
     # the 512K workload's pyramid (L=5, p=4) at N=32K: S = 128 + 4*4*32 = 640
     _case(32768, 2, 128, 5, 4, 32, n_plant=32, bwd=True, tag="bwd-L5")
