@@ -138,6 +138,9 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_DST] = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
+    b[IR_QLO8] = b[IR_K8] = Hs * Sp * D;
+    b[IR_TMAX] = 4 * 2 * Hs * (Sp / 32);
+    b[IR_SC8] = 4 * 2 * Hs;
     size_t off = 0;
     for (int r = 0; r < IR_COUNT; ++r) {
         pl->off[r] = off;
@@ -254,6 +257,8 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.hi_t[0] = at<uint16_t>(ws, pl, LH_R_QHI_T);
         ga.hi_t[1] = at<uint16_t>(ws, pl, LH_R_KHI_T);
         ga.hi_t[2] = at<uint16_t>(ws, pl, LH_R_V_T);
+        ga.tmax[0] = at<float>(ws, pl, IR_TMAX);
+        ga.tmax[1] = ga.tmax[0] + (int64_t)H * (pl.S_pad / 32);
         ga.N = N; ga.S = pl.S; ga.S_pad = pl.S_pad; ga.mat_rows = pl.mat_rows; ga.tensor_stride = tensor_stride;
         for (int l = 0; l < kMaxLevels; ++l) {
             ga.mat_off[l] = pl.mat_off[l];
@@ -262,6 +267,20 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.H = H; ga.L = L; ga.log2p = pl.log2p;
         if (launch_gather(pl, ga, s) != hipSuccess)
             return LH_EHIP;
+        if (dt == LH_BF16) { // fp8 copies for the lo products of the logits
+            Lo8Args la;
+            la.src[0] = ga.lo[0];
+            la.src[1] = ga.hi[1];
+            la.tmax[0] = ga.tmax[0];
+            la.tmax[1] = ga.tmax[1];
+            la.dst[0] = at<uint8_t>(ws, pl, IR_QLO8);
+            la.dst[1] = at<uint8_t>(ws, pl, IR_K8);
+            la.sc = at<int32_t>(ws, pl, IR_SC8);
+            la.S_pad = pl.S_pad;
+            la.H = H;
+            if (launch_lo8(pl, la, s) != hipSuccess)
+                return LH_EHIP;
+        }
     }
     record(events, 4, s);
     {
@@ -271,6 +290,9 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         aa.khi = at<uint16_t>(ws, pl, LH_R_KHI);
         aa.klo = at<uint16_t>(ws, pl, LH_R_KLO);
         aa.vt = at<uint16_t>(ws, pl, LH_R_V_T);
+        aa.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
+        aa.k8 = at<uint8_t>(ws, pl, IR_K8);
+        aa.sc8 = at<int32_t>(ws, pl, IR_SC8);
         aa.o = at<float>(ws, pl, LH_R_OSUB);
         aa.lse = at<float>(ws, pl, LH_R_LSE);
         aa.S = pl.S; aa.S_pad = pl.S_pad; aa.H = H;
@@ -347,6 +369,9 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.khi = at<uint16_t>(ws, pl, LH_R_KHI);
     ab.klo = at<uint16_t>(ws, pl, LH_R_KLO);
     ab.v = at<uint16_t>(ws, pl, LH_R_V);
+    ab.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
+    ab.k8 = at<uint8_t>(ws, pl, IR_K8);
+    ab.sc8 = at<int32_t>(ws, pl, IR_SC8);
     ab.qhi_t = at<uint16_t>(ws, pl, LH_R_QHI_T);
     ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);
     ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);

@@ -65,12 +65,6 @@ __device__ __forceinline__ uint4 pack8h(const float *x)
     return make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7]));
 }
 
-// Row kappa(r) of the 32-row block that MFMA row r reads (see header).
-__device__ __forceinline__ int kappa(int r)
-{
-    return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
-}
-
 // Physical 16-byte chunk of logical chunk `ch` in row `row` of an LDS tile
 // whose rows hold NCH chunks (16 for 256-byte rows, 8 for 128-byte rows).
 template <int NCH>
@@ -157,12 +151,24 @@ template <int D, bool KLO> struct FwdStage {
     static constexpr int KCH = D / 8;  // chunks per K row
     static constexpr int VCH = BN / 8; // chunks per V^T row
     static constexpr int KROWS = BN * KCH, VROWS = D * VCH;
-    static constexpr int KH = 0, KL = KROWS, VT = (KLO ? 2 : 1) * KROWS;
+    // KL: the K lo tile (fp16, fp32 inputs) or the fp8 K tile (bf16 inputs:
+    // 2D chunks, padded to one transfer per thread)
+    static constexpr int KH = 0, KL = KROWS, KLSIZE = KLO ? KROWS : 256;
+    static constexpr int VT = KROWS + KLSIZE;
     static constexpr int SIZE = VT + VROWS;
     static constexpr int KU = KROWS / 256, VU = VROWS / 256; // load rounds per tile
-    static constexpr int LOADS = (KLO ? 2 : 1) * KU + VU;    // transfers per thread per stage
     static constexpr int NSLOT = 3;
 };
+
+// Block-scaled fp8 product (see lh_device.h): A and B are the two 16-byte
+// halves of each lane's 32 operand bytes, sa / sb their scales (127 + e).
+__device__ __forceinline__ f32x16_t mfma8(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x16_t c, int sa, int sb)
+{
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    const i32x8_t a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8_t b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 
 // hi = fp16(x), lo = fp16(x - hi) for 8 values. The residual comes from one
 // mixed-precision fma per value (fp16 operand, fp32 operand, fp16 result):
@@ -241,7 +247,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     const int64_t qw = q0 + wave * 32;
     const int64_t hS = (int64_t)h * a.S_pad;
     const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D;
+    const uint8_t *k8 = a.k8 + hS * D;
     const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
+    constexpr int NM = D / 64; // fp8 products of the logits' lo part (bf16 inputs)
 
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
@@ -280,24 +288,49 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             if constexpr (KLO)
                 dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
         }
+        if constexpr (!KLO) // the fp8 tile is stored in operand order: a linear copy
+            dma16(k8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::KL + 64 * wave);
 #pragma unroll
         for (int u = 0; u < St::VU; ++u)
             dma16(vt + k0, voff[u], base + St::VT + 256 * u + 64 * wave);
     };
 
     issue(0);
-    uint4 qh[NS], ql[NS];
+    // Q as MFMA operand B: the fp16 hi part, and the lo part as fp16 (fp32
+    // inputs) or as its fp8 tile (bf16 inputs; lane c32 holds query qw + c32,
+    // which the tile keeps at lane position kappa(c32) + 32g)
+    uint4 qh[NS], ql[KLO ? NS : 1], q8[KLO ? 1 : NM][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         qh[s] = ld16(a.qhi + (hS + qw + c32) * D + 16 * s + 8 * g);
-        ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
+        if constexpr (KLO)
+            ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
+    }
+    int qs = 0, ks = 0; // scales of the head's fp8 Q lo and K tiles
+    if constexpr (!KLO) {
+        const uint8_t *qt8 = a.qlo8 + (hS + qw) * D + 16 * (kappa(c32) + 32 * g);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                q8[m][q] = *reinterpret_cast<const uint4 *>(qt8 + 2048 * m + 1024 * q);
+        qs = a.sc8[h];
+        ks = a.sc8[a.H + h];
     }
     // Consume the fragments here: otherwise the compiler waits for them at
     // their first use inside the key loop, in every iteration, and those
     // waits on the memory counter also wait for the ring's transfers in flight.
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        asm volatile("" ::"v"(qh[s].x), "v"(ql[s].x));
+    for (int s = 0; s < NS; ++s) {
+        asm volatile("" ::"v"(qh[s].x));
+        if constexpr (KLO)
+            asm volatile("" ::"v"(ql[s].x));
+    }
+    if constexpr (!KLO) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+            asm volatile("" ::"v"(q8[m][0].x), "v"(q8[m][1].x), "v"(qs), "v"(ks));
+    }
     wait_async(); // stage 0 (its transfers were issued before the fragments)
     issue(1);
     lds_barrier();
@@ -309,9 +342,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         for (int s = 0; s < NS; ++s) {
             const uint4 kh = base[St::KH + 64 * s + lane];
             st = mfma32(kh, qh[s], st);
-            if constexpr (KLO)
+            if constexpr (KLO) {
                 st = mfma32(base[St::KL + 64 * s + lane], qh[s], st);
-            st = mfma32(kh, ql[s], st);
+                st = mfma32(kh, ql[s], st);
+            }
+        }
+        if constexpr (!KLO) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                st = mfma8(base[St::KL + 128 * m + lane], base[St::KL + 128 * m + 64 + lane], q8[m][0], q8[m][1], st,
+                           ks, qs);
         }
         return st;
     };
@@ -387,7 +427,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         // Fragments are read a little ahead of their MFMAs (LDS reads return
         // in order): K of block j+1 two k-steps ahead, V^T of block j during
         // the second half of the logits.
-        uint4 kf[NS], kl[KLO ? NS : 1], vf[2 * NT];
+        uint4 kf[NS], kl[KLO ? NS : 1], k8f[KLO ? 1 : NM][2], vf[2 * NT];
         auto read_k = [&](int s) __attribute__((always_inline)) {
             kf[s] = lds_ld(kb, St::KH + 64 * s);
             if constexpr (KLO)
@@ -421,10 +461,22 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
                 for (int f = (s - HS) * NT / (NS - HS); f < (s - HS + 1) * NT / (NS - HS); ++f)
                     read_v(f);
             }
+            if (!KLO && s == NS - 2) {
+#pragma unroll
+                for (int mm = 0; mm < NM; ++mm) {
+                    k8f[mm][0] = lds_ld(kb, St::KL + 128 * mm);
+                    k8f[mm][1] = lds_ld(kb, St::KL + 128 * mm + 64);
+                }
+            }
             sn = mfma32(kf[s], qh[s], sn);
-            if constexpr (KLO)
+            if constexpr (KLO) {
                 sn = mfma32(kl[s], qh[s], sn);
-            sn = mfma32(kf[s], ql[s], sn);
+                sn = mfma32(kf[s], ql[s], sn);
+            } else if (s == NS - 1) { // the lo part, as block-scaled fp8 products
+#pragma unroll
+                for (int mm = 0; mm < NM; ++mm)
+                    sn = mfma8(k8f[mm][0], k8f[mm][1], q8[mm][0], q8[mm][1], sn, ks, qs);
+            }
             if (s < HS)
                 expo(8 * s / HS, 8 * (s + 1) / HS);
             else if (s == HS)
@@ -577,6 +629,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
     constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
+    constexpr int NM = D / 64; // fp8 products of the logits' lo part (bf16 inputs)
+    // transfers one wave issues per stage (bf16 inputs: the Q lo tile is the
+    // fp8 tile, one transfer per thread)
+    constexpr int LOADS = 3 * RU + (KLO ? RU : 1) + 2 * TU + 1;
     __shared__ uint4 ring[St::NBUF * St::SIZE];
 
     const int h = blockIdx.x % a.H;
@@ -616,6 +672,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // of the previous stage's math: issued in one burst, their LDS writes
     // stall the operand reads of the products.
     auto issue_rows = [&](int q0, const uint4 *base, int t) {
+        if (!KLO && t == 1) { // the fp8 Q lo tile, stored in operand order: a linear copy
+            dma16(a.qlo8 + (hS + q0) * D, 16u * (uint32_t)(tid % (2 * D)), base + 64 * wave + St::QL);
+            return;
+        }
         const uint16_t *rb = rows[t] + (hS + q0) * D;
 #pragma unroll
         for (int u = 0; u < RU; ++u)
@@ -638,7 +698,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         issue_cols(q0, base);
     };
 
-    uint4 kh[NS], vf[NS], klf[KLO ? NS : 1];
+    uint4 kh[NS], vf[NS], klf[KLO ? NS : 1], k8r[KLO ? 1 : NM][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t off = (hS + key) * D + 16 * s + 8 * g;
@@ -646,6 +706,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if constexpr (KLO)
             klf[s] = ld16(a.klo + off);
         vf[s] = ld16(a.v + off);
+    }
+    // bf16 inputs: this wave's fp8 K tile as operand B (the tile keeps key
+    // kw + kappa(c32) at lane position c32 + 32g: this lane's own position)
+    int ks = 0, qs = 0; // scales of the head's fp8 K and Q lo tiles
+    if constexpr (!KLO) {
+        const uint8_t *kt8 = a.k8 + (hS + kw) * D + 16 * lane;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                k8r[m][q] = *reinterpret_cast<const uint4 *>(kt8 + 2048 * m + 1024 * q);
+        ks = a.sc8[a.H + h];
+        qs = a.sc8[h];
+        // consume them here (see the forward kernel)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+            asm volatile("" ::"v"(k8r[m][0].x), "v"(k8r[m][1].x), "v"(ks), "v"(qs));
     }
     f32x16_t dvT[NT], dkT[NT];
 #pragma unroll
@@ -687,7 +764,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // stage it has landed once at most one stage's loads are outstanding
         // (this also waits for the previous stage's dS stores, issued after them:
         // vector memory operations complete in issue order)
-        wait_async_n<St::LOADS>();
+        wait_async_n<LOADS>();
         lds_barrier(); // stage it is visible to all waves; stage it-1's slot is free
         // stage it + 2 is loaded during this one; past the last stage, the last
         // stage again (into the free slot, never read): no branch in the stage
@@ -720,9 +797,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // S: the Q operands of k-step s+1 are read under the products of step s
         f32x16_t st = zero16(), dp = zero16();
         float4 lnext;
-        uint4 qa[2][2];
+        uint4 qa[2][2], q8[KLO ? 1 : NM][2];
         qa[0][0] = rd(0, 0);
-        qa[0][1] = rd(0, 1);
+        if constexpr (KLO)
+            qa[0][1] = rd(0, 1);
         LH_FENCE;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -734,12 +812,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             if (s + 1 < NS) {
                 qa[(s + 1) & 1][0] = rd(s + 1, 0);
-                qa[(s + 1) & 1][1] = rd(s + 1, 1);
+                if constexpr (KLO)
+                    qa[(s + 1) & 1][1] = rd(s + 1, 1);
+            }
+            if (!KLO && s == NS - 2) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    q8[m][0] = base[St::QL + 128 * m + lane];
+                    q8[m][1] = base[St::QL + 128 * m + 64 + lane];
+                }
             }
             st = mfma32(qa[s & 1][0], kh[s], st);
-            st = mfma32(qa[s & 1][1], kh[s], st);
-            if constexpr (KLO)
+            if constexpr (KLO) {
+                st = mfma32(qa[s & 1][1], kh[s], st);
                 st = mfma32(qa[s & 1][0], klf[s], st);
+            } else if (s == NS - 1) { // the lo part, as block-scaled fp8 products
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    st = mfma8(q8[m][0], q8[m][1], k8r[m][0], k8r[m][1], st, qs, ks);
+            }
             if (s == NS - 1)
                 lnext = stat4(sL, 0); // the statistics a piece needs are read a group ahead
             LH_FENCE;

@@ -133,6 +133,53 @@ __device__ __forceinline__ void unraw(const Raw8<LH_F32> &r, float (&x)[8])
 }
 
 // Element type tags for the layer's inputs / outputs.
+// Row kappa(r) of a 32-row block that MFMA operand row r reads: swaps bits 2
+// and 3 of r (an involution). With it, register v of lane group g of a
+// 32x32 MFMA result holds row 16*(v/8) + 8*g + v%8: runs of 8 consecutive rows.
+__device__ __forceinline__ int kappa(int r)
+{
+    return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+
+// ---------------------------------------------------------------- fp8 lo products
+// The second product of an fp16 pair q = hi + lo (q_lo . k) only corrects the
+// first, so it runs as a block-scaled fp8 (OCP e4m3) MFMA: x is stored as
+// fp8(x * 2^-e) with one exponent e per 32-row tile (scale byte 127 + e).
+// e is the smallest exponent that keeps the tile's largest magnitude within
+// e4m3's 448.
+__device__ __forceinline__ int fp8_scale_exp(float amax)
+{
+    if (!(amax > 0.0f))
+        return -127;
+    int e = (int)ceilf(__log2f(amax * (1.0f / 448.0f)));
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    while (e < 127 && ldexpf(amax, -e) > 448.0f) // (in case log2 rounded down)
+        ++e;
+    return e;
+}
+
+// 8 values times mul to 8 e4m3 bytes (round to nearest even).
+__device__ __forceinline__ uint2 pack8_fp8(const float (&x)[8], float mul)
+{
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * mul, x[1] * mul, 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * mul, x[3] * mul, w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * mul, x[5] * mul, 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * mul, x[7] * mul, w1, true);
+    return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+// Byte offset, inside a 32-row fp8 tile, of elements 8c .. 8c+7 of row rr.
+// The tile is stored in the operand order of v_mfma_scale_f32_32x32x64_f8f6f4:
+// fragment m (elements 64m .. 64m+63) is 64 lanes x 32 bytes, lane l holding
+// row kappa(l % 32) with byte 8p + j = element 64m + 16p + 8(l/32) + j; each
+// fragment is split into two 1 KiB halves (bytes 0-15, then 16-31 of every
+// lane) so that a half is one linear 16-byte-per-lane LDS read.
+__device__ __forceinline__ int fp8_tile_offset(int rr, int c)
+{
+    const int m = c >> 3, p = (c & 7) >> 1, h = c & 1;
+    return m * 2048 + (p >> 1) * 1024 + (kappa(rr) + 32 * h) * 16 + (p & 1) * 8;
+}
+
 template <lh_dtype DT> struct Elem;
 template <> struct Elem<LH_BF16> { typedef uint16_t T; };
 template <> struct Elem<LH_F32> { typedef float T; };

@@ -26,8 +26,11 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     constexpr int NLG = 256 / LANES;
     constexpr int LD = D + 8; // LDS row pitch in bf16 (16 B pad)
     constexpr int CHUNK = 4;  // window rows in flight per tensor
+    constexpr int NR = kGatherTile / NLG; // rows per lane group
+    constexpr bool F8 = DT == LH_BF16;    // fp8 tiles for the lo products (see lh_device.h)
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
     __shared__ int32_t s_ent[kGatherTile];
+    __shared__ uint32_t s_amax[2][2]; // [Q lo, K hi][32-row tile]: largest magnitude (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
     const int lane = threadIdx.x % LANES;
@@ -36,9 +39,13 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
                        reinterpret_cast<const T *>(a.v)};
     if (threadIdx.x < kGatherTile)
         s_ent[threadIdx.x] = a.ent[(int64_t)h * a.S_pad + s0 + threadIdx.x];
+    if (threadIdx.x < 4)
+        s_amax[threadIdx.x >> 1][threadIdx.x & 1] = 0u;
     __syncthreads();
 
-    for (int r = lg; r < kGatherTile; r += NLG) {
+#pragma unroll
+    for (int ri = 0; ri < NR; ++ri) {
+        const int r = lg + NLG * ri;
         const int64_t s = s0 + r;
         const int32_t en = s_ent[r];
         float x[3][8];
@@ -100,6 +107,18 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
             if (t < 2) {
                 split8_f16(x[t], hi, lo);
                 *reinterpret_cast<uint4 *>(a.lo[t] + off) = lo;
+                if constexpr (F8) { // largest magnitude of the fp16 lo part of Q / hi part of K
+                    float v8[8], m8 = 0.0f;
+                    unpack8_f16(t == 0 ? lo : hi, v8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        m8 = fmaxf(m8, fabsf(v8[e]));
+#pragma unroll
+                    for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
+                        m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
+                    if (lane == 0 && m8 > 0.0f) // (32-row tile NLG * ri / 32 of row r)
+                        atomicMax(&s_amax[t][NLG * ri / 32], __float_as_uint(m8));
+                }
             } else {
                 hi = pack8_f16(x[t]);
             }
@@ -108,6 +127,11 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
         }
     }
     __syncthreads();
+
+    // per 32-row tile maxima for the fp8 copies (bf16 inputs; k_lo8 below)
+    if (F8 && threadIdx.x < 4)
+        a.tmax[threadIdx.x >> 1][(int64_t)h * (a.S_pad / 32) + s0 / 32 + (threadIdx.x & 1)] =
+            __uint_as_float(s_amax[threadIdx.x >> 1][threadIdx.x & 1]);
 
     // Transposed copy: 8 consecutive positions of one dimension per 16-byte store.
     constexpr int CH = kGatherTile / 8;
@@ -126,6 +150,61 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
         *reinterpret_cast<uint4 *>(a.hi_t[t] + ((int64_t)h * D + dim) * a.S_pad + s0 + sc * 8) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+// fp8 copies of the gathered Q lo part and K hi part for the block-scaled
+// lo products of the logits (bf16 inputs; see lh_device.h): one scale per
+// head and tensor, from the largest magnitude over the head's tile maxima;
+// tiles of 32 rows in operand order. One workgroup per 32-row tile of a head.
+template <int D>
+__global__ __launch_bounds__(256) void k_lo8(Lo8Args a)
+{
+    __shared__ float s_m[2][4];
+    const int h = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+    const int ntile = (int)(a.S_pad / 32);
+    float m[2] = {0.0f, 0.0f};
+    for (int i = tid; i < ntile; i += 256)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            m[t] = fmaxf(m[t], a.tmax[t][(int64_t)h * ntile + i]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            m[t] = fmaxf(m[t], __shfl_xor(m[t], o));
+        if ((tid & 63) == 0)
+            s_m[t][tid >> 6] = m[t];
+    }
+    __syncthreads();
+    int ex[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        ex[t] = fp8_scale_exp(fmaxf(fmaxf(s_m[t][0], s_m[t][1]), fmaxf(s_m[t][2], s_m[t][3])));
+    if (tile == 0 && tid < 2)
+        a.sc[tid * a.H + h] = 127 + ex[tid]; // every tile computes the same value
+    // 32 rows x D elements of each tensor, 8 elements per thread and step
+    constexpr int CH = D / 8;
+    for (int c = tid; c < 32 * CH; c += 256) {
+        const int rr = c / CH, ch = c % CH;
+        const int64_t row = (int64_t)h * a.S_pad + 32 * tile + rr;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float v8[8];
+            unpack8_f16(*reinterpret_cast<const uint4 *>(a.src[t] + row * D + 8 * ch), v8);
+            uint8_t *tb = a.dst[t] + ((int64_t)h * a.S_pad + 32 * tile) * D;
+            *reinterpret_cast<uint2 *>(tb + fp8_tile_offset(rr, ch)) = pack8_fp8(v8, ldexpf(1.0f, -ex[t]));
+        }
+    }
+}
+
+hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(pl.S_pad / 32), pl.H);
+    if (pl.d == 128)
+        hipLaunchKernelGGL((k_lo8<128>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_lo8<64>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s)

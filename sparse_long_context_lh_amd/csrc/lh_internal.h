@@ -29,6 +29,10 @@ enum InternalRegion {
     IR_DST,                 // fp16 [H][T(T+1)/2][32][32], T = S_pad/32: dS tiles (query-major), causal half
     IR_FPART,               // fp32 window sums [3][H][fpart_rows][d], then maxima [H][fpart_rows]
     IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
+    IR_QLO8,                // e4m3 [H][S_pad/32][32 d] (bf16 inputs): Q lo part, fp8 tiles
+    IR_K8,                  // e4m3 [H][S_pad/32][32 d] (bf16 inputs): K hi part, fp8 tiles
+    IR_TMAX,                // fp32 [2][H][S_pad/32]: largest magnitude of each Q lo / K hi tile
+    IR_SC8,                 // int32 [2][H]: scale of the fp8 Q lo / K tiles of a head (127 + exponent)
     IR_COUNT
 };
 
@@ -129,14 +133,26 @@ struct GatherArgs {
     uint16_t *hi[3];           // fp16 [H][S_pad][d]: Q hi, K hi, V
     uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
     uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
+    float *tmax[2];            // (bf16 inputs) per-tile maxima of the Q lo part and of K hi
     int64_t N, S, S_pad, mat_rows, tensor_stride;
     int64_t mat_off[kMaxLevels];
     int64_t n[kMaxLevels];
     int H, L, log2p;
 };
 
+struct Lo8Args {
+    const uint16_t *src[2]; // fp16 [H][S_pad][d]: Q lo part, K hi part
+    const float *tmax[2];   // [H][S_pad/32] tile maxima
+    uint8_t *dst[2];        // fp8 tiles [H][S_pad/32][32 d]
+    int32_t *sc;            // [2][H]
+    int64_t S_pad;
+    int H;
+};
+
 struct AttnFwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *vt; // fp16 gathered rows (vt: [H][d][S_pad])
+    const uint8_t *qlo8, *k8;                   // bf16 inputs: fp8 tiles of the Q lo part and of K
+    const int32_t *sc8;                         // ... and their scales [2][H]
     float *o;                           // [H][S_pad][d]
     float *lse;                         // [H][S_pad]
     int64_t S, S_pad;
@@ -146,6 +162,8 @@ struct AttnFwdArgs {
 
 struct AttnBwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
+    const uint8_t *qlo8, *k8;                    // bf16 inputs: fp8 tiles of the Q lo part and of K
+    const int32_t *sc8;                          // ... and their scales [2][H]
     const uint16_t *qhi_t, *khi_t;              // fp16 [H][d][S_pad]
     const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
     const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
@@ -202,6 +220,7 @@ hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s);
 hipError_t launch_topk(const Plan &pl, const TopkArgs &a, hipStream_t s);
 hipError_t launch_index(const Plan &pl, const IndexArgs &a, hipStream_t s);
 hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s);
+hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, hipStream_t s);
 hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s);
 hipError_t launch_scatter(const Plan &pl, const ScatterArgs &a, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s);
