@@ -48,7 +48,7 @@ KERNEL_STAGES = [
     (r"lh::k_front(_up)?<", "front"),
     (r"lh::k_topk\(", "topk"),
     (r"lh::k_index\(", "index"),
-    (r"lh::k_gather<", "gather"),
+    (r"lh::k_(gather|lo8)<", "gather"),
     (r"lh::k_attn_fwd<", "attn_fwd"),
     (r"lh::k_pull<\d+, [^,]+, 1, 1,", "scatter"),
     (r"lh::k_scatter_bwd(_up)?<", "scatter_bwd"),

@@ -22,7 +22,11 @@
 // fall in distinct banks.
 //
 // Precision: a logit is q_hi.k_hi + q_lo.k_hi over the fp16 pair q = hi + lo
-// of the gathered query row, plus q_hi.k_lo when the inputs are fp32. A
+// of the gathered query row, plus q_hi.k_lo when the inputs are fp32. With
+// bf16 inputs the correction q_lo.k_hi runs on block-scaled fp8 copies of
+// q_lo and k_hi (one power-of-two scale per head and tensor): it carries the
+// query's low bits, and its own error sits about 2^-15 below the largest
+// |q_lo| |k| of the head, far under the fp16 hi product's. A
 // query's rounding error shifts every logit of its row coherently, so its lo
 // part is needed; keys' rounding errors are independent and average out over
 // a row, except on the level-0 keys the selection concentrates attention on,

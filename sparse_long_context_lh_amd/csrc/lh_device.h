@@ -144,9 +144,11 @@ __device__ __forceinline__ int kappa(int r)
 // ---------------------------------------------------------------- fp8 lo products
 // The second product of an fp16 pair q = hi + lo (q_lo . k) only corrects the
 // first, so it runs as a block-scaled fp8 (OCP e4m3) MFMA: x is stored as
-// fp8(x * 2^-e) with one exponent e per 32-row tile (scale byte 127 + e).
-// e is the smallest exponent that keeps the tile's largest magnitude within
-// e4m3's 448.
+// fp8(x * 2^-e) with one exponent e per head and tensor (scale byte 127 + e),
+// the smallest that keeps the head's largest magnitude within e4m3's 448.
+// Rows far below that maximum lose bits of their lo part, but their logits
+// are small by the same factor, so the absolute logit error stays bounded by
+// about 2^-15 of the head's largest |q_lo| |k|.
 __device__ __forceinline__ int fp8_scale_exp(float amax)
 {
     if (!(amax > 0.0f))
