@@ -106,64 +106,80 @@ __global__ __launch_bounds__(256) void k_pull(PullArgs a)
         base[l] = b;
         b += pull_count(x0, tile, l * lp);
     }
-    float acc[NC + 1][NT][8];
+    float coarse[NT][8]; // levels >= NC, shared by the lane group's R positions
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            acc[NC][t][e] = 0.0f;
+            coarse[t][e] = 0.0f;
     for (int l = NC; l < a.L; ++l) { // levels shared by the lane group's R positions
         const int sh = l * lp;
         const int sl = s_slot[b + (int)((xg >> sh) - (x0 >> sh))];
         b += pull_count(x0, tile, sh);
         if ((uint32_t)sl < (uint32_t)a.S_pad)
-            pull_add<NT>(acc[NC], a, (rowbase + sl) * D + col, a.weighted ? 1.0f / (float)(1 << sh) : 1.0f);
+            pull_add<NT>(coarse, a, (rowbase + sl) * D + col, a.weighted ? 1.0f / (float)(1 << sh) : 1.0f);
     }
     if constexpr (NC == 0) { // L = 1: one position per lane group, level 0 already summed
         const int64_t t = xg - OFF;
         if (t >= 0 && t < a.N)
 #pragma unroll
             for (int u = 0; u < NT; ++u)
-                store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, acc[0][u]);
+                store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, coarse[u]);
     } else {
-        for (int r = 0; r < R; ++r) {
-            const int64_t x = xg + r;
+        // tensor after tensor (the finer levels' partial sums of one tensor
+        // live at a time, which keeps the register count and with it the
+        // number of resident workgroups up)
 #pragma unroll
-            for (int l = NC - 1; l >= 1; --l) {
-                const int sh = l * lp;
-                if ((r & ((1 << sh) - 1)) == 0) {
+        for (int u = 0; u < NT; ++u) {
+            float fine[NC][8]; // fine[l]: levels >= l of the current window (l >= 1)
+            const float *src = a.src[u];
+            T *dst = reinterpret_cast<T *>(a.dst[u]) + (int64_t)h * a.N * D + col;
+            for (int r = 0; r < R; ++r) {
+                const int64_t x = xg + r;
 #pragma unroll
-                    for (int t = 0; t < NT; ++t)
+                for (int l = NC - 1; l >= 1; --l) {
+                    const int sh = l * lp;
+                    if ((r & ((1 << sh) - 1)) == 0) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            acc[l][t][e] = acc[l + 1][t][e];
-                    const int sl = s_slot[base[l] + (int)((x >> sh) - (x0 >> sh))];
-                    if ((uint32_t)sl < (uint32_t)a.S_pad)
-                        pull_add<NT>(acc[l], a, (rowbase + sl) * D + col, a.weighted ? 1.0f / (float)(1 << sh) : 1.0f);
-                }
-            }
-            float o[NT][8];
+                            fine[l][e] = l + 1 < NC ? fine[l + 1 < NC ? l + 1 : 0][e] : coarse[u][e];
+                        const int sl = s_slot[base[l] + (int)((x >> sh) - (x0 >> sh))];
+                        if ((uint32_t)sl < (uint32_t)a.S_pad) {
+                            float y[8];
+                            load8(src + (rowbase + sl) * D + col, y);
+                            const float w = a.weighted ? 1.0f / (float)(1 << sh) : 1.0f;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+                            for (int e = 0; e < 8; ++e)
+                                fine[l][e] = __builtin_fmaf(y[e], w, fine[l][e]);
+                        }
+                    }
+                }
+                float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    o[t][e] = acc[1][t][e];
-            const int sl = s_slot[base[0] + (int)(x - x0)];
-            if ((uint32_t)sl < (uint32_t)a.S_pad)
-                pull_add<NT>(o, a, (rowbase + sl) * D + col, 1.0f);
-            const int64_t t = x - OFF;
-            if (t >= 0 && t < a.N)
+                    o[e] = NC > 1 ? fine[NC > 1 ? 1 : 0][e] : coarse[u][e];
+                const int sl = s_slot[base[0] + (int)(x - x0)];
+                if ((uint32_t)sl < (uint32_t)a.S_pad) {
+                    float y[8];
+                    load8(src + (rowbase + sl) * D + col, y);
 #pragma unroll
-                for (int u = 0; u < NT; ++u)
-                    store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, o[u]);
+                    for (int e = 0; e < 8; ++e)
+                        o[e] = __builtin_fmaf(y[e], 1.0f, o[e]);
+                }
+                const int64_t t = x - OFF;
+                if (t >= 0 && t < a.N)
+                    store8(dst + t * D, o);
+            }
         }
     }
 }
 
-// Levels shared per lane group: a run of R = p^NC positions, 8 or 16.
-static int pull_levels(const Plan &pl)
+// Levels shared per lane group: a run of R = p^NC positions (8 or 16 for the
+// scatter-back; the three-tensor pool adjoint takes runs of 4 at p = 4, whose
+// smaller tiles write faster there, measured).
+static int pull_levels(const Plan &pl, int nt)
 {
-    const int want = pl.log2p == 1 ? 3 : (pl.log2p == 2 ? 2 : 1);
+    const int want = pl.log2p == 1 ? 3 : (pl.log2p == 2 ? (nt == 3 ? 1 : 2) : 1);
     return want < pl.L - 1 ? want : pl.L - 1;
 }
 
@@ -171,7 +187,7 @@ template <int D, lh_dtype DT, int NT, int OFF>
 static hipError_t launch_pull_t(const Plan &pl, const PullArgs &a, hipStream_t s)
 {
     constexpr int NLG = 256 / (D / 8);
-    const int nc = pull_levels(pl);
+    const int nc = pull_levels(pl, NT);
     const int64_t tile = (int64_t)NLG << (nc * pl.log2p);
     if (tile > kPullMaxTile)
         return hipErrorInvalidValue;
