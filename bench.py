@@ -48,11 +48,11 @@ KERNEL_STAGES = [
     (r"lh::k_front(_up)?<", "front"),
     (r"lh::k_topk\(", "topk"),
     (r"lh::k_index\(", "index"),
-    (r"lh::k_(gather|lo8)<", "gather"),
+    (r"lh::k_(gather<|lo8<\d+, 0>)", "gather"),
     (r"lh::k_attn_fwd<", "attn_fwd"),
     (r"lh::k_pull<\d+, [^,]+, 1, 1,", "scatter"),
     (r"lh::k_scatter_bwd(_up)?<", "scatter_bwd"),
-    (r"lh::k_bwd_prep<", "bwd_prep"),
+    (r"lh::k_(bwd_prep<|lo8<\d+, 1>)", "bwd_prep"),
     (r"lh::k_attn_bwd_dkdv<", "attn_bwd_dkdv"),
     (r"lh::k_attn_bwd_dq<", "attn_bwd_dq"),
     (r"lh::k_pull<\d+, [^,]+, 3, 0,", "pool_bwd"),

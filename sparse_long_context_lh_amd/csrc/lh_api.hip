@@ -138,9 +138,9 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_DST] = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
-    b[IR_QLO8] = b[IR_K8] = Hs * Sp * D;
-    b[IR_TMAX] = 4 * 2 * Hs * (Sp / 32);
-    b[IR_SC8] = 4 * 2 * Hs;
+    b[IR_QLO8] = b[IR_K8] = b[IR_V8] = b[IR_DOLO8] = Hs * Sp * D;
+    b[IR_TMAX] = 4 * 4 * Hs * (Sp / 32);
+    b[IR_SC8] = 4 * 4 * Hs;
     size_t off = 0;
     for (int r = 0; r < IR_COUNT; ++r) {
         pl->off[r] = off;
@@ -259,6 +259,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.hi_t[2] = at<uint16_t>(ws, pl, LH_R_V_T);
         ga.tmax[0] = at<float>(ws, pl, IR_TMAX);
         ga.tmax[1] = ga.tmax[0] + (int64_t)H * (pl.S_pad / 32);
+        ga.tmax[2] = ga.tmax[1] + (int64_t)H * (pl.S_pad / 32);
         ga.N = N; ga.S = pl.S; ga.S_pad = pl.S_pad; ga.mat_rows = pl.mat_rows; ga.tensor_stride = tensor_stride;
         for (int l = 0; l < kMaxLevels; ++l) {
             ga.mat_off[l] = pl.mat_off[l];
@@ -275,10 +276,11 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
             la.tmax[1] = ga.tmax[1];
             la.dst[0] = at<uint8_t>(ws, pl, IR_QLO8);
             la.dst[1] = at<uint8_t>(ws, pl, IR_K8);
-            la.sc = at<int32_t>(ws, pl, IR_SC8);
+            la.sc[0] = at<int32_t>(ws, pl, IR_SC8);
+            la.sc[1] = la.sc[0] + H;
             la.S_pad = pl.S_pad;
             la.H = H;
-            if (launch_lo8(pl, la, s) != hipSuccess)
+            if (launch_lo8(pl, la, 0, s) != hipSuccess)
                 return LH_EHIP;
         }
     }
@@ -358,9 +360,27 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         a.delta = at<float>(ws, pl, IR_DELTA);
         a.lse = at<float>(ws, pl, LH_R_LSE);
         a.lse15 = at<float>(ws, pl, IR_LSE15);
+        float *tmax = at<float>(ws, pl, IR_TMAX);
+        const int64_t ntile = (int64_t)H * (pl.S_pad / 32);
+        a.tmax = pl.dt == LH_BF16 ? tmax + 3 * ntile : nullptr;
         a.S = pl.S; a.S_pad = pl.S_pad; a.H = H;
         if (launch_bwd_prep(pl, a, s) != hipSuccess)
             return LH_EHIP;
+        if (pl.dt == LH_BF16) { // fp8 copies for the lo product of dP: the dO_sub lo part and V
+            Lo8Args la;
+            la.src[0] = a.dolo;
+            la.src[1] = at<uint16_t>(ws, pl, LH_R_V);
+            la.tmax[0] = tmax + 3 * ntile;
+            la.tmax[1] = tmax + 2 * ntile;
+            la.dst[0] = at<uint8_t>(ws, pl, IR_DOLO8);
+            la.dst[1] = at<uint8_t>(ws, pl, IR_V8);
+            la.sc[0] = at<int32_t>(ws, pl, IR_SC8) + 3 * H;
+            la.sc[1] = at<int32_t>(ws, pl, IR_SC8) + 2 * H;
+            la.S_pad = pl.S_pad;
+            la.H = H;
+            if (launch_lo8(pl, la, 1, s) != hipSuccess)
+                return LH_EHIP;
+        }
     }
     record(events, 2, s);
     AttnBwdArgs ab;
@@ -371,6 +391,8 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.v = at<uint16_t>(ws, pl, LH_R_V);
     ab.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
     ab.k8 = at<uint8_t>(ws, pl, IR_K8);
+    ab.v8 = at<uint8_t>(ws, pl, IR_V8);
+    ab.dolo8 = at<uint8_t>(ws, pl, IR_DOLO8);
     ab.sc8 = at<int32_t>(ws, pl, IR_SC8);
     ab.qhi_t = at<uint16_t>(ws, pl, LH_R_QHI_T);
     ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);

@@ -633,10 +633,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
     constexpr int NS = D / 16, NT = D / 32;
     constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
-    constexpr int NM = D / 64; // fp8 products of the logits' lo part (bf16 inputs)
-    // transfers one wave issues per stage (bf16 inputs: the Q lo tile is the
-    // fp8 tile, one transfer per thread)
-    constexpr int LOADS = 3 * RU + (KLO ? RU : 1) + 2 * TU + 1;
+    constexpr int NM = D / 64; // fp8 products of the lo parts (bf16 inputs)
+    // transfers one wave issues per stage (bf16 inputs: the Q lo and dO lo
+    // tiles are fp8 tiles, one transfer per thread each)
+    constexpr int LOADS = 2 * RU + 2 * (KLO ? RU : 1) + 2 * TU + 1;
     __shared__ uint4 ring[St::NBUF * St::SIZE];
 
     const int h = blockIdx.x % a.H;
@@ -676,8 +676,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // of the previous stage's math: issued in one burst, their LDS writes
     // stall the operand reads of the products.
     auto issue_rows = [&](int q0, const uint4 *base, int t) {
-        if (!KLO && t == 1) { // the fp8 Q lo tile, stored in operand order: a linear copy
-            dma16(a.qlo8 + (hS + q0) * D, 16u * (uint32_t)(tid % (2 * D)), base + 64 * wave + St::QL);
+        if (!KLO && (t == 1 || t == 3)) { // fp8 Q lo / dO lo tile, stored in operand order: a linear copy
+            dma16((t == 1 ? a.qlo8 : a.dolo8) + (hS + q0) * D, 16u * (uint32_t)(tid % (2 * D)),
+                  base + 64 * wave + (t == 1 ? St::QL : St::DL));
             return;
         }
         const uint16_t *rb = rows[t] + (hS + q0) * D;
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         issue_cols(q0, base);
     };
 
-    uint4 kh[NS], vf[NS], klf[KLO ? NS : 1], k8r[KLO ? 1 : NM][2];
+    uint4 kh[NS], vf[NS], klf[KLO ? NS : 1], k8r[KLO ? 1 : NM][2], v8r[KLO ? 1 : NM][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t off = (hS + key) * D + 16 * s + 8 * g;
@@ -711,22 +712,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             klf[s] = ld16(a.klo + off);
         vf[s] = ld16(a.v + off);
     }
-    // bf16 inputs: this wave's fp8 K tile as operand B (the tile keeps key
-    // kw + kappa(c32) at lane position c32 + 32g: this lane's own position)
-    int ks = 0, qs = 0; // scales of the head's fp8 K and Q lo tiles
+    // bf16 inputs: this wave's fp8 K and V tiles as operand B (the tiles keep
+    // key kw + kappa(c32) at lane position c32 + 32g: this lane's own position)
+    int ks = 0, qs = 0, vs = 0, ds8 = 0; // scales of the head's fp8 K, Q lo, V, dO lo tiles
     if constexpr (!KLO) {
         const uint8_t *kt8 = a.k8 + (hS + kw) * D + 16 * lane;
+        const uint8_t *vt8 = a.v8 + (hS + kw) * D + 16 * lane;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q) {
                 k8r[m][q] = *reinterpret_cast<const uint4 *>(kt8 + 2048 * m + 1024 * q);
-        ks = a.sc8[a.H + h];
+                v8r[m][q] = *reinterpret_cast<const uint4 *>(vt8 + 2048 * m + 1024 * q);
+            }
         qs = a.sc8[h];
+        ks = a.sc8[a.H + h];
+        vs = a.sc8[2 * a.H + h];
+        ds8 = a.sc8[3 * a.H + h];
         // consume them here (see the forward kernel)
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-            asm volatile("" ::"v"(k8r[m][0].x), "v"(k8r[m][1].x), "v"(ks), "v"(qs));
+            asm volatile("" ::"v"(k8r[m][0].x), "v"(k8r[m][1].x), "v"(v8r[m][0].x), "v"(v8r[m][1].x));
+        asm volatile("" ::"v"(ks), "v"(qs), "v"(vs), "v"(ds8));
     }
     f32x16_t dvT[NT], dkT[NT];
 #pragma unroll
@@ -842,18 +849,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // dP; behind its products, pr = P * 2^15 (keeps small P out of the fp16
         // underflow range; the statistics arrive as LSE - 15 and delta * 2^-15)
         float pr[16], ds[16];
-        uint4 da[2][2];
+        uint4 da[2][2], d8[KLO ? 1 : NM][2];
         da[0][0] = rd(0, 2);
-        da[0][1] = rd(0, 3);
+        if constexpr (KLO)
+            da[0][1] = rd(0, 3);
         LH_FENCE;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (s + 1 < NS) {
                 da[(s + 1) & 1][0] = rd(s + 1, 2);
-                da[(s + 1) & 1][1] = rd(s + 1, 3);
+                if constexpr (KLO)
+                    da[(s + 1) & 1][1] = rd(s + 1, 3);
+            }
+            if (!KLO && s == NS - 2) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    d8[m][0] = base[St::DL + 128 * m + lane];
+                    d8[m][1] = base[St::DL + 128 * m + 64 + lane];
+                }
             }
             dp = mfma32(da[s & 1][0], vf[s], dp);
-            dp = mfma32(da[s & 1][1], vf[s], dp);
+            if constexpr (KLO) {
+                dp = mfma32(da[s & 1][1], vf[s], dp);
+            } else if (s == NS - 1) { // the lo part, as block-scaled fp8 products
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    dp = mfma8(d8[m][0], d8[m][1], v8r[m][0], v8r[m][1], dp, ds8, vs);
+            }
 #pragma unroll
             for (int i = 4 * s / NS; i < 4 * (s + 1) / NS; ++i) { // values 4i .. 4i+3
                 const int v0 = 4 * i;

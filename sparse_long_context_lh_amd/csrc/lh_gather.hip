@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     constexpr bool F8 = DT == LH_BF16;    // fp8 tiles for the lo products (see lh_device.h)
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
     __shared__ int32_t s_ent[kGatherTile];
-    __shared__ uint32_t s_amax[2][2]; // [Q lo, K hi][32-row tile]: largest magnitude (fp32 bits)
+    __shared__ uint32_t s_amax[3][2]; // [Q lo, K hi, V][32-row tile]: largest magnitude (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
     const int lane = threadIdx.x % LANES;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
                        reinterpret_cast<const T *>(a.v)};
     if (threadIdx.x < kGatherTile)
         s_ent[threadIdx.x] = a.ent[(int64_t)h * a.S_pad + s0 + threadIdx.x];
-    if (threadIdx.x < 4)
+    if (threadIdx.x < 6)
         s_amax[threadIdx.x >> 1][threadIdx.x & 1] = 0u;
     __syncthreads();
 
@@ -107,20 +107,20 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
             if (t < 2) {
                 split8_f16(x[t], hi, lo);
                 *reinterpret_cast<uint4 *>(a.lo[t] + off) = lo;
-                if constexpr (F8) { // largest magnitude of the fp16 lo part of Q / hi part of K
-                    float v8[8], m8 = 0.0f;
-                    unpack8_f16(t == 0 ? lo : hi, v8);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        m8 = fmaxf(m8, fabsf(v8[e]));
-#pragma unroll
-                    for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
-                        m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
-                    if (lane == 0 && m8 > 0.0f) // (32-row tile NLG * ri / 32 of row r)
-                        atomicMax(&s_amax[t][NLG * ri / 32], __float_as_uint(m8));
-                }
             } else {
                 hi = pack8_f16(x[t]);
+            }
+            if constexpr (F8) { // largest magnitude of the fp16 lo part of Q, of K hi and of V
+                float v8[8], m8 = 0.0f;
+                unpack8_f16(t == 0 ? lo : hi, v8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m8 = fmaxf(m8, fabsf(v8[e]));
+#pragma unroll
+                for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
+                    m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
+                if (lane == 0 && m8 > 0.0f) // (32-row tile NLG * ri / 32 of row r)
+                    atomicMax(&s_amax[t][NLG * ri / 32], __float_as_uint(m8));
             }
             *reinterpret_cast<uint4 *>(a.hi[t] + off) = hi;
             *reinterpret_cast<uint4 *>(&tile[t][r * LD + lane * 8]) = hi;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     __syncthreads();
 
     // per 32-row tile maxima for the fp8 copies (bf16 inputs; k_lo8 below)
-    if (F8 && threadIdx.x < 4)
+    if (F8 && threadIdx.x < 6)
         a.tmax[threadIdx.x >> 1][(int64_t)h * (a.S_pad / 32) + s0 / 32 + (threadIdx.x & 1)] =
             __uint_as_float(s_amax[threadIdx.x >> 1][threadIdx.x & 1]);
 
@@ -152,11 +152,12 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     }
 }
 
-// fp8 copies of the gathered Q lo part and K hi part for the block-scaled
-// lo products of the logits (bf16 inputs; see lh_device.h): one scale per
-// head and tensor, from the largest magnitude over the head's tile maxima;
-// tiles of 32 rows in operand order. One workgroup per 32-row tile of a head.
-template <int D>
+// fp8 copies of two fp16 tensors for the block-scaled lo products (bf16
+// inputs; see lh_device.h): the gathered Q lo part and K hi part (logits), or
+// the dO_sub lo part and V (dP). One scale per head and tensor, from the
+// largest magnitude over the head's tile maxima; tiles of 32 rows in operand
+// order. One workgroup per 32-row tile of a head.
+template <int D, int WHICH> // (0: Q lo / K hi for the logits, 1: dO lo / V for dP; the same work)
 __global__ __launch_bounds__(256) void k_lo8(Lo8Args a)
 {
     __shared__ float s_m[2][4];
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void k_lo8(Lo8Args a)
     for (int t = 0; t < 2; ++t)
         ex[t] = fp8_scale_exp(fmaxf(fmaxf(s_m[t][0], s_m[t][1]), fmaxf(s_m[t][2], s_m[t][3])));
     if (tile == 0 && tid < 2)
-        a.sc[tid * a.H + h] = 127 + ex[tid]; // every tile computes the same value
+        a.sc[tid][h] = 127 + ex[tid]; // every tile computes the same value
     // 32 rows x D elements of each tensor, 8 elements per thread and step
     constexpr int CH = D / 8;
     for (int c = tid; c < 32 * CH; c += 256) {
@@ -197,13 +198,20 @@ __global__ __launch_bounds__(256) void k_lo8(Lo8Args a)
     }
 }
 
-hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, hipStream_t s)
+hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, int which, hipStream_t s)
 {
     const dim3 grid((unsigned)(pl.S_pad / 32), pl.H);
-    if (pl.d == 128)
-        hipLaunchKernelGGL((k_lo8<128>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_lo8<64>), grid, dim3(256), 0, s, a);
+    if (pl.d == 128) {
+        if (which == 0)
+            hipLaunchKernelGGL((k_lo8<128, 0>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_lo8<128, 1>), grid, dim3(256), 0, s, a);
+    } else {
+        if (which == 0)
+            hipLaunchKernelGGL((k_lo8<64, 0>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_lo8<64, 1>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -31,8 +31,10 @@ enum InternalRegion {
     IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
     IR_QLO8,                // e4m3 [H][S_pad/32][32 d] (bf16 inputs): Q lo part, fp8 tiles
     IR_K8,                  // e4m3 [H][S_pad/32][32 d] (bf16 inputs): K hi part, fp8 tiles
-    IR_TMAX,                // fp32 [2][H][S_pad/32]: largest magnitude of each Q lo / K hi tile
-    IR_SC8,                 // int32 [2][H]: scale of the fp8 Q lo / K tiles of a head (127 + exponent)
+    IR_V8,                  // e4m3 [H][S_pad/32][32 d] (bf16 inputs): V, fp8 tiles
+    IR_DOLO8,               // e4m3 [H][S_pad/32][32 d] (bf16 inputs): lo part of dO_sub, fp8 tiles
+    IR_TMAX,                // fp32 [4][H][S_pad/32]: largest magnitude of each Q lo / K hi / V / dO lo tile
+    IR_SC8,                 // int32 [4][H]: scale of a head's fp8 Q lo / K / V / dO lo tiles (127 + exponent)
     IR_COUNT
 };
 
@@ -133,7 +135,7 @@ struct GatherArgs {
     uint16_t *hi[3];           // fp16 [H][S_pad][d]: Q hi, K hi, V
     uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
     uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
-    float *tmax[2];            // (bf16 inputs) per-tile maxima of the Q lo part and of K hi
+    float *tmax[3];            // (bf16 inputs) per-tile maxima of the Q lo part, of K hi and of V
     int64_t N, S, S_pad, mat_rows, tensor_stride;
     int64_t mat_off[kMaxLevels];
     int64_t n[kMaxLevels];
@@ -141,10 +143,10 @@ struct GatherArgs {
 };
 
 struct Lo8Args {
-    const uint16_t *src[2]; // fp16 [H][S_pad][d]: Q lo part, K hi part
+    const uint16_t *src[2]; // fp16 [H][S_pad][d]: Q lo part and K hi part, or V and the dO_sub lo part
     const float *tmax[2];   // [H][S_pad/32] tile maxima
     uint8_t *dst[2];        // fp8 tiles [H][S_pad/32][32 d]
-    int32_t *sc;            // [2][H]
+    int32_t *sc[2];         // [H] each
     int64_t S_pad;
     int H;
 };
@@ -162,8 +164,8 @@ struct AttnFwdArgs {
 
 struct AttnBwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
-    const uint8_t *qlo8, *k8;                    // bf16 inputs: fp8 tiles of the Q lo part and of K
-    const int32_t *sc8;                          // ... and their scales [2][H]
+    const uint8_t *qlo8, *k8, *v8, *dolo8;       // bf16 inputs: fp8 tiles of the Q lo part, K, V, dO lo part
+    const int32_t *sc8;                          // ... and their scales [4][H]
     const uint16_t *qhi_t, *khi_t;              // fp16 [H][d][S_pad]
     const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
     const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
@@ -203,6 +205,7 @@ struct BwdPrepArgs {
     float *delta;              // [H][S_pad]: rowsum * 2^-15
     const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
     float *lse15;              // [H][S_pad]: lse - 15
+    float *tmax;               // bf16 inputs: [H][S_pad/32] maxima of the lo part's tiles (else null)
     int64_t S, S_pad;
     int H;
 };
@@ -220,7 +223,7 @@ hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s);
 hipError_t launch_topk(const Plan &pl, const TopkArgs &a, hipStream_t s);
 hipError_t launch_index(const Plan &pl, const IndexArgs &a, hipStream_t s);
 hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s);
-hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, hipStream_t s);
+hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, int which, hipStream_t s);
 hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s);
 hipError_t launch_scatter(const Plan &pl, const ScatterArgs &a, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s);

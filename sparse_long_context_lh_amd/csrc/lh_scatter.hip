@@ -430,14 +430,20 @@ hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream
 // The attention backward works with probabilities scaled by 2^15 (kept out of
 // the fp16 underflow range): it reads delta_s * 2^-15 (an exact scaling) and
 // the log2-domain LSE minus 15, so that one fma gives the scaled exponent.
+// With bf16 inputs it also records the largest magnitude of the lo part in
+// each 32-row tile (for its fp8 copy, see k_lo8).
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
 {
     constexpr int LANES = D / 8, NLG = 256 / LANES, LD = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t tile[kPrepTile * LD];
+    __shared__ uint32_t s_amax[kPrepTile / 32]; // largest |lo| per 32-row tile (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kPrepTile;
     const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
+    if (threadIdx.x < kPrepTile / 32)
+        s_amax[threadIdx.x] = 0u;
+    __syncthreads();
     for (int r = lg; r < kPrepTile; r += NLG) {
         const int64_t s = s0 + r;
         const int64_t off = ((int64_t)h * a.S_pad + s) * D + lane * 8;
@@ -469,8 +475,21 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
         *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
         *reinterpret_cast<uint4 *>(&tile[r * LD + lane * 8]) = hi;
+        if (a.tmax) {
+            float m8 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                m8 = fmaxf(m8, fabsf(xl[e]));
+#pragma unroll
+            for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
+                m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
+            if (lane == 0 && m8 > 0.0f)
+                atomicMax(&s_amax[r / 32], __float_as_uint(m8));
+        }
     }
     __syncthreads();
+    if (a.tmax && threadIdx.x < kPrepTile / 32)
+        a.tmax[(int64_t)h * (a.S_pad / 32) + s0 / 32 + threadIdx.x] = __uint_as_float(s_amax[threadIdx.x]);
     constexpr int CH = kPrepTile / 8;
     for (int c = threadIdx.x; c < D * CH; c += 256) {
         const int dim = c / CH, sc = c - (c / CH) * CH;
