@@ -57,8 +57,8 @@
  * accumulation: the logits use an fp16 hi/lo pair for the query rows (about
  * 22 significant bits, so pooled rows are not truncated before the softmax)
  * and fp16 key rows, plus the key's lo part for fp32 inputs; with bf16 inputs
- * the query lo product runs on block-scaled fp8 (e4m3) copies with one
- * power-of-two scale per head; P, V, dS and the
+ * the query lo product and the dO_sub lo product of dP run on block-scaled
+ * fp8 (e4m3) copies with one power-of-two scale per head; P, V, dS and the
  * fp16 hi/lo pair of dO_sub
  * feed the other products; row statistics, Delta = rowsum(dO_sub * O_sub) and
  * all sums are fp32. Consequently every input, pooled row, scattered-back

@@ -31,8 +31,10 @@
 // part is needed; keys' rounding errors are independent and average out over
 // a row, except on the level-0 keys the selection concentrates attention on,
 // and those are the bf16 inputs themselves, exact in fp16. The forward and the
-// backward form the same logits, so both see the same P. dP uses the
-// fp16 pair of dO_sub (two products); the forward's P.V uses an fp16 pair of
+// backward form the same logits, so both see the same P. dP uses the pair
+// of dO_sub: its hi part in fp16 products, its lo part as fp16 (fp32 inputs)
+// or, with bf16 inputs, as a block-scaled fp8 product against an e4m3 copy of
+// V (per-head scales again); the forward's P.V uses an fp16 pair of
 // P (two products), so O_sub, and with it delta = rowsum(dO_sub * O_sub),
 // agree with the P the backward recomputes (dS = P (dP - delta) cancels
 // heavily when |dO_sub| is large). dS, V, the backward's P, dO_sub's hi part
