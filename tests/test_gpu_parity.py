@@ -124,3 +124,29 @@ def test_heads_are_independent():
     full = GpuRun(q, kk, v, L, p, k)
     one = GpuRun(q[1:2].contiguous(), kk[1:2].contiguous(), v[1:2].contiguous(), L, p, k)
     assert torch.equal(full.out[1], one.out[0])
+
+
+def test_heads_of_very_different_magnitudes():
+    # the fp8 copies of the lo products take one scale per head and tensor:
+    # head 0 has Q and V 32 times larger, K 32 times smaller and dO 8 times
+    # larger than the seeded inputs, head 1 the reverse (logits unchanged;
+    # dP, and with it dS, stays well inside the fp16 range)
+    N, H, d, L, p, k = 16384, 2, 128, 3, 4, 64
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 8, 11)
+    dout = make_dout(N, H, d, torch.bfloat16, 12)
+    f = torch.tensor([32.0, 1.0 / 32.0]).view(H, 1, 1)  # powers of two: exact in bf16
+    g = torch.tensor([8.0, 1.0 / 8.0]).view(H, 1, 1)
+    q, kk, v, dout = ((x.float() * s).to(torch.bfloat16) for x, s in ((q, f), (kk, 1.0 / f), (v, f), (dout, g)))
+    say("case scaled heads: N=%d H=%d d=%d L=%d p=%d k=%d" % (N, H, d, L, p, k))
+    check_case(q.cuda(), kk.cuda(), v.cuda(), L, p, k, dout.cuda(), tag="scaled-heads")
+
+
+def test_zero_upstream_gradient():
+    # dO = 0: every lo part and tile maximum is zero (the fp8 scales take
+    # their smallest exponent); all gradients must be exactly zero
+    N, H, d, L, p, k = 8192, 2, 128, 3, 4, 50
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 8, 13))
+    run = GpuRun(q, kk, v, L, p, k, torch.zeros(H, N, d, dtype=torch.bfloat16, device="cuda"))
+    for g in run.grads:
+        assert torch.count_nonzero(g).item() == 0
+    assert torch.all(torch.isfinite(run.out.float()))
