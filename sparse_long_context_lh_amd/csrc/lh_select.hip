@@ -3,12 +3,13 @@
 // k_topk: the stratified top-K of one level (aitrends summary, 핵심 기여 and
 // 방법론 item 6: a chunked bitonic top-K, non-differentiable; techllm review,
 // 한계와 주의할 점: stratified, every segment contributes a fixed count). One
-// workgroup per (head, level, stratum of up to 2048 entries): the stratum's
-// 64-bit keys (fp32 score bits << 32 | ~index, so larger score first and then
-// the lower index) are sorted by a bitonic network in LDS; the quota-th
-// largest key is the threshold, and a ballot compaction writes the kept
-// entries in ascending index order. It also marks the children of every
-// dropped parent as not gathered (slot = -1).
+// workgroup per (head, level, stratum of up to 2048 entries). The pages'
+// kernel sorts each chunk with a bitonic network; only the quota-th largest
+// key (score, then lower index) is needed, so here a radix select finds the
+// quota-th largest score T a byte at a time (per-wave digit histograms in
+// LDS) together with how many entries equal to T are kept, and a ballot
+// compaction writes the kept entries in ascending index order. It also marks
+// the children of every dropped parent as not gathered (slot = -1).
 //
 // k_index: the causal order of the gathered sub-sequence (techllm review,
 // 어떻게 동작하나 step 3: the chosen entries are sorted into causal order).
@@ -22,16 +23,14 @@
 
 namespace lh {
 
-__device__ __forceinline__ uint64_t topk_key(float s, int64_t i)
-{
-    return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-}
-
 __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
 {
-    __shared__ uint64_t keys[kStratum];
-    __shared__ int wave_count[16];
-    const int tid = threadIdx.x;
+    constexpr int NW = 16; // waves of the workgroup
+    static_assert(kStratum == 2 * 1024, "two entries per thread");
+    __shared__ int hist[NW][256]; // per-wave digit counts (no contention across waves)
+    __shared__ int wave_count[NW];
+    __shared__ int s_dig, s_need;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
     int l = 1;
     while (l + 1 < a.L && (int)blockIdx.x >= a.strata_before[l + 1])
@@ -43,56 +42,117 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
     const int64_t base = (int64_t)c * m;
     const float *s = a.scores + (int64_t)h * a.lvl_total + a.lvl_off[l] + base;
 
-    int n2 = 1;
-    while (n2 < m)
-        n2 <<= 1;
-    for (int e = tid; e < n2; e += 1024)
-        keys[e] = e < m ? topk_key(s[e], base + e) : 0ull; // pads sort below every real key
-    __syncthreads();
+    // Scores are non-negative, so their bit patterns order like the values.
+    // Entry tid and entry tid + 1024 of the stratum.
+    uint32_t v[2];
+    bool valid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = tid + 1024 * u;
+        valid[u] = e < m;
+        v[u] = valid[u] ? __float_as_uint(s[e]) : 0u;
+    }
 
-    // Bitonic sort, ascending.
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < (n2 >> 1); t += 1024) {
-                const int i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
-                const int j = i + stride;
-                const bool up = (i & size) == 0;
-                const uint64_t x = keys[i], y = keys[j];
-                if ((x > y) == up) {
-                    keys[i] = y;
-                    keys[j] = x;
+    // The q-th largest score T, one byte at a time from the top (radix
+    // select), and r: how many entries equal to T are kept (the lowest
+    // indices among them). Together these keep exactly the q largest keys
+    // (score, then lower index).
+    uint32_t T = 0u;
+    int r = 0;
+    if (q > 0) { // (uniform)
+        uint32_t prefix = 0u, mask = 0u;
+        int need = q;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < NW * 256; i += 1024)
+                (&hist[0][0])[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (valid[u] && (v[u] & mask) == prefix)
+                    atomicAdd(&hist[wave][(v[u] >> shift) & 255u], 1);
+            __syncthreads();
+            if (wave == 0) {
+                // lane owns digits 4 lane .. 4 lane + 3; suf = entries with a
+                // digit >= 4 lane (suffix sum over lanes)
+                int cnt[4], tot = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int x = 0;
+                    for (int w = 0; w < NW; ++w)
+                        x += hist[w][4 * lane + j];
+                    cnt[j] = x;
+                    tot += x;
+                }
+                int suf = tot;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_down(suf, o);
+                    if (lane + o < 64)
+                        suf += y;
+                }
+                const int above = suf - tot;
+                if (above < need && need <= suf) { // the q-th largest has a digit of this lane
+                    int acc = above, dsel = 0;
+                    for (int j = 3; j >= 0; --j) {
+                        if (acc + cnt[j] >= need) {
+                            dsel = j;
+                            break;
+                        }
+                        acc += cnt[j];
+                    }
+                    s_dig = 4 * lane + dsel;
+                    s_need = need - acc;
                 }
             }
             __syncthreads();
+            prefix |= (uint32_t)s_dig << shift;
+            mask |= 255u << shift;
+            need = s_need;
         }
+        T = prefix;
+        r = need;
     }
-    const uint64_t thr = q > 0 ? keys[n2 - q] : ~0ull;
 
-    // Ballot compaction in ascending index order, 1024 entries per pass.
+    // Ballot compaction in ascending index order, 1024 entries per pass: an
+    // entry is kept if its score is above T, or equal to T with fewer than r
+    // equal ones before it.
     int32_t *sel = a.sel + ((int64_t)h * (a.L - 1) + (l - 1)) * a.k + (int64_t)c * (a.k / C) + min(c, a.k % C);
     int32_t *child_slot = a.slot + (int64_t)h * a.lvl_total + a.lvl_off[l - 1];
-    const int lane = tid & 63, wave = tid >> 6;
     const int p = 1 << a.log2p;
-    int done = 0;
-    for (int e0 = 0; e0 < m; e0 += 1024) {
-        const int e = e0 + tid;
-        const bool keep = e < m && topk_key(s[e], base + e) >= thr;
-        const uint64_t ball = __ballot(keep);
+    int done = 0, tied = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (1024 * u >= m) // (uniform)
+            break;
+        const int e = tid + 1024 * u;
+        const bool tie = q > 0 && valid[u] && v[u] == T;
+        const uint64_t tb = __ballot(tie);
         if (lane == 0)
-            wave_count[wave] = __popcll(ball);
+            wave_count[wave] = __popcll(tb);
         __syncthreads();
-        int before = done;
-        for (int w = 0; w < wave; ++w)
-            before += wave_count[w];
-        int total = 0;
-        for (int w = 0; w < 16; ++w)
+        int tie_rank = tied + __popcll(tb & ((1ull << lane) - 1ull)), ties = 0;
+        for (int w = 0; w < NW; ++w) {
+            tie_rank += w < wave ? wave_count[w] : 0;
+            ties += wave_count[w];
+        }
+        __syncthreads();
+        const bool keep = q > 0 && valid[u] && (v[u] > T || (tie && tie_rank < r));
+        const uint64_t kb = __ballot(keep);
+        if (lane == 0)
+            wave_count[wave] = __popcll(kb);
+        __syncthreads();
+        int before = done + __popcll(kb & ((1ull << lane) - 1ull)), total = 0;
+        for (int w = 0; w < NW; ++w) {
+            before += w < wave ? wave_count[w] : 0;
             total += wave_count[w];
+        }
         if (keep)
-            sel[before + __popcll(ball & ((1ull << lane) - 1ull))] = (int32_t)(base + e);
-        if (e < m && !keep)
+            sel[before] = (int32_t)(base + e);
+        if (valid[u] && !keep)
             for (int cc = 0; cc < p; ++cc)
                 child_slot[((base + e) << a.log2p) + cc] = -1;
         done += total;
+        tied += ties;
         __syncthreads();
     }
 }
