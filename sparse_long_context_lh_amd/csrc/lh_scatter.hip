@@ -18,6 +18,8 @@
 // gathered (pull again, ascending l).
 #include <string.h>
 
+#include <algorithm>
+
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -174,12 +176,29 @@ __global__ __launch_bounds__(256) void k_pull(PullArgs a)
     }
 }
 
-// Levels shared per lane group: a run of R = p^NC positions (8 or 16 for the
-// scatter-back; the three-tensor pool adjoint takes runs of 4 at p = 4, whose
-// smaller tiles write faster there, measured).
+// Gathered rows of levels >= nc a position loads on average with runs of
+// p^nc positions (a shared level's row once per run; finer levels once per
+// window). Level l < L-1 gathers p k of its n_l entries, the top level all.
+static double pull_rows_per_position(const Plan &pl, int nc)
+{
+    double rows = 0.0;
+    for (int l = 0; l < pl.L; ++l) {
+        const double g = l == pl.L - 1 ? 1.0 : std::min(1.0, (double)pl.p * pl.k / (double)pl.n[l]);
+        rows += g / (double)((int64_t)1 << ((l < nc ? l : nc) * pl.log2p));
+    }
+    return rows;
+}
+
+// Levels shared per lane group: a run of R = p^NC positions (8 or 16). The
+// three-tensor pool adjoint takes runs of 4 at p = 4 when that keeps its
+// row loads low: its smaller tiles write faster (measured: 512K tokens, 0.33
+// rows per position, 1.28 -> 1.25 ms), while many shared rows per run make
+// it slower (1M tokens, 0.58 rows per position, 1.29 -> 1.56 ms).
 static int pull_levels(const Plan &pl, int nt)
 {
-    const int want = pl.log2p == 1 ? 3 : (pl.log2p == 2 ? (nt == 3 ? 1 : 2) : 1);
+    int want = pl.log2p == 1 ? 3 : (pl.log2p == 2 ? 2 : 1);
+    if (nt == 3 && pl.log2p == 2 && pl.L > 2 && pull_rows_per_position(pl, 1) <= 0.4)
+        want = 1;
     return want < pl.L - 1 ? want : pl.L - 1;
 }
 
