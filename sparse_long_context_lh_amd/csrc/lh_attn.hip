@@ -129,8 +129,6 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t off_bytes, cons
 
 __device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Workgroup barrier without a memory fence; this wave's LDS reads are complete.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Generic swizzle for NCH chunks per row: rows per 256-byte bank window are
 // 16/NCH; XOR the chunk with the window index so 16 consecutive rows map the

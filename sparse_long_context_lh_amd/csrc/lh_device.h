@@ -132,6 +132,10 @@ __device__ __forceinline__ void unraw(const Raw8<LH_F32> &r, float (&x)[8])
     x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
+// Workgroup barrier without a memory fence: this wave's LDS accesses are
+// complete; its global loads and stores in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Element type tags for the layer's inputs / outputs.
 // Row kappa(r) of a 32-row block that MFMA operand row r reads: swaps bits 2
 // and 3 of r (an involution). With it, register v of lane group g of a

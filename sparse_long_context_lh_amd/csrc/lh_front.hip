@@ -109,12 +109,6 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         const float nk = row_norm2<LANES>(x);
         s[r] = sqrtf(nq) + sqrtf(nk);
     }
-    // every lane holds the run's scores; lane r stages score r (masked
-    // stores: selecting s[lane] by index would put s in scratch memory)
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (lane == r)
-            s_sc[lg * R + r] = s[r];
 
     // window sums of the run, tensor after tensor
     float tot[3][8];
@@ -154,80 +148,151 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
     cascade(1, rk);
     cascade(2, rv);
 
-    // levels NC+1 .. LT from the run totals, in LDS
-    if (LT > NC) {
+    // Levels NC+1 .. LT. A wave's G lane groups hold G consecutive runs, so
+    // every level whose windows fit in G runs is finished by that wave alone,
+    // in its own rows of LDS (ordered by LDS waits, no workgroup barrier);
+    // after one barrier (LDS only: stores in flight are not waited for), wave
+    // 0 finishes the levels whose windows span waves. Window sums are the
+    // ascending sums of their p children from 0, window scores the maxima of
+    // their children (exact, order-free).
+    constexpr int G = 64 / LANES;     // lane groups (runs) per wave
+    constexpr int WL = clog2(G) / LP; // levels above NC whose windows fit in a wave
+    const int wave = threadIdx.x / 64, gl = lg % G, l64 = threadIdx.x & 63;
+    auto lds_wave_sync = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    // level-l scores of the tile, in tile order, from s_sc[sb(l)] (T / p^l of them)
+    auto sb = [&](int l) {
+        int b = 0;
+        for (int q = 0; q < l; ++q)
+            b += Sh::T >> (q * LP);
+        return b;
+    };
+    auto put_score = [&](int l, int e) {
+        const int64_t i = (x0 >> (l * LP)) + e;
+        if (i < (a.N >> (l * LP))) {
+            const float m = s_sc[sb(l) + e];
+            sc[a.lvl_off[l] + i] = m;
+            if (keep && l == LT)
+                pmax[a.part_off[l] + i] = m;
+        }
+    };
+    // Window sums of level l: W windows, child c of window w at row
+    // crow(w P + c) of s_sum, the result to row w0 + w and to memory as window
+    // i0 + w of the level; the 3 W (tensor, window) tasks are shared out over
+    // nslots lane groups (this one is slot). Reads complete before any write.
+    auto sum_level = [&](int l, int W, int i0, int w0, int cbase, int cper, int slot, int nslots) {
+        auto crow = [&](int g) { return cbase + (g / cper) * G + g % cper; };
+        float res[2][8];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int task = slot + n * nslots;
+            if (task < 3 * W) {
+                const int t = task / W, w = task - t * W;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    res[n][e] = 0.0f;
+                for (int c = 0; c < P; ++c) {
+                    const int row = crow(w * P + c);
+                    const float4 lo = *reinterpret_cast<const float4 *>(&s_sum[t][row][col]);
+                    const float4 hi = *reinterpret_cast<const float4 *>(&s_sum[t][row][col + 4]);
+                    res[n][0] += lo.x; res[n][1] += lo.y; res[n][2] += lo.z; res[n][3] += lo.w;
+                    res[n][4] += hi.x; res[n][5] += hi.y; res[n][6] += hi.z; res[n][7] += hi.w;
+                }
+                const int64_t i = (x0 >> (l * LP)) + i0 + w;
+                if (i < (a.N >> (l * LP)))
+                    put_sum(t, l, i, res[n]);
+            }
+        }
+        lds_wave_sync();
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int task = slot + n * nslots;
+            if (task < 3 * W) {
+                const int t = task / W, w = task - t * W;
+                *reinterpret_cast<float4 *>(&s_sum[t][w0 + w][col]) = make_float4(res[n][0], res[n][1], res[n][2], res[n][3]);
+                *reinterpret_cast<float4 *>(&s_sum[t][w0 + w][col + 4]) = make_float4(res[n][4], res[n][5], res[n][6], res[n][7]);
+            }
+        }
+        lds_wave_sync();
+    };
+    // Window scores of level l: entries e0 .. e0 + cnt - 1 (tile order), one
+    // per lane of this wave, from level l-1; stored to memory as well.
+    auto score_level = [&](int l, int e0, int cnt) {
+        if (l64 < cnt) {
+            const int e = e0 + l64;
+            const float *c = &s_sc[sb(l - 1) + e * P];
+            float m = c[0];
+#pragma unroll
+            for (int q = 1; q < P; ++q)
+                m = fmaxf(m, c[q]);
+            s_sc[sb(l) + e] = m;
+        }
+        lds_wave_sync();
+        if (l64 < cnt)
+            put_score(l, e0 + l64);
+    };
+
+    // levels 0 .. NC of the scores: lane e of a run stages entry e of each
+    // level (the maxima over the run's windows, in registers)
+    {
+        float m[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            m[r] = s[r];
+        int cnt = R;
+#pragma unroll
+        for (int l = 0; l <= NC; ++l) {
+            if (l > 0) {
+                cnt /= P;
+#pragma unroll
+                for (int e = 0; e < R / P; ++e)
+                    if (e < cnt) {
+                        float x = m[e * P];
+#pragma unroll
+                        for (int c = 1; c < P; ++c)
+                            x = fmaxf(x, m[e * P + c]);
+                        m[e] = x;
+                    }
+            }
+#pragma unroll
+            for (int e = 0; e < R; ++e)
+                if (e < cnt && lane == e)
+                    s_sc[sb(l) + lg * cnt + e] = m[e];
+        }
+    }
+    if (LT > NC) { // the runs' totals of level NC, one row per lane group
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
             *reinterpret_cast<float4 *>(&s_sum[t][lg][col]) = make_float4(tot[t][0], tot[t][1], tot[t][2], tot[t][3]);
             *reinterpret_cast<float4 *>(&s_sum[t][lg][col + 4]) = make_float4(tot[t][4], tot[t][5], tot[t][6], tot[t][7]);
         }
-        __syncthreads();
-        int W = NLG;
-        for (int l = NC + 1; l <= LT; ++l) {
-            W /= P;
-            const int64_t nl = a.N >> (l * LP);
-            float res[2][8];
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int task = lg + n * NLG;
-                if (task < 3 * W) {
-                    const int t = task / W, w = task - t * W;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        res[n][e] = 0.0f;
-                    for (int c = 0; c < P; ++c) {
-                        const float4 lo = *reinterpret_cast<const float4 *>(&s_sum[t][w * P + c][col]);
-                        const float4 hi = *reinterpret_cast<const float4 *>(&s_sum[t][w * P + c][col + 4]);
-                        res[n][0] += lo.x; res[n][1] += lo.y; res[n][2] += lo.z; res[n][3] += lo.w;
-                        res[n][4] += hi.x; res[n][5] += hi.y; res[n][6] += hi.z; res[n][7] += hi.w;
-                    }
-                    const int64_t i = (x0 >> (l * LP)) + w;
-                    if (i < nl)
-                        put_sum(t, l, i, res[n]);
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int task = lg + n * NLG;
-                if (task < 3 * W) {
-                    const int t = task / W, w = task - t * W;
-                    *reinterpret_cast<float4 *>(&s_sum[t][w][col]) = make_float4(res[n][0], res[n][1], res[n][2], res[n][3]);
-                    *reinterpret_cast<float4 *>(&s_sum[t][w][col + 4]) = make_float4(res[n][4], res[n][5], res[n][6], res[n][7]);
-                }
-            }
-            __syncthreads();
-        }
     }
-
-    // score maxima of levels 1..LT over the tile, then every level's scores
-    // to memory with consecutive threads on consecutive entries
-    __syncthreads();
-    int b = 0;
-    for (int l = 1; l <= LT; ++l) {
-        const int below = Sh::T >> ((l - 1) * LP), cnt = below / P;
-        for (int e = threadIdx.x; e < cnt; e += 256) {
-            float m = s_sc[b + e * P];
-#pragma unroll
-            for (int c = 1; c < P; ++c)
-                m = fmaxf(m, s_sc[b + e * P + c]);
-            s_sc[b + below + e] = m;
-        }
-        b += below;
-        __syncthreads();
+    lds_wave_sync();
+    for (int l = 0; l <= NC && l <= LT; ++l) { // this wave's entries of levels 0 .. NC
+        const int cnt = (G * R) >> (l * LP);
+        if (l64 < cnt)
+            put_score(l, wave * cnt + l64);
     }
-    b = 0;
-    for (int l = 0; l <= LT; ++l) {
-        const int cnt = Sh::T >> (l * LP);
-        const int64_t i0 = x0 >> (l * LP), nl = a.N >> (l * LP);
-        for (int e = threadIdx.x; e < cnt; e += 256) {
-            if (i0 + e < nl) {
-                sc[a.lvl_off[l] + i0 + e] = s_sc[b + e];
-                if (keep && l == LT)
-                    pmax[a.part_off[l] + i0 + e] = s_sc[b + e];
+    // levels inside a wave
+    int W = G; // windows of the level below in this wave
+    const int lw = LT < NC + WL ? LT : NC + WL;
+    for (int l = NC + 1; l <= lw; ++l) {
+        W /= P;
+        sum_level(l, W, wave * W, wave * G, wave * G, 1 << 30, gl, G);
+        score_level(l, wave * W, W);
+    }
+    // levels spanning waves: wave 0, after one barrier
+    if (LT > NC + WL) {
+        lds_barrier();
+        if (wave == 0) {
+            int cper = W; // windows per wave at the level below (rows wave * G + w)
+            int Wt = W * 4;
+            for (int l = NC + WL + 1; l <= LT; ++l) {
+                Wt /= P;
+                sum_level(l, Wt, 0, 0, 0, cper, gl, G);
+                score_level(l, 0, Wt);
+                cper = 1 << 30; // from here on in rows 0 .. Wt - 1
             }
         }
-        b += cnt;
     }
 }
 
