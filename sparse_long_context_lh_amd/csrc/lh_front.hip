@@ -66,7 +66,9 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
     float *pmax = a.part + 3 * pstride + (int64_t)h * a.part_rows;
 
     // A finished level-l window i (i < n_l, l <= LT): the pooled mean of a
-    // materialised level, and the sum itself when level LT feeds coarser ones.
+    // materialised level, and the sum itself when level LT feeds coarser ones
+    // and is not materialised (else the next level reads the means: mean *
+    // p^l is the sum, exactly, the scale being a power of two).
     auto put_sum = [&](int t, int l, int64_t i, const float (&acc)[8]) {
         if (a.mat_off[l] >= 0) {
             const float w = 1.0f / (float)(1 << (l * LP)); // exact: power of two
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
                 m8[e] = acc[e] * w;
             store8(pooled + t * a.tensor_stride + (a.mat_off[l] + i) * D, m8);
         }
-        if (keep && l == LT)
+        if (keep && l == LT && a.mat_off[l] < 0)
             store8(part + t * pstride + (a.part_off[l] + i) * D, acc);
     };
 
@@ -296,8 +298,10 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
     }
 }
 
-// Level l > LT: window i sums the p windows i*p .. i*p+p-1 of level l-1 kept
-// in the workspace (ascending, from 0), one lane group per (head, window).
+// Level l > LT: window i sums the p windows i*p .. i*p+p-1 of level l-1
+// (ascending, from 0), one lane group per (head, window). The sums of level
+// l-1 are its kept window sums, or, for a materialised level, its pooled
+// means times p^(l-1) (exact: a power of two, barring subnormal means).
 template <int D>
 __global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
 {
@@ -312,7 +316,11 @@ __global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
     const int P = 1 << a.log2p;
     const bool keep = l < a.L - 1;
     const int64_t pstride = (int64_t)a.H * a.part_rows * D;
-    const float *src = a.part + ((int64_t)h * a.part_rows + a.part_off[l - 1] + i * P) * D + col;
+    const bool from_mean = a.mat_off[l - 1] >= 0;
+    const float up = (float)(1 << ((l - 1) * a.log2p));
+    const float *src = from_mean ? a.pooled + ((int64_t)h * a.mat_rows + a.mat_off[l - 1] + i * P) * D + col
+                                 : a.part + ((int64_t)h * a.part_rows + a.part_off[l - 1] + i * P) * D + col;
+    const int64_t sstride = from_mean ? a.tensor_stride : pstride;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
         float acc[8];
@@ -321,10 +329,10 @@ __global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
             acc[e] = 0.0f;
         for (int c = 0; c < P; ++c) {
             float x[8];
-            load8(src + t * pstride + c * D, x);
+            load8(src + t * sstride + c * D, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                acc[e] += x[e];
+                acc[e] += from_mean ? x[e] * up : x[e];
         }
         if (a.mat_off[l] >= 0) {
             const float w = 1.0f / (float)(1 << (l * a.log2p)); // exact: power of two
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(256) void k_front_up(FrontArgs a, int l)
                 m8[e] = acc[e] * w;
             store8(a.pooled + t * a.tensor_stride + ((int64_t)h * a.mat_rows + a.mat_off[l] + i) * D + col, m8);
         }
-        if (keep)
+        if (keep && a.mat_off[l] < 0)
             store8(a.part + t * pstride + ((int64_t)h * a.part_rows + a.part_off[l] + i) * D + col, acc);
     }
     if (lane == 0) {

@@ -150,3 +150,11 @@ def test_zero_upstream_gradient():
     for g in run.grads:
         assert torch.count_nonzero(g).item() == 0
     assert torch.all(torch.isfinite(run.out.float()))
+
+
+def test_kept_sums_of_a_level_not_materialised():
+    # fp32, k = 1: level 3 (256 entries, the last one finished in the front
+    # pass's tiles at d = 64) is cheaper to re-average in the gather than to
+    # write, so the level above it is built from the kept window sums rather
+    # than from pooled means
+    _case(16384, 1, 64, 5, 4, 1, torch.float32, n_plant=0, bwd=True, tag="kept-sums")
