@@ -15,10 +15,12 @@
 // scores, and sums its run level by level in registers: a level-l window sum
 // is the sum of its p level-(l-1) window sums in ascending order, starting
 // from 0 (the same tree at every level, so the pooled values do not depend on
-// the tiling). Run totals meet in LDS, where the workgroup finishes the levels
-// whose windows fit its tile; each coarser level is one small kernel over the
-// window sums the previous level left in the workspace. No atomics; each
-// input byte is read once.
+// the tiling). A wave's lane groups hold consecutive runs: each wave finishes
+// the levels whose windows fit in its rows, and wave 0 those spanning the
+// workgroup's tile. Each coarser level is one small kernel over the level
+// below: its pooled means times p^l where that level is materialised, else
+// the window sums the tile kernel kept for it. No atomics; each input byte is
+// read once.
 #include "lh_device.h"
 #include "lh_internal.h"
 
