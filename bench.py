@@ -210,10 +210,12 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
                 calls[(st, r["Kernel_Name"])].add(r["Dispatch_Id"])
         if not calib:
             raise SystemExit("no calibration kernel in %s (run bench.py with --copy-calibration)" % d)
-        # launches of each stage = launches of any one of its kernels
+        # launches of each stage = launches of its least launched kernel (every
+        # kernel of a stage runs at least once per step; the per-level kernels
+        # of the front pass run several times at deep pyramids)
         n = {}
         for (st, _), ids in calls.items():
-            n[st] = max(n.get(st, 0), len(ids))
+            n[st] = min(n.get(st, len(ids)), len(ids))
         scale = CALIB_BYTES / (sum(calib) / len(calib))
         return {st: tot[st] / n[st] * scale for st in tot}, scale
 
