@@ -52,6 +52,8 @@ def test_subseq_len_golden(L):
     ((4096, 4, 64, 0, 2, 16, 0), 1),       # L < 1
     ((4096, 4, 64, 9, 2, 1, 0), 3),        # L > 8
     ((4096, 0, 64, 3, 2, 16, 0), 1),       # H < 1
+    ((0, 4, 64, 1, 0, 0, 0), 1),           # N = 0: nothing to attend
+    ((-64, 4, 64, 3, 2, 1, 0), 1),         # N < 0
     ((4096, 65536, 64, 3, 2, 16, 0), 3),   # H > 65535
     ((4096, 4, 64, 3, 2, 16, 7), 1),       # unknown dtype
     ((4096, 4, 64, 1, 0, 0, 0), 0),        # L = 1: dense causal attention, p unused

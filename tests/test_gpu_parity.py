@@ -158,3 +158,26 @@ def test_kept_sums_of_a_level_not_materialised():
     # write, so the level above it is built from the kept window sums rather
     # than from pooled means
     _case(16384, 1, 64, 5, 4, 1, torch.float32, n_plant=0, bwd=True, tag="kept-sums")
+
+
+@pytest.mark.parametrize("N,H,d,L,p,k,dtype", [
+    (4, 1, 64, 3, 2, 1, torch.float32),    # levels of 4, 2 and 1 entries; S = 1 + 2*2*1 = 5
+    (8, 2, 64, 2, 4, 2, torch.bfloat16),   # everything of level 1 selected; S = 2 + 4*2 = 10
+    (64, 1, 128, 3, 2, 3, torch.bfloat16), # one row tile, odd k
+])
+def test_tiny_pyramids(N, H, d, L, p, k, dtype):
+    # far smaller than any tile of any kernel: every load and store is a tail
+    _case(N, H, d, L, p, k, dtype, n_plant=0, bwd=True, tag="tiny")
+
+
+def test_single_token():
+    # N = 1, L = 1: the softmax has one term, so the output is the value row
+    # itself and dV = dO; dQ and dK are zero up to the rounding of dP - delta
+    N, H, d = 1, 2, 128
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 0, 17))
+    dout = make_dout(N, H, d, torch.bfloat16, 18).cuda()
+    say("case single token: N=1 H=2 d=128 L=1")
+    check_case(q, kk, v, 1, 2, 0, dout, tag="single-token")
+    run = GpuRun(q, kk, v, 1, 2, 0, dout)
+    assert torch.equal(run.out, v)
+    assert torch.equal(run.grads[2], dout)
