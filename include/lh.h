@@ -67,7 +67,7 @@
  * output. Outputs are rounded once to the input dtype.
  *
  * Supported shapes: d in {64, 128}; p in {2, 4, 8}; 1 <= L <= 8;
- * N a multiple of p^(L-1), N <= 2^27, 1 <= H <= 65535; 0 <= k <= N/p^(L-1);
+ * 1 <= N <= 2^27, N a multiple of p^(L-1); 1 <= H <= 65535; 0 <= k <= N/p^(L-1);
  * a level of more than 2048 entries must hold a multiple of 2048;
  * (L-1)*k <= 16384; S rounded up to 256, times d, at most 2^30.
  */
