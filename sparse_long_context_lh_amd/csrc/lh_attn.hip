@@ -1055,8 +1055,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     // this wave's dS tiles (qt, kt) are contiguous in kt; lane chunk = 16 B
     const uint16_t *const dsrow = a.dst + (int64_t)h * a.dst_head + (int64_t)qt * (qt + 1) / 2 * 1024;
     // a 32x32 tile is 128 chunks (32 query rows of 4): two DMA rounds, the
-    // physical chunk of (row, c) XOR-swizzled so lane reads avoid bank conflicts
-    const uint32_t doff0 = 16u * (uint32_t)((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3)));
+    // physical chunk of (row, c) is 4 row + (c ^ ((row >> 2) & 3)): the 16
+    // lanes an LDS read serves together (rows r..r+15 of one chunk column)
+    // then hit 16 distinct 16-byte bank groups
+    const uint32_t doff0 = 16u * (uint32_t)((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 4) & 3)));
     const uint32_t doff1 = doff0 + 16u * 64u;
 
     auto issue = [&](int64_t k0, const uint4 *base) {
@@ -1097,7 +1099,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
                 break;
             // dS^T operand: query c32, keys 8g.. and 16 + 8g.. of the tile
             const uint4 *dt = base + St::DS + wave * St::DSW + j * 128 + c32 * 4;
-            const int sw = (c32 >> 1) & 3;
+            const int sw = (c32 >> 2) & 3;
             const uint4 ds0 = dt[g ^ sw], ds1 = dt[(2 + g) ^ sw];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
