@@ -122,7 +122,11 @@ lh_status lh_forward(const void *q, const void *k, const void *v,
  * Backward pass with the indices of the preceding lh_forward held fixed
  * (the top-K is non-differentiable; aitrends summary, 핵심 기여): given dout =
  * dLoss/dout, writes dq, dk, dv. Needs only the context lh_forward left in ws,
- * not q, k, v themselves. Same shape arguments as that lh_forward.
+ * not q, k, v themselves. Same shape arguments as that lh_forward, queued
+ * after it (same stream, or ordered by the caller). The context is trusted,
+ * not checked: on a workspace that no completed lh_forward of this shape
+ * filled, or that was modified since, the results are undefined and the
+ * slot maps read there may address memory outside ws.
  */
 lh_status lh_backward(const void *dout,
                       int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
