@@ -32,8 +32,10 @@
  *   - causal order: by the last token an entry covers, coarser entry first
  *     on equal last tokens;
  *   - R(l, i) = tokens (i+1)p^l - 1 .. (i+2)p^l - 2, clipped at N; outputs
- *     that fall in several ranges are summed (in ascending l); a token in no
- *     range receives 0.
+ *     that fall in several ranges are summed in fp32, in a fixed order: the
+ *     levels a kernel tile shares (the coarse ones) in ascending l first, then
+ *     the finer levels from the coarsest of them down to level 0; a token in
+ *     no range receives 0.
  *
  * Conventions for every entry point:
  *   - q, k, v, out, dout, dq, dk, dv are DEVICE pointers to [H][N][d]
@@ -48,8 +50,10 @@
  *     argument returns LH_EINVAL / LH_EUNSUPPORTED / LH_EWORKSPACE and queues
  *     nothing. LH_EHIP means a launch failed; faults inside kernels surface at
  *     the caller's next synchronisation, as with any HIP call.
- *   - Results are deterministic and bitwise reproducible (no atomics on the
- *     layer's path). Calls on distinct workspaces may run concurrently.
+ *   - Results are deterministic and bitwise reproducible: no global-memory
+ *     atomics anywhere on the layer's path (the top-K's digit histograms and
+ *     two per-tile maxima use LDS integer atomics, whose results do not depend
+ *     on their order). Calls on distinct workspaces may run concurrently.
  *   - Inputs must be finite.
  *
  * Precision. Scores are fp32 in the stated order (bit-exact by design).
@@ -69,7 +73,8 @@
  * Supported shapes: d in {64, 128}; p in {2, 4, 8}; 1 <= L <= 8;
  * 1 <= N <= 2^27, N a multiple of p^(L-1); 1 <= H <= 65535; 0 <= k <= N/p^(L-1);
  * a level of more than 2048 entries must hold a multiple of 2048;
- * (L-1)*k <= 16384; S rounded up to 256, times d, at most 2^30.
+ * (L-1)*k <= 16384; S rounded up to 256, times d, at most 2^30; a
+ * workspace (lh_workspace_bytes) of at most 2^46 bytes.
  */
 #ifndef LH_H
 #define LH_H
@@ -105,14 +110,23 @@ lh_status lh_check_shape(int64_t N, int H, int d, int L, int p, int k, lh_dtype 
 int64_t lh_subseq_len(int64_t N, int L, int p, int k);
 
 /* Bytes of device workspace lh_forward + lh_backward need for this shape;
- * 0 if the shape is invalid. */
+ * 0 if the shape is invalid. The dS tiles the backward stores for its dQ
+ * kernel (the causal half of S x S per head, fp16) are planned only while
+ * they take at most 8 GiB; beyond that the dQ kernel recomputes the logits
+ * and dP, and the workspace grows as O(H S d) only. */
 size_t lh_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt);
+
+/* Bytes of workspace lh_forward alone needs (a prefix of the layout above):
+ * a caller that never runs lh_backward may pass a workspace of this size.
+ * 0 if the shape is invalid. */
+size_t lh_forward_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt);
 
 /*
  * Forward pass: out = Lighthouse(q, k, v). Steps 1-4 above.
  * Leaves in ws the context lh_backward needs (scores, selection, slot maps,
  * gathered rows, sub-sequence output and log-sum-exp); the caller must not
  * modify ws between lh_forward and lh_backward of the same inputs.
+ * ws_bytes >= lh_forward_workspace_bytes() suffices for the forward itself.
  */
 lh_status lh_forward(const void *q, const void *k, const void *v,
                      int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
@@ -123,10 +137,18 @@ lh_status lh_forward(const void *q, const void *k, const void *v,
  * (the top-K is non-differentiable; aitrends summary, 핵심 기여): given dout =
  * dLoss/dout, writes dq, dk, dv. Needs only the context lh_forward left in ws,
  * not q, k, v themselves. Same shape arguments as that lh_forward, queued
- * after it (same stream, or ordered by the caller). The context is trusted,
- * not checked: on a workspace that no completed lh_forward of this shape
- * filled, or that was modified since, the results are undefined and the
- * slot maps read there may address memory outside ws.
+ * after it (same stream, or ordered by the caller); ws_bytes >=
+ * lh_workspace_bytes(). The context is trusted, not checked: on a workspace
+ * that no completed lh_forward of this shape filled, or that was modified
+ * since, dq, dk and dv hold unspecified values (possibly non-finite). Memory
+ * accesses still stay inside ws, dout, dq, dk and dv: every slot-map entry is
+ * bounds-checked against S_pad before it addresses a sub-sequence row, and
+ * no other value read from ws is used as an address.
+ *
+ * Departure from the argument list (q, k, v, N, H, d, L, p, k, ...) of the
+ * layer's plain call: q, k and v are not passed, because every quantity the
+ * gradients need (gathered rows, selection, slot maps, O_sub, log-sum-exp) is
+ * part of the context above; passing them again would be an unused argument.
  */
 lh_status lh_backward(const void *dout,
                       int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
@@ -153,7 +175,7 @@ lh_status lh_backward_timed(const void *dout,
  * lh_forward / lh_backward leave there. Layouts (per head h, heads outermost):
  *   LH_R_SCORES  fp32  [H][sum_l n_l]  level-0 scores, then level 1, ... (n_l = N/p^l);
  *                                      written when L > 1
- *   LH_R_SEL     int32 [H][L-1][k]     selected parents of levels 1..L-1, ascending
+ *   LH_R_SEL     int32 [L-1][H][k]     selected parents of levels 1..L-1, ascending
  *   LH_R_SLOT    int32 [H][sum_l n_l]  sub-sequence position of entry (l, i), or -1
  *   LH_R_ENT     int32 [H][S_pad]      entry at each position: (i << 3) | l; -1 past S
  *   LH_R_QHI/QLO fp16  [H][S_pad][d]   gathered query rows as an fp16 pair: hi =
@@ -180,6 +202,22 @@ typedef enum {
 lh_status lh_region_info(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt,
                          lh_region region, size_t *offset, size_t *bytes);
 int64_t lh_padded_subseq_len(int64_t N, int L, int p, int k);
+
+/*
+ * Test hook for the stratified top-K (techllm review, 한계와 주의할 점: every
+ * segment contributes a fixed number of entries; aitrends summary, 핵심 기여:
+ * the selection is a non-differentiable top-K): sets *sel_dev to the DEVICE
+ * address, inside ws, of the selection lh_forward made at pyramid level
+ * `level` (1 <= level <= L-1): an int32 [H][k_sel] array, row h holding head
+ * h's k_sel selected parents in ascending order (entries i of level `level`,
+ * whose p children at level-1 were gathered). Valid once that lh_forward has
+ * completed; the memory belongs to ws. Queues nothing and reads no device
+ * memory. The address does not depend on the input type. Returns LH_EINVAL
+ * (and sets *sel_dev to NULL when sel_dev is not NULL) for a bad shape, a
+ * NULL or misaligned ws, L < 2 or a level outside 1..L-1.
+ */
+lh_status lh_selection(const void *ws, int64_t N, int H, int d, int L, int p, int k_sel, int level,
+                       const int32_t **sel_dev);
 
 /*
  * Test hook for the score's square root: for every fp32 bit pattern b in

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         "lh_subseq_len": (i64, [i64, i32, i32, i32]),
         "lh_padded_subseq_len": (i64, [i64, i32, i32, i32]),
         "lh_workspace_bytes": (sz, shape),
+        "lh_forward_workspace_bytes": (sz, shape),
+        "lh_selection": (i32, [vp, i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(vp)]),
         "lh_forward": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp]),
         "lh_backward": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp]),
         "lh_forward_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
@@ -101,12 +103,17 @@ def workspace_bytes(N, H, d, L, p, k, dtype) -> int:
     return lib().lh_workspace_bytes(N, H, d, L, p, k, _dt(dtype))
 
 
+def forward_workspace_bytes(N, H, d, L, p, k, dtype) -> int:
+    return lib().lh_forward_workspace_bytes(N, H, d, L, p, k, _dt(dtype))
+
+
 def check_shape(N, H, d, L, p, k, dtype) -> int:
     return lib().lh_check_shape(N, H, d, L, p, k, _dt(dtype))
 
 
-def alloc_workspace(N, H, d, L, p, k, dtype, device="cuda") -> torch.Tensor:
-    n = workspace_bytes(N, H, d, L, p, k, dtype)
+def alloc_workspace(N, H, d, L, p, k, dtype, device="cuda", forward_only=False) -> torch.Tensor:
+    """A workspace for lh_forward + lh_backward (forward_only: lh_forward alone)."""
+    n = (forward_workspace_bytes if forward_only else workspace_bytes)(N, H, d, L, p, k, dtype)
     if n == 0:
         _check(check_shape(N, H, d, L, p, k, dtype), "workspace size")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -119,6 +126,18 @@ def _shape_of(x: torch.Tensor):
     return N, H, d
 
 
+def _like(t: torch.Tensor, ref: torch.Tensor, what: str) -> None:
+    """A caller-supplied output must match ref in shape, dtype and device and be contiguous."""
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (what, ref.dtype, tuple(ref.shape),
+                                                                                ref.device))
+
+
+def _check_ws(ws: torch.Tensor, ref: torch.Tensor) -> None:
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or ws.device != ref.device:
+        raise ValueError("ws must be a contiguous 1-D uint8 tensor on %s" % ref.device)
+
+
 def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
             out: torch.Tensor | None = None, stream=None, events=None):
     """Lighthouse forward on [H, N, d] tensors; returns (out, ws)."""
@@ -129,8 +148,10 @@ def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
     dt = _dt(q.dtype)
     if ws is None:
         ws = alloc_workspace(N, H, d, L, p, k_sel, q.dtype, q.device)
+    _check_ws(ws, q)
     if out is None:
         out = torch.empty_like(q)
+    _like(out, q, "out")
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, dt,
             out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
     if events is None:
@@ -148,6 +169,9 @@ def backward(dout, L: int, p: int, k_sel: int, ws: torch.Tensor, dq=None, dk=Non
     dq = torch.empty_like(dout) if dq is None else dq
     dk = torch.empty_like(dout) if dk is None else dk
     dv = torch.empty_like(dout) if dv is None else dv
+    for t, what in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _like(t, dout, what)
+    _check_ws(ws, dout)
     args = (dout.data_ptr(), N, H, d, L, p, k_sel, dt, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             ws.data_ptr(), ws.numel(), _stream(stream))
     if events is None:
@@ -163,6 +187,15 @@ def region(ws: torch.Tensor, name: str, N, H, d, L, p, k, dtype) -> torch.Tensor
     _check(lib().lh_region_info(N, H, d, L, p, k, _dt(dtype), REGIONS.index(name),
                                 ctypes.byref(off), ctypes.byref(nbytes)), "lh_region_info")
     return ws[off.value:off.value + nbytes.value].view(_REGION_DTYPE[name])
+
+
+def selection(ws: torch.Tensor, N, H, d, L, p, k, level: int) -> torch.Tensor:
+    """The [H, k] selection of pyramid level `level` (1..L-1) that the last
+    lh_forward on ws made, as a view of ws (lh_selection gives its address)."""
+    ptr = ctypes.c_void_p()
+    _check(lib().lh_selection(ws.data_ptr(), N, H, d, L, p, k, level, ctypes.byref(ptr)), "lh_selection")
+    off = (ptr.value or 0) - ws.data_ptr()
+    return ws[off:off + 4 * H * k].view(torch.int32).view(H, k)
 
 
 def stage_names(backward: bool) -> list[str]:

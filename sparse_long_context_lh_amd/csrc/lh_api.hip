@@ -18,17 +18,13 @@ static int ilog2_exact(int p)
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, Plan *pl)
+// The parts of a plan that depend on N, L, p and k alone: level sizes,
+// strata, S and S_pad. Checks the rules of the method on these four.
+static lh_status plan_sizes(int64_t N, int L, int p, int k, Plan *pl)
 {
     memset(pl, 0, sizeof(*pl));
-    if (N < 1 || H < 1 || L < 1 || k < 0)
+    if (N < 1 || L < 1 || k < 0)
         return LH_EINVAL;
-    if (dt != LH_BF16 && dt != LH_F32)
-        return LH_EINVAL;
-    if (d < 16 || d % 16 != 0)
-        return LH_EINVAL;
-    if (d != 64 && d != 128)
-        return LH_EUNSUPPORTED;
     if (L > kMaxLevels)
         return LH_EUNSUPPORTED;
     int log2p = 1;
@@ -41,13 +37,12 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
         if ((L - 1) * log2p > 27)
             return LH_EUNSUPPORTED;
     }
-    if (N > kMaxN || H > kMaxHeads)
+    if (N > kMaxN)
         return LH_EUNSUPPORTED;
     const int top_shift = (L - 1) * log2p;
     if (L > 1 && (N & ((int64_t(1) << top_shift) - 1)) != 0)
         return LH_EINVAL; // N must be a multiple of p^(L-1)
-    pl->N = N; pl->H = H; pl->d = d; pl->L = L; pl->p = L > 1 ? p : 2; pl->log2p = log2p; pl->k = L > 1 ? k : 0;
-    pl->dt = dt;
+    pl->N = N; pl->L = L; pl->p = L > 1 ? p : 2; pl->log2p = log2p; pl->k = L > 1 ? k : 0;
     int64_t tot = 0;
     for (int l = 0; l < L; ++l) {
         pl->n[l] = N >> (l * log2p);
@@ -67,11 +62,32 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
         if ((int64_t)(L - 1) * k > kMaxSelTotal)
             return LH_EUNSUPPORTED;
     }
-    const int64_t pk = (int64_t)pl->p * pl->k;
-    pl->S = pl->n[L - 1] + (int64_t)(L - 1) * pk;
+    pl->S = pl->n[L - 1] + (int64_t)(L - 1) * pl->p * pl->k;
     pl->S_pad = (int64_t)round_up((size_t)pl->S, kSubseqAlign);
+    return LH_OK;
+}
+
+lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, Plan *pl)
+{
+    lh_status st = plan_sizes(N, L, p, k, pl);
+    if (st != LH_OK)
+        return st;
+    if (H < 1)
+        return LH_EINVAL;
+    if (dt != LH_BF16 && dt != LH_F32)
+        return LH_EINVAL;
+    if (d < 16 || d % 16 != 0)
+        return LH_EINVAL;
+    if (d != 64 && d != 128)
+        return LH_EUNSUPPORTED;
+    if (H > kMaxHeads)
+        return LH_EUNSUPPORTED;
+    pl->H = H; pl->d = d; pl->dt = dt;
     if (pl->S_pad * d > (int64_t(1) << 30))
         return LH_EUNSUPPORTED; // attention kernels address a head's sub-sequence with 32-bit offsets
+    const int log2p = pl->log2p;
+    const int64_t tot = pl->lvl_total;
+    const int64_t pk = (int64_t)pl->p * pl->k;
 
     // Pooled levels the front pass writes (fp32 rows): the top level (gathered
     // whole) and every middle level whose full write plus the gathered reads
@@ -119,7 +135,13 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
         }
     }
 
+    // Region sizes. With H <= 2^16, S_pad * d <= 2^30 and N <= 2^27 every
+    // product below stays under 2^50; the dS tiles are the one quadratic term
+    // and are planned only up to kDsTileBudget bytes (above it the dQ kernel
+    // recomputes S and dP instead of reading them).
     const size_t Hs = (size_t)H, Sp = (size_t)pl->S_pad, D = (size_t)d;
+    const size_t ds_bytes = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
+    pl->ds_tiles = ds_bytes <= kDsTileBudget;
     size_t b[IR_COUNT];
     b[LH_R_SCORES] = 4 * Hs * (size_t)tot;
     b[LH_R_SEL] = 4 * Hs * (size_t)(L - 1) * (size_t)pl->k;
@@ -135,19 +157,37 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
     b[IR_LSE15] = 4 * Hs * Sp;
-    b[IR_DST] = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
+    b[IR_DST] = pl->ds_tiles ? ds_bytes : 0;
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
     b[IR_QLO8] = b[IR_K8] = b[IR_V8] = b[IR_DOLO8] = Hs * Sp * D;
     b[IR_TMAX] = 4 * 4 * Hs * (Sp / 32);
     b[IR_SC8] = 4 * 4 * Hs;
+    // What lh_forward writes comes first (the context the backward reads and
+    // the forward's own scratch), so a forward-only caller can pass a
+    // workspace that ends there; the regions only lh_backward writes follow.
+    static const int kFwdOrder[] = {LH_R_SCORES, LH_R_SEL, LH_R_SLOT, LH_R_ENT, LH_R_QHI, LH_R_QLO, LH_R_KHI,
+                                    LH_R_KLO, LH_R_V, LH_R_QHI_T, LH_R_KHI_T, LH_R_V_T, LH_R_OSUB, LH_R_LSE,
+                                    IR_TMAX, IR_SC8, IR_QLO8, IR_K8, IR_POOLED, IR_FPART};
+    static const int kBwdOrder[] = {LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, IR_DOHI, IR_DOLO, IR_DOHI_T,
+                                    IR_DELTA, IR_LSE15, IR_SPART, IR_V8, IR_DOLO8, IR_DST};
+    static_assert(sizeof(kFwdOrder) / sizeof(int) + sizeof(kBwdOrder) / sizeof(int) == IR_COUNT,
+                  "every region placed once");
     size_t off = 0;
-    for (int r = 0; r < IR_COUNT; ++r) {
+    for (int r : kFwdOrder) {
+        pl->off[r] = off;
+        pl->bytes[r] = b[r];
+        off = round_up(off + b[r], 256);
+    }
+    pl->fwd_total = off;
+    for (int r : kBwdOrder) {
         pl->off[r] = off;
         pl->bytes[r] = b[r];
         off = round_up(off + b[r], 256);
     }
     pl->total = off;
+    if (pl->total > kMaxWorkspace)
+        return LH_EUNSUPPORTED;
     return LH_OK;
 }
 
@@ -158,9 +198,9 @@ template <typename Tp> static Tp *at(void *ws, const Plan &pl, int r)
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-static lh_status check_ws(const Plan &pl, void *ws, size_t ws_bytes)
+static lh_status check_ws(void *ws, size_t ws_bytes, size_t need)
 {
-    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < pl.total)
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < need)
         return LH_EWORKSPACE;
     return LH_OK;
 }
@@ -184,7 +224,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         return st;
     if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LH_EINVAL;
-    if ((st = check_ws(pl, ws, ws_bytes)) != LH_OK)
+    if ((st = check_ws(ws, ws_bytes, pl.fwd_total)) != LH_OK)
         return st;
 
     float *scores = at<float>(ws, pl, LH_R_SCORES);
@@ -328,8 +368,10 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         return st;
     if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return LH_EINVAL;
-    if ((st = check_ws(pl, ws, ws_bytes)) != LH_OK)
+    if ((st = check_ws(ws, ws_bytes, pl.total)) != LH_OK)
         return st;
+    if (!pl.ds_tiles)
+        return LH_EUNSUPPORTED; // the dQ kernel that recomputes S and dP is not built yet
     int32_t *slot = at<int32_t>(ws, pl, LH_R_SLOT);
     float *dosub = at<float>(ws, pl, LH_R_DOSUB);
 
@@ -459,7 +501,7 @@ lh_status lh_check_shape(int64_t N, int H, int d, int L, int p, int k, lh_dtype 
 int64_t lh_subseq_len(int64_t N, int L, int p, int k)
 {
     Plan pl;
-    if (make_plan(N, 1, 128, L, p, k, LH_BF16, &pl) != LH_OK)
+    if (plan_sizes(N, L, p, k, &pl) != LH_OK)
         return -1;
     return pl.S;
 }
@@ -467,7 +509,7 @@ int64_t lh_subseq_len(int64_t N, int L, int p, int k)
 int64_t lh_padded_subseq_len(int64_t N, int L, int p, int k)
 {
     Plan pl;
-    if (make_plan(N, 1, 128, L, p, k, LH_BF16, &pl) != LH_OK)
+    if (plan_sizes(N, L, p, k, &pl) != LH_OK)
         return -1;
     return pl.S_pad;
 }
@@ -478,6 +520,33 @@ size_t lh_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype
     if (make_plan(N, H, d, L, p, k, dt, &pl) != LH_OK)
         return 0;
     return pl.total;
+}
+
+size_t lh_forward_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt)
+{
+    Plan pl;
+    if (make_plan(N, H, d, L, p, k, dt, &pl) != LH_OK)
+        return 0;
+    return pl.fwd_total;
+}
+
+lh_status lh_selection(const void *ws, int64_t N, int H, int d, int L, int p, int k_sel, int level,
+                       const int32_t **sel_dev)
+{
+    if (!sel_dev)
+        return LH_EINVAL;
+    *sel_dev = nullptr;
+    Plan pl;
+    // the selection's place depends on N, H, L, p and k only (the first two
+    // regions): it is the same for either input type
+    lh_status st = make_plan(N, H, d, L, p, k_sel, LH_BF16, &pl);
+    if (st != LH_OK)
+        return st;
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || L < 2 || level < 1 || level > L - 1)
+        return LH_EINVAL;
+    *sel_dev = reinterpret_cast<const int32_t *>(static_cast<const char *>(ws) + pl.off[LH_R_SEL]) +
+               (int64_t)(level - 1) * H * pl.k;
+    return LH_OK;
 }
 
 lh_status lh_region_info(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, lh_region region,

@@ -17,6 +17,13 @@ constexpr int kMaxSelTotal = 16384; // (L-1)*k held in LDS by the index kernel
 constexpr int kSubseqAlign = 256;   // S is padded to this for the attention tiles
 constexpr int64_t kMaxN = int64_t(1) << 27;
 constexpr int kMaxHeads = 65535; // heads run along the grid's y dimension
+// Largest workspace share of the backward's stored dS tiles (the causal half
+// of S x S per head, fp16). Above it the dQ kernel recomputes S and dP from
+// the gathered rows instead, and the workspace stays O(S d).
+constexpr size_t kDsTileBudget = size_t(8) << 30;
+// Largest workspace a plan may ask for (64 TiB): shapes beyond it are reported
+// as unsupported rather than sized.
+constexpr size_t kMaxWorkspace = size_t(1) << 46;
 
 // Extra workspace regions that are not exposed through lh_region.
 enum InternalRegion {
@@ -78,7 +85,9 @@ struct Plan {
     int64_t spart_n[kMaxLevels];   // u-space windows of level l kept in IR_SPART (l >= LT)
     int64_t spart_off[kMaxLevels];
     int64_t spart_rows;
+    bool ds_tiles;               // the dK/dV kernel stores dS tiles for the dQ kernel (else dQ recomputes)
     size_t off[IR_COUNT], bytes[IR_COUNT];
+    size_t fwd_total;            // end of the regions lh_forward writes
     size_t total;
 };
 
@@ -108,7 +117,7 @@ struct FrontArgs {
 
 struct TopkArgs {
     const float *scores; // [H][lvl_total]
-    int32_t *sel;        // [H][L-1][k]
+    int32_t *sel;        // [L-1][H][k]
     int32_t *slot;       // [H][lvl_total]
     int64_t lvl_total;
     int64_t lvl_off[kMaxLevels];
@@ -119,7 +128,7 @@ struct TopkArgs {
 };
 
 struct IndexArgs {
-    const int32_t *sel;  // [H][L-1][k]
+    const int32_t *sel;  // [L-1][H][k]
     int32_t *slot;       // [H][lvl_total]
     int32_t *ent;        // [H][S_pad]
     int64_t lvl_total, S, S_pad;

@@ -116,7 +116,8 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
     // Ballot compaction in ascending index order, 1024 entries per pass: an
     // entry is kept if its score is above T, or equal to T with fewer than r
     // equal ones before it.
-    int32_t *sel = a.sel + ((int64_t)h * (a.L - 1) + (l - 1)) * a.k + (int64_t)c * (a.k / C) + min(c, a.k % C);
+    // selections are stored level-major, [L-1][H][k]
+    int32_t *sel = a.sel + ((int64_t)(l - 1) * gridDim.y + h) * a.k + (int64_t)c * (a.k / C) + min(c, a.k % C);
     int32_t *child_slot = a.slot + (int64_t)h * a.lvl_total + a.lvl_off[l - 1];
     const int p = 1 << a.log2p;
     int done = 0, tied = 0;
@@ -174,8 +175,10 @@ __global__ __launch_bounds__(256) void k_index(IndexArgs a)
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
     const int nsel = (a.L - 1) * a.k;
-    for (int e = tid; e < nsel; e += 256)
-        s_sel[e] = a.sel[(int64_t)h * nsel + e];
+    for (int e = tid; e < nsel; e += 256) { // level row r = e / k of the [L-1][H][k] selections
+        const int r = e / a.k;
+        s_sel[e] = a.sel[((int64_t)r * gridDim.y + h) * a.k + (e - r * a.k)];
+    }
     __syncthreads();
 
     const int L = a.L, k = a.k, log2p = a.log2p;

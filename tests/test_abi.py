@@ -67,6 +67,7 @@ def test_shape_validation(L, args, code):
 def test_forward_rejects_before_any_device_call(L):
     shape = (4096, 4, 64, 3, 2, 256, 0)
     need = L.lh_workspace_bytes(*shape)
+    need_fwd = L.lh_forward_workspace_bytes(*shape)
     fake = 1 << 40  # never dereferenced: validation fails first
     # bad shape
     assert L.lh_forward(fake, fake, fake, 4098, 4, 64, 3, 2, 256, 0, fake, fake, need, None) == 1
@@ -75,7 +76,7 @@ def test_forward_rejects_before_any_device_call(L):
     # misaligned output pointer
     assert L.lh_forward(fake, fake, fake, *shape, fake + 2, fake, need, None) == 1
     # workspace too small, null, misaligned
-    assert L.lh_forward(fake, fake, fake, *shape, fake, fake, need - 1, None) == 2
+    assert L.lh_forward(fake, fake, fake, *shape, fake, fake, need_fwd - 1, None) == 2
     assert L.lh_forward(fake, fake, fake, *shape, fake, None, need, None) == 2
     assert L.lh_forward(fake, fake, fake, *shape, fake, fake + 16, need, None) == 2
     # backward: same checks
@@ -106,3 +107,69 @@ def test_stage_names(L):
     from sparse_long_context_lh_amd import binding
     assert binding.stage_names(False) == ["front", "topk", "index", "gather", "attn_fwd", "scatter"]
     assert binding.stage_names(True) == ["scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "pool_bwd"]
+
+
+def test_size_helpers_do_not_depend_on_head_size(L):
+    # S and S_pad need N, L, p and k only: N = 2^24 at L = 1 is a valid
+    # d = 64 shape (S_pad * d = 2^30) even though d = 128 would exceed 2^30
+    assert L.lh_subseq_len(1 << 24, 1, 2, 0) == 1 << 24
+    assert L.lh_padded_subseq_len(1 << 24, 1, 2, 0) == 1 << 24
+    assert L.lh_check_shape(1 << 24, 1, 64, 1, 2, 0, 0) == 0
+    assert L.lh_check_shape(1 << 24, 1, 128, 1, 2, 0, 0) == 3
+    assert L.lh_subseq_len(4098, 3, 2, 1) == -1
+
+
+def test_huge_workspace_is_unsupported_not_wrapped(L):
+    # 65535 heads of 2^24 tokens would need petabytes: reported, never wrapped
+    assert L.lh_workspace_bytes(1 << 24, 65535, 64, 1, 2, 0, 0) == 0
+    assert L.lh_check_shape(1 << 24, 65535, 64, 1, 2, 0, 0) == 3
+
+
+def _region(L, shape, r):
+    import ctypes
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.lh_region_info(*shape, r, ctypes.byref(off), ctypes.byref(nb)) == 0
+    return off.value, nb.value
+
+
+def test_forward_workspace_is_a_prefix(L):
+    from sparse_long_context_lh_amd.binding import REGIONS
+    for shape in [(65536, 16, 128, 3, 2, 1536, 0), (524288, 16, 128, 5, 4, 512, 0), (4096, 4, 64, 3, 2, 256, 1),
+                  (1000, 2, 64, 1, 2, 0, 0)]:
+        fwd, tot = L.lh_forward_workspace_bytes(*shape), L.lh_workspace_bytes(*shape)
+        assert 0 < fwd < tot
+        for name in REGIONS:
+            off, nb = _region(L, shape, REGIONS.index(name))
+            if name in ("dosub", "dqsub", "dksub", "dvsub"):   # written by lh_backward only
+                assert off >= fwd
+            else:                                               # lh_forward's context
+                assert off + nb <= fwd
+    shape = (4096, 4, 64, 3, 2, 256, 0)
+    fwd, tot = L.lh_forward_workspace_bytes(*shape), L.lh_workspace_bytes(*shape)
+    fake = 1 << 40  # never dereferenced: validation fails first
+    assert L.lh_forward(fake, fake, fake, *shape, fake, fake, fwd - 1, None) == 2
+    assert L.lh_backward(fake, *shape, fake, fake, fake, fake, fwd, None) == 2
+    assert L.lh_backward(fake, *shape, fake, fake, fake, fake, tot - 1, None) == 2
+
+
+def test_selection_hook_addresses(L):
+    import ctypes
+    from sparse_long_context_lh_amd.binding import REGIONS
+    N, H, d, Lv, p, k = 524288, 16, 128, 5, 4, 512
+    ws = 1 << 40  # an address only: lh_selection reads no memory
+    off, nb = _region(L, (N, H, d, Lv, p, k, 0), REGIONS.index("sel"))
+    assert nb == 4 * H * (Lv - 1) * k
+    ptr = ctypes.c_void_p()
+    for level in range(1, Lv):
+        for dt in (0, 1):  # same place for either input type
+            assert _region(L, (N, H, d, Lv, p, k, dt), REGIONS.index("sel"))[0] == off
+        assert L.lh_selection(ws, N, H, d, Lv, p, k, level, ctypes.byref(ptr)) == 0
+        assert ptr.value == ws + off + 4 * (level - 1) * H * k
+    for bad_level in (0, Lv, -1):
+        assert L.lh_selection(ws, N, H, d, Lv, p, k, bad_level, ctypes.byref(ptr)) == 1
+        assert ptr.value is None
+    assert L.lh_selection(ws, N, H, d, Lv, p, k, 1, None) == 1
+    assert L.lh_selection(ws + 16, N, H, d, Lv, p, k, 1, ctypes.byref(ptr)) == 1   # misaligned ws
+    assert L.lh_selection(None, N, H, d, Lv, p, k, 1, ctypes.byref(ptr)) == 1
+    assert L.lh_selection(ws, 4096, 2, 64, 1, 2, 0, 1, ctypes.byref(ptr)) == 1     # L = 1: nothing selected
+    assert L.lh_selection(ws, 4098, 2, 64, 3, 2, 4, 1, ctypes.byref(ptr)) == 1     # bad shape

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from parity import GpuRun, compare_backward, compare_forward, compare_selection, head_inputs, say
+from parity import Failures, GpuRun, compare_backward, compare_forward, compare_selection, fmt_stats, head_inputs, say
 from synth_inputs import WORKLOADS, make_dout, make_qkv
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -32,9 +32,12 @@ def test_full_size_workload(w):
     say("  selection of all %d heads bit-exact" % w.H)
     h = w.H // 2  # one sampled head, full numerics
     ref = oracle.forward(head_inputs(q, h), head_inputs(k, h), head_inputs(v, h), w.L, w.p, w.k)
-    stats = compare_forward(run, h, ref, w.name)
+    fails = Failures()
+    stats = compare_forward(run, h, ref, w.name, fails)
     if w.backward:
         gref = oracle.backward(ref, head_inputs(dout, h), w.p)
-        stats.update(compare_backward(run, h, ref, gref, w.name))
-    say("  head %d: %s" % (h, {n: "%.2g/%.2g" % s for n, s in stats.items()}))
+        stats.update(compare_backward(run, h, ref, gref, w.name, fails))
+    for n, st in stats.items():
+        say("  head %d %s: %s" % (h, n, fmt_stats(st)))
+    fails.raise_if_any()
     assert np.all(np.isfinite(run.out.float().cpu().numpy()))

@@ -181,3 +181,27 @@ def test_single_token():
     run = GpuRun(q, kk, v, 1, 2, 0, dout)
     assert torch.equal(run.out, v)
     assert torch.equal(run.grads[2], dout)
+
+
+def test_selection_hook_and_forward_only_workspace():
+    # lh_selection points at the selection lh_forward made (level by level,
+    # [H, k], equal to the oracle's); a forward given only the forward's
+    # prefix of the workspace writes the same output bit for bit
+    N, H, d, L, p, k = 32768, 2, 128, 4, 4, 40
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 8, 21))
+    say("case selection hook: N=%d H=%d d=%d L=%d p=%d k=%d" % (N, H, d, L, p, k))
+    full = GpuRun(q, kk, v, L, p, k)
+    ws_fwd = lh.alloc_workspace(N, H, d, L, p, k, torch.bfloat16, forward_only=True)
+    assert ws_fwd.numel() == lh.forward_workspace_bytes(N, H, d, L, p, k, torch.bfloat16)
+    assert ws_fwd.numel() < full.ws.numel()
+    out2, _ = lh.forward(q, kk, v, L, p, k, ws=ws_fwd)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, full.out)
+    for h in range(H):
+        ref = oracle.forward(q[h].float().cpu().numpy(), kk[h].float().cpu().numpy(), v[h].float().cpu().numpy(),
+                             L, p, k)
+        for l in range(1, L):
+            a = lh.selection(full.ws, N, H, d, L, p, k, l)[h].cpu().numpy()
+            b = lh.selection(ws_fwd, N, H, d, L, p, k, l)[h].cpu().numpy()
+            assert np.array_equal(a, ref["sel"][l]) and np.array_equal(b, ref["sel"][l])
+            assert np.array_equal(a, full.head("sel", h)[l - 1].numpy())

@@ -40,6 +40,24 @@ def test_subseq_len_golden():
         assert np.array_equal(G[L - 1], np.arange(n[L - 1]))  # top level kept whole
 
 
+def test_expand_children_bruteforce():
+    # G_l for l < L-1 is every entry of level l whose parent floor(i/p) was
+    # selected at level l+1, found by scanning all of level l; the top level
+    # is gathered whole. Random selections at several shapes, so a wrong
+    # child map of the right size (p*j + c permuted, j*p^2, c*p + j, ...) fails.
+    rng = np.random.default_rng(31)
+    for N, L, p, k in [(256, 4, 2, 7), (1024, 3, 4, 16), (4096, 2, 8, 64), (512, 5, 2, 3), (64, 2, 4, 16)]:
+        n = oracle.level_sizes(N, L, p)
+        sel = {l: np.sort(rng.choice(n[l], size=k, replace=False)) for l in range(1, L)}
+        G = oracle.expand(sel, N, L, p)
+        for l in range(L - 1):
+            chosen = set(sel[l + 1].tolist())
+            want = [i for i in range(n[l]) if i // p in chosen]
+            assert sorted(G[l].tolist()) == want, (N, L, p, k, l)
+            assert len(set(G[l].tolist())) == G[l].shape[0]      # no entry twice
+        assert G[L - 1].tolist() == list(range(n[L - 1]))
+
+
 @pytest.mark.parametrize("N,L,p,k", [(4096, 3, 2, 256), (8192, 4, 2, 100), (16384, 3, 4, 300),
                                      (2048 * 4 * 3, 2, 4, 1000), (512, 1, 2, 0), (1024, 3, 2, 0)])
 def test_selection_counts(N, L, p, k):
