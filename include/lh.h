@@ -155,6 +155,27 @@ lh_status lh_backward(const void *dout,
                       void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * lh_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The same work as lh_forward, writing the same out;
+ * its workspace is a static device array of lh_static_scratch_bytes() bytes
+ * (64 MiB) inside the library, one per GPU, held until the process ends.
+ * Allocates nothing and calls no allocating routine; the first call on a
+ * device looks up that device's array (the device that `stream` belongs to
+ * must be current). A shape whose lh_forward_workspace_bytes() exceeds the
+ * array returns LH_EWORKSPACE before anything is queued. Every call on a GPU
+ * uses that GPU's one array, and the forward writes every part of it that it
+ * reads before reading it (no part must start at zero): calls that overlap
+ * in time on one GPU (two streams, two threads) race and give undefined
+ * results; calls ordered on one stream do not. The array keeps the last
+ * call's context, but lh_backward cannot use it (it takes a workspace).
+ */
+lh_status lh_forward_static(const void *q, const void *k, const void *v,
+                            int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
+                            void *out, void *stream);
+size_t lh_static_scratch_bytes(void);
+
+/*
  * Timed variants: identical work, and in addition record hipEvent_t handles
  * events[0] before the first kernel and events[i+1] after stage i, on the
  * same stream. `events` holds lh_stage_count(backward)+1 caller-created

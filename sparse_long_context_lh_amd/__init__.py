@@ -9,5 +9,5 @@ causal-safe shifted range. ``forward`` / ``backward`` call liblh.so; see
 include/lh.h for the ABI.
 """
 from .binding import (LighthouseError, alloc_workspace, backward, check_shape, forward,  # noqa: F401
-                      forward_workspace_bytes, lib, padded_subseq_len, region, selection, selftest_sqrt,
-                      stage_names, subseq_len, workspace_bytes)
+                      forward_static, forward_workspace_bytes, lib, padded_subseq_len, region, selection, selftest_sqrt,
+                      stage_names, static_scratch_bytes, subseq_len, workspace_bytes)

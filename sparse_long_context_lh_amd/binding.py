@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         "lh_forward": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp]),
         "lh_backward": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp]),
         "lh_forward_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
+        "lh_forward_static": (i32, [vp, vp, vp] + shape + [vp, vp]),
+        "lh_static_scratch_bytes": (sz, []),
         "lh_backward_timed": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp, vp]),
         "lh_stage_count": (i32, [i32]),
         "lh_stage_name": (ctypes.c_char_p, [i32, i32]),
@@ -159,6 +161,25 @@ def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
     else:
         _check(lib().lh_forward_timed(*args, events), "lh_forward_timed")
     return out, ws
+
+
+def forward_static(q, k, v, L: int, p: int, k_sel: int, out: torch.Tensor | None = None, stream=None):
+    """Lighthouse forward that uses the library's static device scratch as its
+    workspace (no allocation inside the call); returns out."""
+    N, H, d = _shape_of(q)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    _like(out, q, "out")
+    _check(lib().lh_forward_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, _dt(q.dtype),
+                                   out.data_ptr(), _stream(stream)), "lh_forward_static")
+    return out
+
+
+def static_scratch_bytes() -> int:
+    return lib().lh_static_scratch_bytes()
 
 
 def backward(dout, L: int, p: int, k_sel: int, ws: torch.Tensor, dq=None, dk=None, dv=None,

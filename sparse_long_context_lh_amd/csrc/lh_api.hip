@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lh_internal.h"
 
 namespace lh {
@@ -474,6 +476,37 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     return LH_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// Workspace of lh_forward_static: a file-scope device array. Every GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address reaches the kernels.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices]; // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device; the device must be current, as for any launch).
+static lh_status scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return LH_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return LH_EHIP;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return LH_OK;
+}
+
 } // namespace lh
 
 using namespace lh;
@@ -577,6 +610,28 @@ lh_status lh_forward(const void *q, const void *k, const void *v, int64_t N, int
 {
     return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
+
+lh_status lh_forward_static(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
+                            int k_sel, lh_dtype dt, void *out, void *stream)
+{
+    // shape, pointers and the scratch size first: nothing touches the device
+    // before the call is known to fit
+    Plan pl;
+    lh_status st = make_plan(N, H, d, L, p, k_sel, dt, &pl);
+    if (st != LH_OK)
+        return st;
+    if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LH_EINVAL;
+    if (pl.fwd_total > kStaticScratchBytes)
+        return LH_EWORKSPACE;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != LH_OK)
+        return st;
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, kStaticScratchBytes, (hipStream_t)stream,
+                        nullptr);
+}
+
+size_t lh_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 lh_status lh_forward_timed(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
                            int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream,

@@ -173,3 +173,15 @@ def test_selection_hook_addresses(L):
     assert L.lh_selection(None, N, H, d, Lv, p, k, 1, ctypes.byref(ptr)) == 1
     assert L.lh_selection(ws, 4096, 2, 64, 1, 2, 0, 1, ctypes.byref(ptr)) == 1     # L = 1: nothing selected
     assert L.lh_selection(ws, 4098, 2, 64, 3, 2, 4, 1, ctypes.byref(ptr)) == 1     # bad shape
+
+
+def test_static_forward_validates_before_any_device_call(L):
+    # rejections come before the scratch is looked up on a device
+    assert L.lh_static_scratch_bytes() == 64 << 20
+    fake = 1 << 40
+    big = (65536, 16, 128, 3, 2, 1536, 0)      # forward workspace 1.3 GiB > 64 MiB
+    assert L.lh_forward_workspace_bytes(*big) > L.lh_static_scratch_bytes()
+    assert L.lh_forward_static(fake, fake, fake, *big, fake, None) == 2
+    assert L.lh_forward_static(fake, fake, fake, 4098, 4, 64, 3, 2, 256, 0, fake, None) == 1
+    assert L.lh_forward_static(None, fake, fake, 4096, 4, 64, 3, 2, 256, 0, fake, None) == 1
+    assert L.lh_forward_static(fake, fake, fake, 4096, 4, 64, 3, 2, 256, 0, fake + 8, None) == 1
