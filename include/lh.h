@@ -111,10 +111,17 @@ int64_t lh_subseq_len(int64_t N, int L, int p, int k);
 
 /* Bytes of device workspace lh_forward + lh_backward need for this shape;
  * 0 if the shape is invalid. The dS tiles the backward stores for its dQ
- * kernel (the causal half of S x S per head, fp16) are planned only while
- * they take at most 8 GiB; beyond that the dQ kernel recomputes the logits
- * and dP, and the workspace grows as O(H S d) only. */
+ * kernel (the causal half of S x S per head, fp16: H * T(T+1)/2 * 2 KiB,
+ * T = S_pad/32) are planned only while they fit the dS tile budget (8 GiB
+ * unless set otherwise); beyond it the dQ kernel recomputes the logits and
+ * dP instead, and the workspace grows as O(H S d) only. */
 size_t lh_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt);
+
+/* The dS tile budget of every later plan in this process (bytes; 0: always
+ * recompute). Sizes and calls must agree: a workspace sized under one budget
+ * and used under another may be too small (LH_EWORKSPACE). Thread-safe. */
+void lh_set_ds_tile_budget(size_t bytes);
+size_t lh_ds_tile_budget(void);
 
 /* Bytes of workspace lh_forward alone needs (a prefix of the layout above):
  * a caller that never runs lh_backward may pass a workspace of this size.

@@ -8,6 +8,6 @@ dense causal attention over it and scatters every output back over its
 causal-safe shifted range. ``forward`` / ``backward`` call liblh.so; see
 include/lh.h for the ABI.
 """
-from .binding import (LighthouseError, alloc_workspace, backward, check_shape, forward,  # noqa: F401
-                      forward_static, forward_workspace_bytes, lib, padded_subseq_len, region, selection, selftest_sqrt,
+from .binding import (LighthouseError, alloc_workspace, backward, check_shape, ds_tile_budget, forward,  # noqa: F401
+                      forward_static, forward_workspace_bytes, lib, padded_subseq_len, region, selection, selftest_sqrt, set_ds_tile_budget,
                       stage_names, static_scratch_bytes, subseq_len, workspace_bytes)

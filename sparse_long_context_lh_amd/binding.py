@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         "lh_forward_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
         "lh_forward_static": (i32, [vp, vp, vp] + shape + [vp, vp]),
         "lh_static_scratch_bytes": (sz, []),
+        "lh_set_ds_tile_budget": (None, [sz]),
+        "lh_ds_tile_budget": (sz, []),
         "lh_backward_timed": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp, vp]),
         "lh_stage_count": (i32, [i32]),
         "lh_stage_name": (ctypes.c_char_p, [i32, i32]),
@@ -176,6 +178,16 @@ def forward_static(q, k, v, L: int, p: int, k_sel: int, out: torch.Tensor | None
     _check(lib().lh_forward_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, _dt(q.dtype),
                                    out.data_ptr(), _stream(stream)), "lh_forward_static")
     return out
+
+
+def set_ds_tile_budget(nbytes: int) -> None:
+    """Largest share of a workspace the backward's stored dS tiles may take
+    (0: the dQ kernel always recomputes S and dP)."""
+    lib().lh_set_ds_tile_budget(nbytes)
+
+
+def ds_tile_budget() -> int:
+    return lib().lh_ds_tile_budget()
 
 
 def static_scratch_bytes() -> int:

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "lh_internal.h"
@@ -19,6 +20,9 @@ static int ilog2_exact(int p)
 }
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static std::atomic<size_t> g_ds_tile_budget{kDsTileBudgetDefault};
+size_t ds_tile_budget() { return g_ds_tile_budget.load(std::memory_order_relaxed); }
 
 // The parts of a plan that depend on N, L, p and k alone: level sizes,
 // strata, S and S_pad. Checks the rules of the method on these four.
@@ -143,7 +147,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     // recomputes S and dP instead of reading them).
     const size_t Hs = (size_t)H, Sp = (size_t)pl->S_pad, D = (size_t)d;
     const size_t ds_bytes = 2 * Hs * (size_t)dst_tiles(pl->S_pad) * 1024;
-    pl->ds_tiles = ds_bytes <= kDsTileBudget;
+    pl->ds_tiles = ds_bytes <= ds_tile_budget();
     size_t b[IR_COUNT];
     b[LH_R_SCORES] = 4 * Hs * (size_t)tot;
     b[LH_R_SEL] = 4 * Hs * (size_t)(L - 1) * (size_t)pl->k;
@@ -372,8 +376,6 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         return LH_EINVAL;
     if ((st = check_ws(ws, ws_bytes, pl.total)) != LH_OK)
         return st;
-    if (!pl.ds_tiles)
-        return LH_EUNSUPPORTED; // the dQ kernel that recomputes S and dP is not built yet
     int32_t *slot = at<int32_t>(ws, pl, LH_R_SLOT);
     float *dosub = at<float>(ws, pl, LH_R_DOSUB);
 
@@ -448,7 +450,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.dq = at<float>(ws, pl, LH_R_DQSUB);
     ab.dk = at<float>(ws, pl, LH_R_DKSUB);
     ab.dv = at<float>(ws, pl, LH_R_DVSUB);
-    ab.dst = at<uint16_t>(ws, pl, IR_DST);
+    ab.dst = pl.ds_tiles ? at<uint16_t>(ws, pl, IR_DST) : nullptr; // none: the dQ kernel recomputes S and dP
     ab.dst_head = dst_tiles(pl.S_pad) * 1024;
     ab.S = pl.S; ab.S_pad = pl.S_pad; ab.H = H;
     ab.scale = (float)(1.0 / sqrt((double)d));
@@ -632,6 +634,10 @@ lh_status lh_forward_static(const void *q, const void *k, const void *v, int64_t
 }
 
 size_t lh_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+void lh_set_ds_tile_budget(size_t bytes) { g_ds_tile_budget.store(bytes, std::memory_order_relaxed); }
+
+size_t lh_ds_tile_budget(void) { return ds_tile_budget(); }
 
 lh_status lh_forward_timed(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
                            int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream,

@@ -756,7 +756,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         eye0 = make_uint4(w0[0], w0[1], w0[2], w0[3]);
         eye1 = make_uint4(w1[0], w1[1], w1[2], w1[3]);
     }
-    uint16_t *const dst_head = a.dst + (int64_t)h * a.dst_head;
+    uint16_t *const dst_head = a.dst + (a.dst != nullptr ? (int64_t)h * a.dst_head : 0);
     const int kt = kw / 32; // this wave's key tile
     const int nst = (S - k0 + BQ - 1) / BQ;
 
@@ -935,7 +935,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             dkT[t] = mfma32(ga[t & 1][2], db0, dkT[t]);
             dkT[t] = mfma32(ga[t & 1][3], db1, dkT[t]);
-            if (t == NT - 1) { // (the transposes have finished by now)
+            if (t == NT - 1 && a.dst != nullptr) { // (the transposes have finished by now)
                 const int qt = q0 / 32;
                 uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
                 float t8[8];
@@ -1124,20 +1124,222 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
                             dqT[t][4 * i4 + 3] * a.scale);
 }
 
-template <int D>
-static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, hipStream_t s)
+// ============================================================== backward: dQ, recomputed
+// dQ without stored dS tiles (the plan drops them when the causal half of
+// S x S per head would take too much of the workspace): the query side of
+// the softmax gradient, with S and dP formed again from the gathered rows.
+// One workgroup per 128 queries (32 per wave); keys stream through a two-slot
+// LDS ring 32 at a time. Per key block, as in the forward, keys are the rows
+// of every product so that a lane owns one query:
+//   S^T = K Q^T (the logits the other kernels form, same operands),
+//   P^T = 2^(S^T log2(e)/sqrt(d) - LSE + 15)  (probabilities times 2^15),
+//   dP^T = V dO^T (the fp16 pair of dO_sub, as in the dK/dV kernel),
+//   dS^T = P^T (dP^T 2^-15 - delta 2^-15)    (delta is per query: per lane),
+//   dQ^T += K^T dS^T, with dS^T straight from the accumulator as operand B
+// (the kappa row order of K and V puts each lane's keys in runs of 8).
+template <int D, bool KLO> struct DqrcStage {
+    static constexpr int BN = 32;
+    static constexpr int KCH = D / 8, TCH = BN / 8;
+    static constexpr int KROWS = BN * KCH, TROWS = D * TCH;
+    // K hi rows, the key's second operand (fp16 K lo for fp32 inputs, the fp8
+    // K tile for bf16 inputs, padded to one transfer per thread), V rows, the
+    // fp8 V tile (bf16 inputs), K^T
+    static constexpr int KH = 0, KL = KROWS, KLSIZE = KLO ? KROWS : 256;
+    static constexpr int VR = KL + KLSIZE, V8 = VR + KROWS, V8SIZE = KLO ? 0 : 256;
+    static constexpr int KT = V8 + V8SIZE;
+    static constexpr int SIZE = KT + TROWS;
+    static constexpr int KU = KROWS / 256, TU = TROWS / 256;
+};
+
+template <int D, bool KLO>
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
 {
-    hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), 0, s, a);
+    typedef DqrcStage<D, KLO> St;
+    constexpr int BM = 128, BN = St::BN;
+    constexpr int NS = D / 16, NT = D / 32, NM = D / 64;
+    __shared__ uint4 ring[2 * St::SIZE];
+
+    const int nqb = (int)((a.S + BM - 1) / BM);
+    const int h = blockIdx.x % a.H;
+    const int qb = nqb - 1 - (int)(blockIdx.x / a.H); // longest rows first
+    const int64_t q0 = (int64_t)qb * BM;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
+    const int64_t qw = q0 + wave * 32;
+    const int64_t hS = (int64_t)h * a.S_pad;
+    const int64_t kend = min(q0 + BM, a.S);
+    const int nkb = (int)((kend + BN - 1) / BN);
+    // last key block this wave uses: its diagonal block (rows past S: the
+    // workgroup's last one; their results are never read)
+    const int jl = (int)min((int64_t)(nkb - 1), qw / BN);
+
+    // per-thread byte offsets inside a stage (operand order, as in the forward):
+    // K / V row chunk of k-step f = 4u + wave, key row kappa(c32); K^T chunk of
+    // fragment f = (hh, t): dimension 32t + c32, keys 16hh + 8g .. +7
+    uint32_t koff[St::KU], toff[St::TU];
+#pragma unroll
+    for (int u = 0; u < St::KU; ++u) {
+        const int f = 4 * u + wave;
+        koff[u] = 2u * (uint32_t)(kappa(c32) * D + (2 * f + g) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < St::TU; ++u) {
+        const int f = 4 * u + wave, hh = f / NT, t = f % NT;
+        toff[u] = 2u * ((uint32_t)(32 * t + c32) * (uint32_t)a.S_pad + (uint32_t)(16 * hh + 8 * g));
+    }
+    const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D, *vr = a.v + hS * D;
+    const uint8_t *k8 = a.k8 + hS * D, *v8 = a.v8 + hS * D;
+    const uint16_t *kt = a.khi_t + (int64_t)h * D * a.S_pad;
+    auto slot = [&](int kb) { return ring + (kb & 1) * St::SIZE; };
+    auto issue = [&](int kb) {
+        if (kb >= nkb)
+            return;
+        const int64_t k0 = (int64_t)kb * BN;
+        const uint4 *base = slot(kb);
+#pragma unroll
+        for (int u = 0; u < St::KU; ++u) {
+            dma16(khi + k0 * D, koff[u], base + St::KH + 256 * u + 64 * wave);
+            if constexpr (KLO)
+                dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
+            dma16(vr + k0 * D, koff[u], base + St::VR + 256 * u + 64 * wave);
+        }
+        if constexpr (!KLO) { // fp8 tiles, stored in operand order: linear copies
+            dma16(k8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::KL + 64 * wave);
+            dma16(v8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::V8 + 64 * wave);
+        }
+#pragma unroll
+        for (int u = 0; u < St::TU; ++u)
+            dma16(kt + k0, toff[u], base + St::KT + 256 * u + 64 * wave);
+    };
+    issue(0);
+
+    // this lane's query as operand B: Q hi, dO_sub hi, and their lo parts
+    // (fp16 for fp32 inputs; the fp8 tiles for bf16 inputs, which keep query
+    // qw + c32 at lane position kappa(c32) + 32g)
+    const int64_t qrow = (hS + qw + c32) * D;
+    uint4 qh[NS], dh[NS], ql[KLO ? NS : 1], dl[KLO ? NS : 1], q8[KLO ? 1 : NM][2], d8[KLO ? 1 : NM][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        qh[s] = ld16(a.qhi + qrow + 16 * s + 8 * g);
+        dh[s] = ld16(a.dohi + qrow + 16 * s + 8 * g);
+        if constexpr (KLO) {
+            ql[s] = ld16(a.qlo + qrow + 16 * s + 8 * g);
+            dl[s] = ld16(a.dolo + qrow + 16 * s + 8 * g);
+        }
+    }
+    int qs = 0, ks = 0, vs = 0, ds8 = 0;
+    if constexpr (!KLO) {
+        const int64_t t8 = (hS + qw) * D + 16 * (kappa(c32) + 32 * g);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                q8[m][q] = *reinterpret_cast<const uint4 *>(a.qlo8 + t8 + 2048 * m + 1024 * q);
+                d8[m][q] = *reinterpret_cast<const uint4 *>(a.dolo8 + t8 + 2048 * m + 1024 * q);
+            }
+        qs = a.sc8[h];
+        ks = a.sc8[a.H + h];
+        vs = a.sc8[2 * a.H + h];
+        ds8 = a.sc8[3 * a.H + h];
+    }
+    const float lq = a.lse[hS + qw + c32];   // log2-domain LSE - 15 of this lane's query
+    const float dq8 = a.delta[hS + qw + c32]; // delta * 2^-15
+    // consume the loads here (see the forward kernel)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        asm volatile("" ::"v"(qh[s].x), "v"(dh[s].x));
+        if constexpr (KLO)
+            asm volatile("" ::"v"(ql[s].x), "v"(dl[s].x));
+    }
+    if constexpr (!KLO) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+            asm volatile("" ::"v"(q8[m][0].x), "v"(q8[m][1].x), "v"(d8[m][0].x), "v"(d8[m][1].x));
+        asm volatile("" ::"v"(qs), "v"(ks), "v"(vs), "v"(ds8));
+    }
+    asm volatile("" ::"v"(lq), "v"(dq8));
+
+    f32x16_t dq[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        dq[t] = zero16();
+    for (int j = 0; j < nkb; ++j) {
+        wait_async();  // stage j (the only one in flight)
+        lds_barrier(); // ... visible to all waves; the other slot (stage j-1) is free
+        issue(j + 1);
+        if (j > jl) // (uniform) keys after every query of this wave
+            continue;
+        const uint4 *base = slot(j);
+        f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint4 kf = base[St::KH + 64 * s + lane];
+            st = mfma32(kf, qh[s], st);
+            if constexpr (KLO) {
+                st = mfma32(base[St::KL + 64 * s + lane], qh[s], st);
+                st = mfma32(kf, ql[s], st);
+            }
+            const uint4 vf = base[St::VR + 64 * s + lane];
+            dp = mfma32(vf, dh[s], dp);
+            if constexpr (KLO)
+                dp = mfma32(vf, dl[s], dp);
+        }
+        if constexpr (!KLO) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                st = mfma8(base[St::KL + 128 * m + lane], base[St::KL + 128 * m + 64 + lane], q8[m][0], q8[m][1], st,
+                           ks, qs);
+                dp = mfma8(base[St::V8 + 128 * m + lane], base[St::V8 + 128 * m + 64 + lane], d8[m][0], d8[m][1], dp,
+                           vs, ds8);
+            }
+        }
+        // register v holds key 16(v/8) + 8g + v%8 of the block; keys after
+        // the lane's query (diagonal block) have P = 0, so dS = 0
+        const int rel = (int)((int64_t)j * BN - qw); // first key of the block - first query of the wave
+        float ds[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const bool ok = rel + 16 * (v >> 3) + 8 * g + (v & 7) <= c32;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lq)) : 0.0f;
+            ds[v] = pr * __builtin_fmaf(dp[v], kPScaleInv, -dq8);
+        }
+        const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dq[t] = mfma32(base[St::KT + 64 * t + lane], db0, dq[t]);
+            dq[t] = mfma32(base[St::KT + 64 * (NT + t) + lane], db1, dq[t]);
+        }
+    }
+    float *dqr = a.dq + qrow;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<float4 *>(dqr + 32 * t + 8 * i4 + 4 * g) =
+                make_float4(dq[t][4 * i4] * a.scale, dq[t][4 * i4 + 1] * a.scale, dq[t][4 * i4 + 2] * a.scale,
+                            dq[t][4 * i4 + 3] * a.scale);
+}
+
+template <int D>
+static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, bool tiles, bool klo, hipStream_t s)
+{
+    if (tiles)
+        hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), 0, s, a);
+    else if (klo)
+        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, false>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
 {
     const unsigned nqb = (unsigned)((pl.S + 127) / 128);
     const dim3 grid(nqb * pl.H);
+    const bool klo = pl.dt == LH_F32;
     if (pl.d == 128)
-        launch_dq_t<128>(grid, a, s);
+        launch_dq_t<128>(grid, a, pl.ds_tiles, klo, s);
     else
-        launch_dq_t<64>(grid, a, s);
+        launch_dq_t<64>(grid, a, pl.ds_tiles, klo, s);
     return hipGetLastError();
 }
 

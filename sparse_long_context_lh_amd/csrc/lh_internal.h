@@ -17,10 +17,12 @@ constexpr int kMaxSelTotal = 16384; // (L-1)*k held in LDS by the index kernel
 constexpr int kSubseqAlign = 256;   // S is padded to this for the attention tiles
 constexpr int64_t kMaxN = int64_t(1) << 27;
 constexpr int kMaxHeads = 65535; // heads run along the grid's y dimension
-// Largest workspace share of the backward's stored dS tiles (the causal half
-// of S x S per head, fp16). Above it the dQ kernel recomputes S and dP from
-// the gathered rows instead, and the workspace stays O(S d).
-constexpr size_t kDsTileBudget = size_t(8) << 30;
+// Default largest workspace share of the backward's stored dS tiles (the
+// causal half of S x S per head, fp16). Above it the dQ kernel recomputes S
+// and dP from the gathered rows instead, and the workspace stays O(S d). The
+// process-wide value is set with lh_set_ds_tile_budget.
+constexpr size_t kDsTileBudgetDefault = size_t(8) << 30;
+size_t ds_tile_budget();
 // Largest workspace a plan may ask for (64 TiB): shapes beyond it are reported
 // as unsupported rather than sized.
 constexpr size_t kMaxWorkspace = size_t(1) << 46;

@@ -185,3 +185,30 @@ def test_static_forward_validates_before_any_device_call(L):
     assert L.lh_forward_static(fake, fake, fake, 4098, 4, 64, 3, 2, 256, 0, fake, None) == 1
     assert L.lh_forward_static(None, fake, fake, 4096, 4, 64, 3, 2, 256, 0, fake, None) == 1
     assert L.lh_forward_static(fake, fake, fake, 4096, 4, 64, 3, 2, 256, 0, fake + 8, None) == 1
+
+
+def test_ds_tile_budget_sizes_the_workspace(L):
+    shape = (524288, 16, 128, 5, 4, 512, 0)
+    S_pad = L.lh_padded_subseq_len(524288, 5, 4, 512)
+    T = S_pad // 32
+    tiles = 2 * 16 * (T * (T + 1) // 2) * 1024
+    old = L.lh_ds_tile_budget()
+    assert old == 8 << 30
+    full = L.lh_workspace_bytes(*shape)
+    fwd = L.lh_forward_workspace_bytes(*shape)
+    try:
+        L.lh_set_ds_tile_budget(0)
+        small = L.lh_workspace_bytes(*shape)
+        assert L.lh_forward_workspace_bytes(*shape) == fwd
+        # the dS tiles are the last region: exactly their bytes (rounded to 256) go
+        assert full - small == (tiles + 255) // 256 * 256
+        L.lh_set_ds_tile_budget(tiles)       # exactly enough: kept
+        assert L.lh_workspace_bytes(*shape) == full
+        L.lh_set_ds_tile_budget(tiles - 1)   # one byte short: recomputed
+        assert L.lh_workspace_bytes(*shape) == small
+    finally:
+        L.lh_set_ds_tile_budget(old)
+    # dense attention over 512K tokens (L = 1): the tiles would take 4.4 TB;
+    # the plan recomputes instead and the workspace is O(H S d)
+    dense = L.lh_workspace_bytes(524288, 16, 128, 1, 2, 0, 0)
+    assert 0 < dense < 200 << 30

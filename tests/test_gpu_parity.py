@@ -205,3 +205,47 @@ def test_selection_hook_and_forward_only_workspace():
             b = lh.selection(ws_fwd, N, H, d, L, p, k, l)[h].cpu().numpy()
             assert np.array_equal(a, ref["sel"][l]) and np.array_equal(b, ref["sel"][l])
             assert np.array_equal(a, full.head("sel", h)[l - 1].numpy())
+
+
+@pytest.fixture
+def recompute_dq():
+    """Plans without stored dS tiles: the dQ kernel recomputes S and dP."""
+    old = lh.ds_tile_budget()
+    lh.set_ds_tile_budget(0)
+    yield
+    lh.set_ds_tile_budget(old)
+
+
+@pytest.mark.parametrize("N,H,d,L,p,k,dtype,n_plant", [
+    (32768, 2, 128, 5, 4, 32, torch.bfloat16, 32),   # the 512K workload's pyramid
+    (8192, 2, 128, 3, 4, 50, torch.bfloat16, 8),
+    (4096, 2, 64, 3, 2, 200, torch.float32, 0),
+    (4096, 2, 128, 3, 2, 128, torch.float32, 4),
+    (1000, 2, 64, 1, 2, 0, torch.bfloat16, 8),       # dense, ragged
+    (64, 1, 128, 3, 2, 3, torch.bfloat16, 0),        # one tile, all tail
+])
+def test_recomputed_dq(recompute_dq, N, H, d, L, p, k, dtype, n_plant):
+    _case(N, H, d, L, p, k, dtype, n_plant=n_plant, bwd=True, tag="dq-recompute")
+
+
+def test_recomputed_dq_against_stored_tiles():
+    # same dK and dV bit for bit (the dK/dV kernel only skips its dS store);
+    # dQ from recomputed S and dP within the tolerance of the stored tiles' dQ
+    N, H, d, L, p, k = 16384, 2, 128, 4, 4, 60
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, torch.bfloat16, 8, 41))
+    dout = make_dout(N, H, d, torch.bfloat16, 42).cuda()
+    a = GpuRun(q, kk, v, L, p, k, dout)
+    old = lh.ds_tile_budget()
+    lh.set_ds_tile_budget(0)
+    try:
+        b = GpuRun(q, kk, v, L, p, k, dout)
+    finally:
+        lh.set_ds_tile_budget(old)
+    assert b.ws.numel() < a.ws.numel()
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.grads[1], b.grads[1]) and torch.equal(a.grads[2], b.grads[2])
+    for h in range(H):
+        x, y = a.head("dqsub", h)[:a.S].numpy(), b.head("dqsub", h)[:a.S].numpy()
+        err = np.abs(x.astype(np.float64) - y)
+        assert np.all(err <= 2e-2 + 2.0 ** -7 * np.abs(x).max(axis=-1, keepdims=True))
+        say("  head %d: dQ_sub recomputed vs stored tiles: max %.3g" % (h, err.max()))
