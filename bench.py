@@ -1,7 +1,7 @@
 """Throughput of the Lighthouse layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--copy-calibration]
+                    [--no-extra] [--copy-calibration]
     python bench.py --summarize-stats DIR              (rocprofv3 --stats output -> markdown)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR [--workload NAME]
 
@@ -10,6 +10,12 @@ of the path, all heads), inputs resident in HBM. The default workload is the
 512K-token forward + backward shape (H=16, d=128, L=5, p=4, k=512, S=10240),
 the single-layer setting at which the layer's forward and forward+backward
 speedups are quoted. Prints one JSON line.
+
+With the default workload the same JSON line also carries the rest of the
+metric's range ("workloads": 1M tokens forward + backward, 128K and 64K
+forward, each with its dominant stage's roofline) and dense causal attention
+over the same 512K tokens ("dense_512k": L = 1, S = N, one warmup and one
+timed step), with the layer's speedup over it, forward and forward+backward.
 
 Per-kernel timing: the library records caller-created HIP events between its
 stages on the launch stream (lh_forward_timed / lh_backward_timed), so every
@@ -69,6 +75,15 @@ def stage_of(kernel_name: str):
     return None
 
 
+def ds_tiles_kept(w, S: int) -> bool:
+    """Whether the library's plan stores the backward's dS tiles for this shape
+    (the causal half of S x S per head in fp16, within the dS tile budget);
+    otherwise its dQ kernel recomputes S and dP."""
+    import sparse_long_context_lh_amd as lh
+    T = (S + 255) // 256 * 256 // 32
+    return 2 * w.H * (T * (T + 1) // 2) * 1024 <= lh.ds_tile_budget()
+
+
 def algorithmic(stage: str, w, S: int) -> float:
     """Algorithmic work of one launch of `stage` over the whole workload:
     flops for the attention stages, HBM bytes for the others (the least
@@ -82,8 +97,8 @@ def algorithmic(stage: str, w, S: int) -> float:
         return 2.0 * S * S * d * H
     if stage == "attn_bwd_dkdv":   # S, dP, dV, dK: four causal products
         return 4.0 * S * S * d * H
-    if stage == "attn_bwd_dq":     # dQ: one causal product
-        return 1.0 * S * S * d * H
+    if stage == "attn_bwd_dq":     # dQ: one causal product (three when S and dP are recomputed)
+        return (1.0 if ds_tiles_kept(w, S) else 3.0) * S * S * d * H
     if stage == "front":           # read Q, K, V; write the score pyramid
         return 3.0 * N * d * H * s_io + 4.0 * lvl * H
     if stage == "topk":            # read levels 1.. of the scores; write the selection
@@ -151,9 +166,16 @@ def cpu_baseline(q, k, v, dout, w, min_seconds=10.0):
         dt += time.perf_counter() - t0
         del ref
         heads += 1
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host = os.cpu_count() or 1
     return {"value": w.N * heads / (dt * w.H), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": "heads 0-%d of %d (forward + backward, %.1f s of oracle time), scaled by the share of heads"
-                      % (heads - 1, w.H, dt)}
+                      % (heads - 1, w.H, dt),
+            "host_cores": host,
+            "threads": "cores = the BLAS threads of the oracle's matrix products; its per-entry scatter, "
+                       "scatter-adjoint and pool-adjoint loops run on one thread"}
 
 
 def load_traffic(stage: str, workload: str):
@@ -236,6 +258,89 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
             f.write("\n")
 
 
+def measure(lh, hip, w0, steps, warmup, backward=True):
+    """Time `steps` calls of the layer on workload w0 (forward + backward, or
+    forward alone) after `warmup` untimed ones; per-stage times from the HIP
+    events the library records between its kernels on the launch stream."""
+    import torch
+    from synth_inputs import make_dout, make_qkv
+
+    class W:  # workload fields used by algorithmic()
+        pass
+    w = W()
+    w.N, w.H, w.d, w.L, w.p, w.k = w0.N, w0.H, w0.d, w0.L, w0.p, w0.k
+    w.dtype_name = "bf16" if w0.dtype == torch.bfloat16 else "fp32"
+    q, k, v = make_qkv(w.N, w.H, w.d, w0.dtype, w0.n_plant, seed=0, device="cuda")
+    dout = make_dout(w.N, w.H, w.d, w0.dtype, seed=1, device="cuda") if backward else None
+    S = lh.subseq_len(w.N, w.L, w.p, w.k)
+    ws = lh.alloc_workspace(w.N, w.H, w.d, w.L, w.p, w.k, w0.dtype, forward_only=not backward)
+    out = torch.empty_like(q)
+    grads = tuple(torch.empty_like(q) for _ in range(3)) if backward else None
+    stream = torch.cuda.current_stream()
+
+    def step(evf=None, evb=None):
+        lh.forward(q, k, v, w.L, w.p, w.k, ws=ws, out=out, stream=stream, events=evf)
+        if backward:
+            lh.backward(dout, w.L, w.p, w.k, ws, *grads, stream=stream, events=evb)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    fnames, bnames = lh.stage_names(False), (lh.stage_names(True) if backward else [])
+    evf = [hip.events(len(fnames) + 1) for _ in range(steps)]
+    evb = [hip.events(len(bnames) + 1) for _ in range(steps)] if backward else [None] * steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evf[i], evb[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {}
+    for names, evs in ((fnames, evf), (bnames, evb)):
+        for j, name in enumerate(names):
+            stage_ms[name] = sum(hip.elapsed(e[j], e[j + 1]) for e in evs) / steps
+    fwd_ms = sum(hip.elapsed(e[0], e[len(fnames)]) for e in evf) / steps
+    bwd_ms = sum(hip.elapsed(e[0], e[len(bnames)]) for e in evb) / steps if backward else 0.0
+    for e in evf + (evb if backward else []):
+        hip.destroy(e)
+
+    stages = {}
+    for name, ms in stage_ms.items():
+        a = algorithmic(name, w, S) / (ms / 1000.0) if ms > 0 else 0.0
+        if name in MFMA_STAGES:
+            stages[name] = {"ms": round(ms, 4), "TFLOP/s": round(a / 1e12, 1), "frac": round(a / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+        else:
+            stages[name] = {"ms": round(ms, 4), "GB/s": round(a / 1e9, 1), "frac": round(a / 1e9 / HBM_PEAK_GBS, 4)}
+    dom = max(stage_ms, key=stage_ms.get)
+    work = algorithmic(dom, w, S)
+    sec = stage_ms[dom] / 1000.0
+    if dom in MFMA_STAGES:
+        achieved, peak, unit, bound = work / sec / 1e12, MFMA_F16_PEAK_TFS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = work / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    res = {"w": w, "S": S, "ms_per_step": wall * 1000.0 / steps, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+           "stages": stages,
+           "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                        "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, w0.name)},
+           "inputs": (q, k, v, dout)}
+    del ws, out, grads
+    return res
+
+
+def summary(r, steps, warmup, backward):
+    """The record of one extra workload in the JSON line."""
+    w = r["w"]
+    d = {"N": w.N, "H": w.H, "d": w.d, "L": w.L, "p": w.p, "k": w.k, "S": r["S"], "steps": steps, "warmup": warmup,
+         "fwd_ms": round(r["fwd_ms"], 4), "fwd_tokens_per_s": round(w.N / (r["fwd_ms"] / 1000.0), 1),
+         "roofline": r["roofline"]}
+    if backward:
+        d.update({"fwdbwd_ms": round(r["ms_per_step"], 4),
+                  "fwdbwd_tokens_per_s": round(w.N / (r["ms_per_step"] / 1000.0), 1),
+                  "bwd_ms": round(r["bwd_ms"], 4)})
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +348,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lh-fwdbwd-512k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the headline workload only (no other sizes, no dense denominator)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB read + 1 GiB write elementwise kernel before the warmup")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -261,100 +368,65 @@ def main():
 
     import torch
     import sparse_long_context_lh_amd as lh
-    from synth_inputs import by_name, make_dout, make_qkv
+    from synth_inputs import by_name
 
-    w0 = by_name(args.workload)
-
-    class W:  # workload fields used by algorithmic()
-        pass
-    w = W()
-    w.N, w.H, w.d, w.L, w.p, w.k = w0.N, w0.H, w0.d, w0.L, w0.p, w0.k
-    w.dtype_name = "bf16" if w0.dtype == torch.bfloat16 else "fp32"
     torch.cuda.set_device(0)
-    dev = "cuda"
-    q, k, v = make_qkv(w.N, w.H, w.d, w0.dtype, w0.n_plant, seed=0, device=dev)
-    dout = make_dout(w.N, w.H, w.d, w0.dtype, seed=1, device=dev)
-    S = lh.subseq_len(w.N, w.L, w.p, w.k)
-    ws = lh.alloc_workspace(w.N, w.H, w.d, w.L, w.p, w.k, w0.dtype)
-    out = torch.empty_like(q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    stream = torch.cuda.current_stream()
-
-    def step(evf=None, evb=None):
-        lh.forward(q, k, v, w.L, w.p, w.k, ws=ws, out=out, stream=stream, events=evf)
-        lh.backward(dout, w.L, w.p, w.k, ws, dq, dk, dv, stream=stream, events=evb)
-
     if args.copy_calibration:
-        src = torch.full((CALIB_BYTES // 4,), 7, dtype=torch.int32, device=dev)
+        src = torch.full((CALIB_BYTES // 4,), 7, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(2):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     hip = Hip()
-    fnames, bnames = lh.stage_names(False), lh.stage_names(True)
-    evf = [hip.events(len(fnames) + 1) for _ in range(args.steps)]
-    evb = [hip.events(len(bnames) + 1) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evf[i], evb[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    stage_ms = {}
-    for names, evs in ((fnames, evf), (bnames, evb)):
-        for j, name in enumerate(names):
-            stage_ms[name] = sum(hip.elapsed(e[j], e[j + 1]) for e in evs) / args.steps
-    fwd_ms = sum(hip.elapsed(e[0], e[len(fnames)]) for e in evf) / args.steps
-    bwd_ms = sum(hip.elapsed(e[0], e[len(bnames)]) for e in evb) / args.steps
-    for e in evf + evb:
-        hip.destroy(e)
-
-    ms_per_step = wall * 1000.0 / args.steps
-    dom = max(stage_ms, key=stage_ms.get)
-    work = algorithmic(dom, w, S)
-    sec = stage_ms[dom] / 1000.0
-    if dom in MFMA_STAGES:
-        achieved, peak, unit, bound = work / sec / 1e12, MFMA_F16_PEAK_TFS, "TFLOP/s", "mfma"
-    else:
-        achieved, peak, unit, bound = work / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-    stages = {}
-    for name, ms in stage_ms.items():
-        a = algorithmic(name, w, S) / (ms / 1000.0) if ms > 0 else 0.0
-        if name in MFMA_STAGES:
-            stages[name] = {"ms": round(ms, 4), "TFLOP/s": round(a / 1e12, 1), "frac": round(a / 1e12 / MFMA_F16_PEAK_TFS, 4)}
-        else:
-            stages[name] = {"ms": round(ms, 4), "GB/s": round(a / 1e9, 1), "frac": round(a / 1e9 / HBM_PEAK_GBS, 4)}
-
+    w0 = by_name(args.workload)
+    head = measure(lh, hip, w0, args.steps, args.warmup, backward=w0.backward)
+    w = head["w"]
     res = {
         "metric": METRIC,
-        "value": round(w.N / (ms_per_step / 1000.0), 1),
+        "value": round(w.N / (head["ms_per_step"] / 1000.0), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w0.dtype == torch.bfloat16 else "fp32",
         "data": "synthetic",
-        "config": {"workload": w0.name, "N": w.N, "H": w.H, "d": w.d, "L": w.L, "p": w.p, "k": w.k, "S": S,
-                   "step": "forward+backward", "parallelism": "none (1 GPU)"},
-        "fwd_tokens_per_s": round(w.N / (fwd_ms / 1000.0), 1),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, w0.name)},
-        "stages": stages,
+        "config": {"workload": w0.name, "N": w.N, "H": w.H, "d": w.d, "L": w.L, "p": w.p, "k": w.k, "S": head["S"],
+                   "step": "forward+backward" if w0.backward else "forward", "parallelism": "none (1 GPU)"},
+        "fwd_tokens_per_s": round(w.N / (head["fwd_ms"] / 1000.0), 1),
+        "fwd_ms": round(head["fwd_ms"], 4),
+        "bwd_ms": round(head["bwd_ms"], 4),
+        "roofline": head["roofline"],
+        "stages": head["stages"],
     }
     if not args.no_cpu_baseline:
+        q, k, v, dout = head["inputs"]
         res["cpu_baseline"] = cpu_baseline(q, k, v, dout, w)
+    head.pop("inputs")
+    torch.cuda.empty_cache()
+    if not args.no_extra and w0.name == "lh-fwdbwd-512k":
+        # the rest of the metric's range (1M forward + backward, 128K and 64K
+        # forward), then dense causal attention over the same 512K tokens: the
+        # denominator of the layer's speedup
+        extra = {}
+        for name, steps, warm, bwd in (("lh-fwdbwd-1m", 5, 2, True), ("lh-fwd-128k", 5, 2, False),
+                                       ("lh-fwd-64k", 5, 2, False)):
+            r = measure(lh, hip, by_name(name), steps, warm, backward=bwd)
+            r.pop("inputs")
+            extra[name] = summary(r, steps, warm, bwd)
+            torch.cuda.empty_cache()
+        res["workloads"] = extra
+        r = measure(lh, hip, by_name("dense-fwdbwd-512k"), 1, 1, backward=True)
+        r.pop("inputs")
+        dense = summary(r, 1, 1, True)
+        dense["speedup_fwd"] = round(r["fwd_ms"] / head["fwd_ms"], 2)
+        dense["speedup_fwdbwd"] = round(r["ms_per_step"] / head["ms_per_step"], 2)
+        res["dense_512k"] = dense
+        torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

@@ -405,3 +405,41 @@ def attention_rows(qt, kt, vt, rows: np.ndarray) -> tuple[np.ndarray, np.ndarray
         out[r] = (e / lsum) @ vt[:a + 1]
         lse[r] = m + np.log(lsum)
     return out, lse
+
+
+def attention_bwd_query_rows(qt, kt, vt, dot, rows: np.ndarray) -> np.ndarray:
+    """dQ of the listed sub-sequence rows only (the textbook gradient of
+    attention_bwd, one query at a time): with the query's own softmax row P,
+    dP_b = dO_a . V_b, delta = sum_b P_b dP_b, dS_b = P_b (dP_b - delta),
+    dQ_a = sum_(b <= a) dS_b K_b / sqrt(d)."""
+    d = qt.shape[1]
+    out = np.empty((rows.shape[0], d), dtype=np.float64)
+    for r, a in enumerate(rows):
+        a = int(a)
+        z = (kt[:a + 1] @ qt[a]) / np.sqrt(d)
+        P = np.exp(z - z.max())
+        P /= P.sum()
+        dP = vt[:a + 1] @ dot[a]
+        dS = P * (dP - np.dot(P, dP))
+        out[r] = (dS @ kt[:a + 1]) / np.sqrt(d)
+    return out
+
+
+def attention_bwd_key_rows(qt, kt, vt, dot, keys: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """dK and dV of the listed sub-sequence rows only: dV_b = sum_(a >= b) P_ab
+    dO_a and dK_b = sum_(a >= b) dS_ab Q_a / sqrt(d), with each query's softmax
+    row formed on its own (every query from the smallest listed key on)."""
+    S, d = qt.shape
+    keys = np.asarray(keys, dtype=np.int64)
+    dk = np.zeros((keys.shape[0], d), dtype=np.float64)
+    dv = np.zeros((keys.shape[0], d), dtype=np.float64)
+    for a in range(int(keys.min()), S):
+        z = (kt[:a + 1] @ qt[a]) / np.sqrt(d)
+        P = np.exp(z - z.max())
+        P /= P.sum()
+        dP = vt[:a + 1] @ dot[a]
+        dS = P * (dP - np.dot(P, dP))
+        seen = keys <= a
+        dv[seen] += P[keys[seen], None] * dot[a][None, :]
+        dk[seen] += dS[keys[seen], None] * qt[a][None, :] / np.sqrt(d)
+    return dk, dv

@@ -45,8 +45,15 @@ WORKLOADS = [
 ]
 
 
+# Dense causal attention over the whole sequence (L = 1: S = N, every token
+# its own entry), the denominator of the layer's speedup at 512K tokens.
+DENSE_WORKLOADS = [
+    Workload("dense-fwdbwd-512k", 16, 128, 524288, 1, 2, 0, torch.bfloat16, 32, True),
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + DENSE_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

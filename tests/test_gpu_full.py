@@ -41,3 +41,37 @@ def test_full_size_workload(w):
         say("  head %d %s: %s" % (h, n, fmt_stats(st)))
     fails.raise_if_any()
     assert np.all(np.isfinite(run.out.float().cpu().numpy()))
+
+
+@pytest.mark.timeout(1200)
+def test_dense_512k_sampled_rows():
+    # dense causal attention over all 524288 tokens (L = 1, S = N), in the
+    # launch configuration the benchmark times (the dS tiles would take 4.4 TB,
+    # so the dQ kernel recomputes S and dP). The layer output of token a is the
+    # attention output of row a. Sampled query rows: output and dq; the last
+    # keys: dk and dv (they see only the last queries, so the oracle's per-row
+    # backward stays cheap).
+    from synth_inputs import by_name
+    from parity import assert_close
+    w = by_name("dense-fwdbwd-512k")
+    say("workload %s: N=%d H=%d d=%d L=%d (dense causal)" % (w.name, w.N, w.H, w.d, w.L))
+    q, k, v = make_qkv(w.N, w.H, w.d, w.dtype, w.n_plant, seed=0, device="cuda")
+    dout = make_dout(w.N, w.H, w.d, w.dtype, seed=1, device="cuda")
+    run = GpuRun(q, k, v, w.L, w.p, w.k, dout)
+    assert np.all(np.isfinite(run.out.float().cpu().numpy()))
+    h = 5
+    qh, kh, vh, dh = (head_inputs(x, h).astype(np.float64) for x in (q, k, v, dout))
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 2, 255, 256, 4095, w.N // 2, w.N - 1], rng.integers(0, w.N, 8)]))
+    o_ref, _ = oracle.attention_rows(qh, kh, vh, rows)
+    dq_ref = oracle.attention_bwd_query_rows(qh, kh, vh, dh, rows)
+    keys = np.array([w.N - 40, w.N - 17, w.N - 2, w.N - 1])
+    dk_ref, dv_ref = oracle.attention_bwd_key_rows(qh, kh, vh, dh, keys)
+    out = run.out[h].float().cpu().numpy()
+    dq, dk, dv = (g[h].float().cpu().numpy() for g in run.grads)
+    st = {"out": assert_close(out[rows], o_ref, "dense out", stored_bf16=True),
+          "dq": assert_close(dq[rows], dq_ref, "dense dq", stored_bf16=True, row_scaled=True),
+          "dk": assert_close(dk[keys], dk_ref, "dense dk", stored_bf16=True, row_scaled=True),
+          "dv": assert_close(dv[keys], dv_ref, "dense dv", stored_bf16=True)}
+    for n, s_ in st.items():
+        say("  head %d %s (%d rows): %s" % (h, n, len(keys) if n in ("dk", "dv") else len(rows), fmt_stats(s_)))

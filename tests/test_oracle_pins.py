@@ -321,6 +321,21 @@ def test_attention_rows_match_full():
     assert np.allclose(lse[rows], lse2, rtol=1e-12)
 
 
+def test_backward_rows_match_full():
+    # the per-row gradients used at sizes where the whole backward is slow
+    # equal the whole-matrix backward (itself pinned to torch's fp64 autograd)
+    q, k, v = (x.astype(np.float64) for x in _inputs(200, 16, seed=19))
+    dout = np.random.default_rng(20).standard_normal((200, 16))
+    o, lse = oracle.attention(q, k, v)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, lse, dout)
+    rows = np.array([0, 1, 57, 150, 199])
+    assert np.allclose(oracle.attention_bwd_query_rows(q, k, v, dout, rows), dq[rows], rtol=1e-10, atol=1e-12)
+    keys = np.array([120, 121, 180, 199])
+    dk2, dv2 = oracle.attention_bwd_key_rows(q, k, v, dout, keys)
+    assert np.allclose(dk2, dk[keys], rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv2, dv[keys], rtol=1e-10, atol=1e-12)
+
+
 def test_shape_rules():
     with pytest.raises(ValueError):
         oracle.check_shape(102, 64, 3, 2, 4)       # N not a multiple of p^(L-1)
