@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-extra] [--copy-calibration]
+    python bench.py --sweep [--steps K] [--warmup W]   ((L, p, k) sweep at 512K tokens)
     python bench.py --summarize-stats DIR              (rocprofv3 --stats output -> markdown)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR [--workload NAME]
 
@@ -350,6 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time the headline workload only (no other sizes, no dense denominator)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the (L, p, k) sweep at 512K tokens instead: one JSON line per shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB read + 1 GiB write elementwise kernel before the warmup")
     ap.add_argument("--summarize-stats", metavar="DIR")
@@ -379,6 +382,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     hip = Hip()
+    if args.sweep:
+        from synth_inputs import SWEEP_WORKLOADS
+        for w0 in SWEEP_WORKLOADS:
+            r = measure(lh, hip, w0, args.steps, args.warmup, backward=True)
+            r.pop("inputs")
+            rec = {"workload": w0.name, **summary(r, args.steps, args.warmup, True),
+                   "ds_tiles": ds_tiles_kept(r["w"], r["S"]),
+                   "stages_ms": {n: x["ms"] for n, x in r["stages"].items()}}
+            print(json.dumps(rec), flush=True)
+            torch.cuda.empty_cache()
+        return
     w0 = by_name(args.workload)
     head = measure(lh, hip, w0, args.steps, args.warmup, backward=w0.backward)
     w = head["w"]

@@ -52,8 +52,27 @@ DENSE_WORKLOADS = [
 ]
 
 
+# The (L, p, k) sweep at a fixed 512K tokens (H = 16, d = 128, bf16, 32
+# planted tokens): p in {2, 4}, k from 512 to 6144, L = 3 or 5 where the
+# pyramid allows it ((L-1) k <= 16384, k at most the top level's N/p^(L-1)
+# entries). S runs from 10240 to 155648.
+def _sweep():
+    out = []
+    for p in (2, 4):
+        for L in (3, 5):
+            for k in (512, 1536, 3072, 6144):
+                if (L - 1) * k > 16384 or k > 524288 // p ** (L - 1):
+                    continue
+                out.append(Workload("sweep-512k-L%d-p%d-k%d" % (L, p, k), 16, 128, 524288, L, p, k,
+                                    torch.bfloat16, 32, True))
+    return out
+
+
+SWEEP_WORKLOADS = _sweep()
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS + DENSE_WORKLOADS:
+    for w in WORKLOADS + DENSE_WORKLOADS + SWEEP_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)

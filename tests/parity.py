@@ -259,3 +259,72 @@ def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag=""):
         say("  %s head %d: %s" % (tag, h, "; ".join("%s %s" % (k2, fmt_stats(v2)) for k2, v2 in out[h].items())))
     fails.raise_if_any()
     return run, out
+
+
+def selection_ref(q, k, h, L, p, kk):
+    """The oracle's scores, selection and causal order of head h."""
+    qh, kh = head_inputs(q, h), head_inputs(k, h)
+    sc = oracle.score_pyramid(oracle.token_scores(qh, kh), L, p)
+    sel = oracle.select(sc, L, kk)
+    lev, idx = oracle.causal_order(oracle.expand(sel, q.shape[1], L, p), p)
+    return dict(scores=sc, sel=sel, ent_level=lev, ent_index=idx)
+
+
+def check_sampled_tokens(run: GpuRun, q, k, v, dout, h: int, tokens, last: int, tag: str = "") -> dict:
+    """Full-size check of one head on sampled tokens, where the whole oracle
+    would be slow: the oracle builds the selection, causal order and gathered
+    rows of the head, then only the sub-sequence rows the sampled tokens need.
+    Layer output and dq of `tokens`; dk and dv of the `last` final tokens
+    (their entries end at the sequence's end, so the key rows of the oracle's
+    backward need only the last few queries)."""
+    N, L, p = run.N, run.L, run.p
+    ref = selection_ref(q, k, h, L, p, run.k)
+    lev, idx = ref["ent_level"], ref["ent_index"]
+    S = lev.shape[0]
+    pos = [np.full(N // p ** l, -1, dtype=np.int64) for l in range(L)]
+    for l in range(L):
+        rows = np.nonzero(lev == l)[0]
+        pos[l][idx[rows]] = rows
+    xs = [head_inputs(x, h).astype(np.float64) for x in (q, k, v)]
+    qt, kt, vt = (oracle.gather(x, lev, idx, p) for x in xs)
+    tokens = np.asarray(sorted(set(int(t) for t in tokens)), dtype=np.int64)
+    # layer output: O_j = sum over l of O_sub of entry (l, (j+1)/p^l - 1) when gathered
+    cover_o = [[pos[l][(j + 1) // p ** l - 1] for l in range(L) if (j + 1) // p ** l - 1 >= 0] for j in tokens]
+    need = np.unique(np.array([a for c in cover_o for a in c if a >= 0], dtype=np.int64))
+    o_rows, _ = oracle.attention_rows(qt, kt, vt, need)
+    o_of = {int(a): o_rows[r] for r, a in enumerate(need)}
+    out_ref = np.array([sum((o_of[int(a)] for a in c if a >= 0), np.zeros(run.d)) for c in cover_o])
+    # gradients: dX_j = sum over l of p^-l dX_sub of entry (l, j / p^l) when gathered
+    dot = oracle.scatter_bwd(head_inputs(dout, h).astype(np.float64), lev, idx, p)
+
+    def pulled(rows_of, toks):
+        out = np.zeros((len(toks), run.d))
+        for r, j in enumerate(toks):
+            for l in range(L):
+                a = int(pos[l][j // p ** l])
+                if a >= 0:
+                    out[r] += rows_of[a] / float(p ** l)
+        return out
+    cover_g = np.unique(np.array([pos[l][j // p ** l] for j in tokens for l in range(L)], dtype=np.int64))
+    cover_g = cover_g[cover_g >= 0]
+    dq_rows = oracle.attention_bwd_query_rows(qt, kt, vt, dot, cover_g)
+    dq_ref = pulled({int(a): dq_rows[r] for r, a in enumerate(cover_g)}, tokens)
+    late = np.arange(N - last, N)
+    cover_l = np.unique(np.array([pos[l][j // p ** l] for j in late for l in range(L)], dtype=np.int64))
+    cover_l = cover_l[cover_l >= 0]
+    dk_rows, dv_rows = oracle.attention_bwd_key_rows(qt, kt, vt, dot, cover_l)
+    dk_ref = pulled({int(a): dk_rows[r] for r, a in enumerate(cover_l)}, late)
+    dv_ref = pulled({int(a): dv_rows[r] for r, a in enumerate(cover_l)}, late)
+    bf = run.dtype == torch.bfloat16
+    out = run.out[h].float().cpu().numpy()
+    dq, dk, dv = (g[h].float().cpu().numpy() for g in run.grads)
+    fails = Failures()
+    st = {}
+    fails.check(st, "out", out[tokens], out_ref, "%s head %d out" % (tag, h), stored_bf16=bf)
+    fails.check(st, "dq", dq[tokens], dq_ref, "%s head %d dq" % (tag, h), stored_bf16=bf, row_scaled=True)
+    fails.check(st, "dk", dk[late], dk_ref, "%s head %d dk" % (tag, h), stored_bf16=bf, row_scaled=True)
+    fails.check(st, "dv", dv[late], dv_ref, "%s head %d dv" % (tag, h), stored_bf16=bf)
+    say("  %s head %d (%d tokens, last %d; S = %d): %s" % (tag, h, len(tokens), last, S,
+                                                         "; ".join("%s %s" % (n, fmt_stats(x)) for n, x in st.items())))
+    fails.raise_if_any()
+    return st

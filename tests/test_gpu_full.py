@@ -75,3 +75,25 @@ def test_dense_512k_sampled_rows():
           "dv": assert_close(dv[keys], dv_ref, "dense dv", stored_bf16=True)}
     for n, s_ in st.items():
         say("  head %d %s (%d rows): %s" % (h, n, len(keys) if n in ("dk", "dv") else len(rows), fmt_stats(s_)))
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["sweep-512k-L3-p2-k6144", "sweep-512k-L5-p4-k1536", "sweep-512k-L5-p2-k1536"])
+def test_sweep_workload_sampled(name):
+    # shapes of the (L, p, k) sweep at 512K tokens, full size, as the sweep
+    # times them (S = 155648 and 57344 drop the dS tiles: dQ recomputes):
+    # selection bit-exact on every head; sampled tokens of one head
+    from synth_inputs import by_name
+    from parity import check_sampled_tokens, selection_ref
+    w = by_name(name)
+    say("workload %s: N=%d H=%d d=%d L=%d p=%d k=%d S=%d" % (w.name, w.N, w.H, w.d, w.L, w.p, w.k,
+                                                            oracle.subseq_len(w.N, w.L, w.p, w.k)))
+    q, k, v = make_qkv(w.N, w.H, w.d, w.dtype, w.n_plant, seed=0, device="cuda")
+    dout = make_dout(w.N, w.H, w.d, w.dtype, seed=1, device="cuda")
+    run = GpuRun(q, k, v, w.L, w.p, w.k, dout)
+    for h in range(w.H):
+        compare_selection(run, h, selection_ref(q, k, h, w.L, w.p, w.k))
+    say("  selection of all %d heads bit-exact" % w.H)
+    rng = np.random.default_rng(11)
+    tokens = np.concatenate([[0, 1, 2, 3, 1023, 1024, w.N // 2, w.N - 1], rng.integers(0, w.N, 24)])
+    check_sampled_tokens(run, q, k, v, dout, 9, tokens, last=8, tag=w.name)
