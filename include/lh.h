@@ -99,6 +99,18 @@ typedef enum {
     LH_F32 = 1
 } lh_dtype;
 
+/* The level-0 score, from nq = sqrt(||q_j||^2) and nk = sqrt(||k_j||^2) (both
+ * in the order and rounding stated above), combined in fp32. The pages rank
+ * entries by parameter-free query/key l2 norms of more than one kind
+ * (aitrends summary, 핵심 기여; techllm review, 한계와 주의할 점: the norm
+ * scorer's retrieval differs from the dense baseline's). */
+typedef enum {
+    LH_SCORE_SUM = 0,     /* nq + nk (lh_forward's score) */
+    LH_SCORE_PRODUCT = 1, /* nq * nk */
+    LH_SCORE_QUERY = 2,   /* nq */
+    LH_SCORE_KEY = 3      /* nk */
+} lh_scorer;
+
 /* Human-readable name of a status code (static storage). */
 const char *lh_strerror(lh_status s);
 
@@ -138,6 +150,15 @@ size_t lh_forward_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, 
 lh_status lh_forward(const void *q, const void *k, const void *v,
                      int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
                      void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lh_forward with the level-0 score chosen by `scorer` (LH_SCORE_*); the rest
+ * of the layer is the same, and so are the workspace and the context it
+ * leaves for lh_backward. LH_EINVAL for an unknown scorer.
+ */
+lh_status lh_forward_scored(const void *q, const void *k, const void *v,
+                            int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt, lh_scorer scorer,
+                            void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Backward pass with the indices of the preceding lh_forward held fixed

@@ -71,6 +71,9 @@ def _scorer():
         fn = lib.oracle_token_scores
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+        fn = lib.oracle_token_scores_v
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         _scorer_lib = lib
     return _scorer_lib
 
@@ -145,17 +148,30 @@ def row_norm2_f32(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def token_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
-    """Level-0 score s_j = sqrt(||q_j||^2) + sqrt(||k_j||^2), fp32.
+# Score variants, in the numbering the library's C ABI uses.
+SCORERS = ("sum", "product", "query", "key")
+
+
+def token_scores(q: np.ndarray, k: np.ndarray, scorer: str = "sum") -> np.ndarray:
+    """Level-0 score, fp32, from nq = sqrt(||q_j||^2) and nk = sqrt(||k_j||^2):
+    "sum" nq + nk (default), "product" nq * nk, "query" nq, "key" nk.
 
     [AIT, "기술 상세" item 2]: level 0 is scored by the l2 norms of Q_i and K_i;
-    [TLL, "어떻게 동작하나" step 2]: the score is parameter-free. Reading: the two
-    norms are added (the plainest single scalar built from both).
+    [TLL, "어떻게 동작하나" step 2]: the score is parameter-free; [AIT, "핵심
+    기여"]: the query/key scores are l2 norms of more than one kind ("QK and KQ
+    l2 norms, etc."). Reading: the default adds the two norms (the plainest
+    single scalar built from both); the variants are their product and either
+    norm alone.
     """
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     s = np.empty(q.shape[0], dtype=np.float32)
-    if _scorer().oracle_token_scores(q.ctypes.data, k.ctypes.data, q.shape[0], q.shape[1], s.ctypes.data):
+    if scorer == "sum":
+        rc = _scorer().oracle_token_scores(q.ctypes.data, k.ctypes.data, q.shape[0], q.shape[1], s.ctypes.data)
+    else:
+        rc = _scorer().oracle_token_scores_v(q.ctypes.data, k.ctypes.data, q.shape[0], q.shape[1],
+                                             SCORERS.index(scorer), s.ctypes.data)
+    if rc:
         raise ValueError("unsupported d=%d for the scorer" % q.shape[1])
     return s
 
@@ -295,17 +311,18 @@ def scatter(ot: np.ndarray, ent_level: np.ndarray, ent_index: np.ndarray, p: int
     return out
 
 
-def forward(q, k, v, L: int, p: int, kk: int, sel: dict | None = None) -> dict:
+def forward(q, k, v, L: int, p: int, kk: int, sel: dict | None = None, scorer: str = "sum") -> dict:
     """Whole layer for one head, with every intermediate.
 
     Steps in the pages' order [AIT, "방법론" and "기술 상세"]: pyramid pool,
     score and top-K, gathered-sequence attention, scatter-back. ``sel`` holds
     the selection fixed (the top-K is non-differentiable, so a caller may pass
-    the indices of an earlier call).
+    the indices of an earlier call); ``scorer`` names the score variant (see
+    token_scores).
     """
     N, d = q.shape
     check_shape(N, d, L, p, kk)
-    s0 = token_scores(q, k)
+    s0 = token_scores(q, k, scorer)
     scores = score_pyramid(s0, L, p)
     if sel is None:
         sel = select(scores, L, kk)

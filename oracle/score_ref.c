@@ -24,6 +24,16 @@
  * sqrt is the IEEE-754 correctly rounded single-precision square root, and
  * the two roots are added in fp32.
  *
+ * Variants of the score. The pages rank entries by parameter-free query/key
+ * l2 norms and name more than one combination ("QK and KQ l2 norms, etc.",
+ * aitrends summary, "핵심 기여"; a norm scorer whose retrieval differs,
+ * techllm review, "한계와 주의할 점"). From the same two correctly rounded
+ * roots nq = sqrt(||q||^2) and nk = sqrt(||k||^2), in fp32:
+ *   0 sum     nq + nk   (the default above)
+ *   1 product nq * nk
+ *   2 query   nq
+ *   3 key     nk
+ *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC (no -ffast-math,
  * so fmaf is a true fused multiply-add and no other operation is fused).
  */
@@ -80,6 +90,25 @@ int oracle_token_scores(const float *q, const float *k, int64_t n_rows, int d, f
         float nq = row_norm2(q + r * (int64_t)d, d);
         float nk = row_norm2(k + r * (int64_t)d, d);
         s[r] = sqrtf(nq) + sqrtf(nk);
+    }
+    return 0;
+}
+
+/* s[r] = the score of variant `scorer` (0 sum, 1 product, 2 query, 3 key) of
+ * row r. Returns 0, or -1 on a bad d or scorer. */
+int oracle_token_scores_v(const float *q, const float *k, int64_t n_rows, int d, int scorer, float *s)
+{
+    if (!shape_ok(d) || scorer < 0 || scorer > 3)
+        return -1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        float nq = sqrtf(row_norm2(q + r * (int64_t)d, d));
+        float nk = sqrtf(row_norm2(k + r * (int64_t)d, d));
+        switch (scorer) {
+        case 0: s[r] = nq + nk; break;
+        case 1: s[r] = nq * nk; break;
+        case 2: s[r] = nq; break;
+        default: s[r] = nk; break;
+        }
     }
     return 0;
 }

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "liblh.so")
 
 LH_OK, LH_EINVAL, LH_EWORKSPACE, LH_EUNSUPPORTED, LH_EHIP = range(5)
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+SCORERS = ("sum", "product", "query", "key")  # lh_scorer, in order
 REGIONS = ["scores", "sel", "slot", "ent", "qhi", "qlo", "khi", "klo", "v", "qhi_t", "khi_t", "v_t",
            "osub", "lse", "dosub", "dqsub", "dksub", "dvsub"]
 _REGION_DTYPE = {"scores": torch.float32, "sel": torch.int32, "slot": torch.int32, "ent": torch.int32,
@@ -58,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "lh_backward": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp]),
         "lh_forward_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
         "lh_forward_static": (i32, [vp, vp, vp] + shape + [vp, vp]),
+        "lh_forward_scored": (i32, [vp, vp, vp] + shape + [i32, vp, vp, sz, vp]),
         "lh_static_scratch_bytes": (sz, []),
         "lh_set_ds_tile_budget": (None, [sz]),
         "lh_ds_tile_budget": (sz, []),
@@ -143,8 +145,9 @@ def _check_ws(ws: torch.Tensor, ref: torch.Tensor) -> None:
 
 
 def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
-            out: torch.Tensor | None = None, stream=None, events=None):
-    """Lighthouse forward on [H, N, d] tensors; returns (out, ws)."""
+            out: torch.Tensor | None = None, stream=None, events=None, scorer: str = "sum"):
+    """Lighthouse forward on [H, N, d] tensors; returns (out, ws). `scorer`
+    picks the level-0 score ("sum", "product", "query", "key")."""
     N, H, d = _shape_of(q)
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
@@ -156,9 +159,15 @@ def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
     if out is None:
         out = torch.empty_like(q)
     _like(out, q, "out")
+    if scorer not in SCORERS:
+        raise ValueError("scorer must be one of %s" % (SCORERS,))
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, dt,
             out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
-    if events is None:
+    if scorer != "sum":
+        if events is not None:
+            raise ValueError("timed calls use the default scorer")
+        _check(lib().lh_forward_scored(*args[:10], SCORERS.index(scorer), *args[10:]), "lh_forward_scored")
+    elif events is None:
         _check(lib().lh_forward(*args), "lh_forward")
     else:
         _check(lib().lh_forward_timed(*args, events), "lh_forward_timed")

@@ -222,12 +222,14 @@ static const char *kBwdStages[] = {"scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "
 
 static lh_status forward_impl(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
                               int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, hipStream_t s,
-                              void *const *events)
+                              void *const *events, lh_scorer scorer = LH_SCORE_SUM)
 {
     Plan pl;
     lh_status st = make_plan(N, H, d, L, p, k_sel, dt, &pl);
     if (st != LH_OK)
         return st;
+    if ((int)scorer < LH_SCORE_SUM || (int)scorer > LH_SCORE_KEY)
+        return LH_EINVAL;
     if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LH_EINVAL;
     if ((st = check_ws(ws, ws_bytes, pl.fwd_total)) != LH_OK)
@@ -255,6 +257,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         for (int l = 0; l < kMaxLevels; ++l)
             fa.part_off[l] = pl.fpart_off[l];
         fa.H = H; fa.L = L; fa.log2p = pl.log2p; fa.LT = pl.LT;
+        fa.scorer = (int)scorer;
         if (launch_front(pl, fa, s) != hipSuccess)
             return LH_EHIP;
     }
@@ -611,6 +614,13 @@ lh_status lh_forward(const void *q, const void *k, const void *v, int64_t N, int
                      lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream)
 {
     return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+lh_status lh_forward_scored(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
+                            int k_sel, lh_dtype dt, lh_scorer scorer, void *out, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr, scorer);
 }
 
 lh_status lh_forward_static(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,

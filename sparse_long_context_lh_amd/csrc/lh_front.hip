@@ -1,9 +1,11 @@
 // Front pass of the Lighthouse layer: one streaming read of Q, K and V that
 // produces
 //   * the token scores s_j = sqrt(||q_j||^2) + sqrt(||k_j||^2) (fp32, fixed
-//     order; aitrends summary, 기술 상세 item 2) and their max-pooled values at
-//     every coarser level (same passage: coarser levels receive the score by
-//     max-pooling);
+//     order; aitrends summary, 기술 상세 item 2) — or a variant built from the
+//     same two roots (their product, either one alone; aitrends summary, 핵심
+//     기여: query/key l2-norm scores of more than one kind) — and their
+//     max-pooled values at every coarser level (same passage: coarser levels
+//     receive the score by max-pooling);
 //   * the average-pooled rows (aitrends summary, 기술 상세 item 1; techllm
 //     review, 어떻게 동작하나 step 1) of the levels the host chose to
 //     materialise, as fp32 means of an fp32 sum (no rounding to 16 bits, so
@@ -41,6 +43,19 @@ __device__ __forceinline__ float row_norm2(const float (&x)[8])
     for (int off = LANES / 2; off >= 1; off >>= 1)
         a = a + __shfl_xor(a, off, LANES);
     return a;
+}
+
+// The token score from the two squared norms: both roots correctly rounded,
+// then combined in fp32 as `scorer` says (uniform over the launch).
+__device__ __forceinline__ float token_score(int scorer, float nq2, float nk2)
+{
+    const float nq = sqrtf(nq2), nk = sqrtf(nk2);
+    switch (scorer) {
+    case LH_SCORE_PRODUCT: return nq * nk;
+    case LH_SCORE_QUERY: return nq;
+    case LH_SCORE_KEY: return nk;
+    default: return nq + nk;
+    }
 }
 
 constexpr int ipow(int b, int e) { return e == 0 ? 1 : b * ipow(b, e - 1); }
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         const float nq = row_norm2<LANES>(x);
         unraw(rk[r], x);
         const float nk = row_norm2<LANES>(x);
-        s[r] = sqrtf(nq) + sqrtf(nk);
+        s[r] = token_score(a.scorer, nq, nk);
     }
 
     // window sums of the run, tensor after tensor

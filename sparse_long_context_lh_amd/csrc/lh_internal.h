@@ -115,6 +115,7 @@ struct FrontArgs {
     int64_t part_rows;
     int64_t part_off[kMaxLevels];
     int H, L, log2p, LT;
+    int scorer; // lh_scorer
 };
 
 struct TopkArgs {

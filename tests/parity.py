@@ -105,10 +105,10 @@ class GpuRun:
     """One forward (and optionally backward) through the C ABI, with views of
     the intermediates it leaves in the workspace."""
 
-    def __init__(self, q, k, v, L, p, kk, dout=None):
+    def __init__(self, q, k, v, L, p, kk, dout=None, scorer="sum"):
         self.H, self.N, self.d = q.shape
         self.L, self.p, self.k, self.dtype = L, p, kk, q.dtype
-        self.out, self.ws = lh.forward(q, k, v, L, p, kk)
+        self.out, self.ws = lh.forward(q, k, v, L, p, kk, scorer=scorer)
         self.grads = None
         if dout is not None:
             self.grads = lh.backward(dout, L, p, kk, self.ws)
@@ -242,15 +242,15 @@ def compare_backward(run: GpuRun, h: int, ref: dict, gref: dict, tag: str = "",
     return stats
 
 
-def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag=""):
+def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum"):
     """Whole-path parity of one case on the listed heads (default: all)."""
-    run = GpuRun(q, k, v, L, p, kk, dout)
+    run = GpuRun(q, k, v, L, p, kk, dout, scorer=scorer)
     heads = range(run.H) if heads is None else heads
     out = {}
     fails = Failures()
     for h in heads:
         qh, kh, vh = head_inputs(q, h), head_inputs(k, h), head_inputs(v, h)
-        ref = oracle.forward(qh, kh, vh, L, p, kk)
+        ref = oracle.forward(qh, kh, vh, L, p, kk, scorer=scorer)
         compare_selection(run, h, ref)
         out[h] = compare_forward(run, h, ref, tag, fails)
         if dout is not None:

@@ -212,3 +212,12 @@ def test_ds_tile_budget_sizes_the_workspace(L):
     # the plan recomputes instead and the workspace is O(H S d)
     dense = L.lh_workspace_bytes(524288, 16, 128, 1, 2, 0, 0)
     assert 0 < dense < 200 << 30
+
+
+def test_scored_forward_rejects_unknown_scorer(L):
+    fake = 1 << 40
+    shape = (4096, 4, 64, 3, 2, 256, 0)
+    need = L.lh_workspace_bytes(*shape)
+    assert L.lh_forward_scored(fake, fake, fake, *shape, 4, fake, fake, need, None) == 1
+    assert L.lh_forward_scored(fake, fake, fake, *shape, -1, fake, fake, need, None) == 1
+    assert L.lh_forward_scored(fake, fake, fake, 4098, 4, 64, 3, 2, 256, 0, 1, fake, fake, need, None) == 1

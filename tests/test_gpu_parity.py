@@ -14,12 +14,12 @@ from synth_inputs import make_dout, make_qkv
 pytestmark = pytest.mark.gpu
 
 
-def _case(N, H, d, L, p, k, dtype=torch.bfloat16, n_plant=8, seed=0, bwd=False, heads=None, tag=""):
-    say("case %s: N=%d H=%d d=%d L=%d p=%d k=%d dtype=%s S=%d bwd=%s"
-        % (tag, N, H, d, L, p, k, dtype, oracle.subseq_len(N, L, p, k), bwd))
+def _case(N, H, d, L, p, k, dtype=torch.bfloat16, n_plant=8, seed=0, bwd=False, heads=None, tag="", scorer="sum"):
+    say("case %s: N=%d H=%d d=%d L=%d p=%d k=%d dtype=%s S=%d bwd=%s scorer=%s"
+        % (tag, N, H, d, L, p, k, dtype, oracle.subseq_len(N, L, p, k), bwd, scorer))
     q, kk, v = (x.cuda() for x in make_qkv(N, H, d, dtype, n_plant, seed))
     dout = make_dout(N, H, d, dtype, seed + 1).cuda() if bwd else None
-    return check_case(q, kk, v, L, p, k, dout, heads=heads, tag=tag)
+    return check_case(q, kk, v, L, p, k, dout, heads=heads, tag=tag, scorer=scorer)
 
 
 def test_sqrt_correctly_rounded_all_positive_floats():
@@ -249,3 +249,36 @@ def test_recomputed_dq_against_stored_tiles():
         err = np.abs(x.astype(np.float64) - y)
         assert np.all(err <= 2e-2 + 2.0 ** -7 * np.abs(x).max(axis=-1, keepdims=True))
         say("  head %d: dQ_sub recomputed vs stored tiles: max %.3g" % (h, err.max()))
+
+
+@pytest.mark.parametrize("scorer", ["product", "query", "key", "sum"])
+@pytest.mark.parametrize("N,H,d,L,p,k,dtype", [
+    (16384, 2, 128, 3, 2, 300, torch.bfloat16),   # level 1 in 4 strata
+    (32768, 2, 64, 4, 4, 100, torch.float32),
+])
+def test_scorer_variants(scorer, N, H, d, L, p, k, dtype):
+    # each score variant: scores at every level and the selection bit-exact,
+    # the whole layer (forward and backward) within tolerance
+    _case(N, H, d, L, p, k, dtype, n_plant=16, bwd=True, tag="score-" + scorer, scorer=scorer)
+
+
+def test_scorers_select_differently():
+    # the variants are really different rankings on these inputs (per-token
+    # scales shared by Q and K make them close, so K gets its own scale here)
+    N, H, d, L, p, k = 16384, 1, 128, 3, 2, 200
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 8, 51)
+    kk = (kk.float() * torch.exp(torch.randn(N, generator=torch.Generator().manual_seed(52)))[None, :, None]).to(
+        torch.bfloat16)
+    q, kk, v = q.cuda(), kk.cuda(), v.cuda()
+    sels = {}
+    for scorer in ("sum", "product", "query", "key"):
+        run = GpuRun(q, kk, v, L, p, k, scorer=scorer)
+        sels[scorer] = run.head("sel", 0).numpy().copy()
+        ref = oracle.forward(q[0].float().cpu().numpy(), kk[0].float().cpu().numpy(), v[0].float().cpu().numpy(),
+                             L, p, k, scorer=scorer)
+        for l in range(1, L):
+            assert np.array_equal(sels[scorer][l - 1], ref["sel"][l]), (scorer, l)
+    names = list(sels)
+    for i in range(len(names)):
+        for j in range(i + 1, len(names)):
+            assert not np.array_equal(sels[names[i]], sels[names[j]]), (names[i], names[j])

@@ -115,6 +115,37 @@ def test_scorer_hand_values():
             assert s[0] == np.float32(c["score_with_zero_key"])
 
 
+def test_scorer_variants_hand_values():
+    with open(os.path.join(GOLDEN, "scorer_cases.json")) as f:
+        cases = json.load(f)["variants"]["cases"]
+    for c in cases:
+        q = np.zeros((1, c["d"]), dtype=np.float32)
+        k = np.zeros((1, c["d"]), dtype=np.float32)
+        for col, val in c["q"].items():
+            q[0, int(col)] = val
+        for col, val in c["k"].items():
+            k[0, int(col)] = val
+        for name, want in c["scores"].items():
+            assert oracle.token_scores(q, k, name)[0] == np.float32(want), (c["name"], name)
+
+
+def test_scorer_variants_follow_the_roots():
+    # every variant combines the same two correctly rounded roots; the sum
+    # variant equals the default scorer bit for bit, and the variants order
+    # entries as their definitions do (query-only ignores K entirely)
+    q, k, _ = _inputs(512, 128, seed=21, n_plant=8, dtype=torch.float32)
+    nq = np.sqrt(oracle.row_norm2_f32(q))
+    nk = np.sqrt(oracle.row_norm2_f32(k))
+    assert np.array_equal(oracle.token_scores(q, k, "sum"), oracle.token_scores(q, k))
+    assert np.array_equal(oracle.token_scores(q, k, "sum"), (nq + nk).astype(np.float32))
+    assert np.array_equal(oracle.token_scores(q, k, "product"), (nq * nk).astype(np.float32))
+    assert np.array_equal(oracle.token_scores(q, k, "query"), nq)
+    assert np.array_equal(oracle.token_scores(q, k, "key"), nk)
+    assert np.array_equal(oracle.token_scores(q, np.zeros_like(k), "query"), nq)
+    with pytest.raises(ValueError):
+        oracle.token_scores(q, k, "bogus")
+
+
 def test_scorer_single_nonzero_exact():
     # one nonzero bf16 element per row: ||x||^2 = x^2 exactly, sqrt exact.
     rng = np.random.default_rng(2)
