@@ -220,6 +220,40 @@ lh_status lh_backward_timed(const void *dout,
                             void *const *events);
 
 /*
+ * The step on either side of the layer, for a training step (aitrends
+ * summary, 방법론 item 5: the gradients reach W_Q, W_K and W_V through
+ * scatter-back, the gather and the attention): the Q, K and V projections of
+ * an input x in, the layer's output out, and the backward to x and to the
+ * projection weights.
+ *   x      [N][d_model]       (dt), DEVICE, 16-byte aligned rows (d_model % 8 == 0)
+ *   w_qkv  [d_model][3 H d]   (dt) row-major, columns [Q head 0..H-1 | K heads | V heads]
+ *   out    [H][N][d]          (dt) = Lighthouse(x W_Q, x W_K, x W_V), as lh_forward
+ *   dout   [H][N][d]          (dt) dLoss/dout
+ *   dx     [N][d_model], dw_qkv [d_model][3 H d]  (dt) the gradients
+ * The projections are dense GEMMs run by rocBLAS with fp32 accumulation,
+ * atomics disallowed (reproducible), on a rocBLAS workspace inside ws; the
+ * projected rows are rounded once to dt and then run through lh_forward /
+ * lh_backward exactly as those entry points do. The first call on a device
+ * creates that device's rocBLAS handle (rocBLAS may allocate device memory
+ * when it creates a handle; every later call allocates nothing). ws holds the
+ * projected rows, the layer's workspace, the rocBLAS workspace and the
+ * gradients at the projected rows: lh_layer_workspace_bytes, 256-byte
+ * aligned, the same ws for the forward and its backward (which does not
+ * modify x, w_qkv or dout). After lh_layer_forward, ws begins with the
+ * projected rows, [3][H][N][d] in dt (Q, K, V), which lh_layer_backward
+ * overwrites; the layer's own workspace follows them at the next multiple of
+ * 256 bytes (the base for lh_selection and lh_region_info). Calls from several host threads are serialised
+ * around the rocBLAS handle. Errors as for lh_forward; LH_EUNSUPPORTED for
+ * d_model not a multiple of 8 or above 65536.
+ */
+size_t lh_layer_workspace_bytes(int64_t N, int H, int d, int d_model, int L, int p, int k, lh_dtype dt);
+lh_status lh_layer_forward(const void *x, const void *w_qkv, int64_t N, int H, int d, int d_model,
+                           int L, int p, int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream);
+lh_status lh_layer_backward(const void *x, const void *w_qkv, const void *dout, int64_t N, int H, int d,
+                            int d_model, int L, int p, int k_sel, lh_dtype dt, void *dx, void *dw_qkv,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Test hook: byte offset and size, inside ws, of one intermediate that
  * lh_forward / lh_backward leave there. Layouts (per head h, heads outermost):
  *   LH_R_SCORES  fp32  [H][sum_l n_l]  level-0 scores, then level 1, ... (n_l = N/p^l);

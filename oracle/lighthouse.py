@@ -460,3 +460,46 @@ def attention_bwd_key_rows(qt, kt, vt, dot, keys: np.ndarray) -> tuple[np.ndarra
         dv[seen] += P[keys[seen], None] * dot[a][None, :]
         dk[seen] += dS[keys[seen], None] * qt[a][None, :] / np.sqrt(d)
     return dk, dv
+
+
+
+# ----------------------------------------------------------------------------
+# the step on either side: the Q, K, V projections and their gradients
+# ----------------------------------------------------------------------------
+def project(x: np.ndarray, w: np.ndarray, H: int, d: int) -> np.ndarray:
+    """Projected rows [3][H][N][d] (Q, K, V) of x [N][d_model] by w [d_model][3 H d]
+    (columns: Q heads, K heads, V heads, d each), in fp64.
+
+    [AIT, "방법론" item 5]: the layer's Q, K and V come from the W_Q, W_K and
+    W_V projections, through which the gradients flow back.
+    """
+    N = x.shape[0]
+    y = x.astype(np.float64) @ w.astype(np.float64)            # [N][3 H d]
+    return y.reshape(N, 3, H, d).transpose(1, 2, 0, 3).copy()  # [3][H][N][d]
+
+
+def project_bwd(x: np.ndarray, w: np.ndarray, dqkv: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Gradients of project() given dLoss at its output dqkv [3][H][N][d]:
+    dx = dY W^T and dW = x^T dY with dY = dqkv as [N][3 H d]."""
+    _, H, N, d = dqkv.shape
+    dy = dqkv.transpose(2, 0, 1, 3).reshape(N, 3 * H * d)
+    return dy @ w.astype(np.float64).T, x.astype(np.float64).T @ dy
+
+
+def layer_forward(x, w, H: int, d: int, L: int, p: int, kk: int, qkv: np.ndarray | None = None) -> dict:
+    """Projections, then the layer head by head: out [H][N][d]. ``qkv`` uses
+    given projected rows instead of computing them (e.g. rows already
+    rounded to the caller's storage type)."""
+    qkv = project(x, w, H, d) if qkv is None else qkv
+    heads = [forward(qkv[0, h], qkv[1, h], qkv[2, h], L, p, kk) for h in range(H)]
+    return dict(qkv=qkv, heads=heads, out=np.stack([f["out"] for f in heads]))
+
+
+def layer_backward(fwd: dict, x, w, dout: np.ndarray, p: int) -> dict:
+    """dx and dW of the layer with its projections, indices held fixed:
+    the layer's backward head by head, then the projections' adjoint."""
+    H = len(fwd["heads"])
+    g = [backward(fwd["heads"][h], dout[h], p) for h in range(H)]
+    dqkv = np.stack([np.stack([gh[n] for gh in g]) for n in ("dq", "dk", "dv")])  # [3][H][N][d]
+    dx, dw = project_bwd(x, w, dqkv)
+    return dict(dqkv=dqkv, dx=dx, dw=dw)

@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         "lh_forward_scored": (i32, [vp, vp, vp] + shape + [i32, vp, vp, sz, vp]),
         "lh_static_scratch_bytes": (sz, []),
         "lh_set_ds_tile_budget": (None, [sz]),
+        "lh_layer_workspace_bytes": (sz, [i64, i32, i32, i32, i32, i32, i32, i32]),
+        "lh_layer_forward": (i32, [vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]),
+        "lh_layer_backward": (i32, [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
         "lh_ds_tile_budget": (sz, []),
         "lh_backward_timed": (i32, [vp] + shape + [vp, vp, vp, vp, sz, vp, vp]),
         "lh_stage_count": (i32, [i32]),
@@ -187,6 +190,56 @@ def forward_static(q, k, v, L: int, p: int, k_sel: int, out: torch.Tensor | None
     _check(lib().lh_forward_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, _dt(q.dtype),
                                    out.data_ptr(), _stream(stream)), "lh_forward_static")
     return out
+
+
+def layer_workspace_bytes(N, H, d, d_model, L, p, k, dtype) -> int:
+    return lib().lh_layer_workspace_bytes(N, H, d, d_model, L, p, k, _dt(dtype))
+
+
+def layer_forward(x, w_qkv, H: int, d: int, L: int, p: int, k_sel: int, ws=None, out=None, stream=None):
+    """Projections of x [N, d_model] by w_qkv [d_model, 3 H d], then the layer;
+    returns (out [H, N, d], ws)."""
+    if x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous [N, d_model] CUDA tensor")
+    N, dm = x.shape
+    if w_qkv.shape != (dm, 3 * H * d) or w_qkv.dtype != x.dtype or not w_qkv.is_contiguous():
+        raise ValueError("w_qkv must be a contiguous [d_model, 3 H d] tensor of x's dtype")
+    if ws is None:
+        n = layer_workspace_bytes(N, H, d, dm, L, p, k_sel, x.dtype)
+        if n == 0:
+            _check(check_shape(N, H, d, L, p, k_sel, x.dtype) or LH_EUNSUPPORTED, "layer workspace size")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _check_ws(ws, x)
+    if out is None:
+        out = torch.empty(H, N, d, dtype=x.dtype, device=x.device)
+    if out.shape != (H, N, d) or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous [H, N, d] tensor of x's dtype")
+    _check(lib().lh_layer_forward(x.data_ptr(), w_qkv.data_ptr(), N, H, d, dm, L, p, k_sel, _dt(x.dtype),
+                                  out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)), "lh_layer_forward")
+    return out, ws
+
+
+def layer_backward(x, w_qkv, dout, H: int, d: int, L: int, p: int, k_sel: int, ws, dx=None, dw=None, stream=None):
+    """dx [N, d_model] and dw [d_model, 3 H d] of the layer with its
+    projections (indices of the preceding layer_forward held fixed)."""
+    N, dm = x.shape
+    if dout.shape != (H, N, d) or dout.dtype != x.dtype or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous [H, N, d] tensor of x's dtype")
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w_qkv) if dw is None else dw
+    _like(dx, x, "dx")
+    _like(dw, w_qkv, "dw")
+    _check_ws(ws, x)
+    _check(lib().lh_layer_backward(x.data_ptr(), w_qkv.data_ptr(), dout.data_ptr(), N, H, d, dm, L, p, k_sel,
+                                   _dt(x.dtype), dx.data_ptr(), dw.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream(stream)), "lh_layer_backward")
+    return dx, dw
+
+
+def layer_qkv(ws: torch.Tensor, N: int, H: int, d: int, dtype) -> torch.Tensor:
+    """The projected rows [3, H, N, d] lh_layer_forward leaves at the start of ws."""
+    nb = 3 * H * N * d * (2 if dtype == torch.bfloat16 else 4)
+    return ws[:nb].view(dtype).view(3, H, N, d)
 
 
 def set_ds_tile_budget(nbytes: int) -> None:

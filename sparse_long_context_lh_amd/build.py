@@ -18,7 +18,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblh.so")
-SOURCES = ["lh_api.hip", "lh_front.hip", "lh_select.hip", "lh_gather.hip", "lh_attn.hip", "lh_scatter.hip"]
+SOURCES = ["lh_api.hip", "lh_front.hip", "lh_select.hip", "lh_gather.hip", "lh_attn.hip", "lh_scatter.hip",
+           "lh_layer.hip"]
+# rocBLAS runs the projection GEMMs of the step around the layer (lh_layer.hip)
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -64,7 +67,7 @@ def build_library(jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "--offload-arch=gfx950", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", "--offload-arch=gfx950", *objs, *LIBS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))

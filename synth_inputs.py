@@ -116,3 +116,21 @@ def make_workload(w: Workload, seed: int = 0, device: str = "cpu", N: int | None
     h = w.H if H is None else H
     q, k, v = make_qkv(n, h, w.d, w.dtype, min(w.n_plant, n), seed, device)
     return q, k, v
+
+
+def make_layer_inputs(N: int, d_model: int, H: int, d: int, dtype=torch.bfloat16, n_plant: int = 0, seed: int = 0,
+                      device: str = "cpu"):
+    """The input x [N, d_model] and projection weights W [d_model, 3 H d] of
+    the layer with its projections: x as the Q/K/V recipe above (per-token
+    LogNormal(0, 0.5) scale, n_plant tokens at scale 4), W ~ N(0, 1/d_model)
+    so the projected rows have about unit variance; W from seed + 2."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    scale = torch.exp(0.5 * torch.randn(N, generator=g, device=device, dtype=torch.float32))
+    if n_plant:
+        pos = torch.randperm(N, generator=g, device=device)[:n_plant]
+        scale[pos] = 4.0
+    x = (torch.randn(N, d_model, generator=g, device=device, dtype=torch.float32) * scale[:, None]).to(dtype)
+    gw = torch.Generator(device=device).manual_seed(seed + 2)
+    w = (torch.randn(d_model, 3 * H * d, generator=gw, device=device, dtype=torch.float32)
+         / d_model ** 0.5).to(dtype)
+    return x, w

@@ -282,3 +282,55 @@ def test_scorers_select_differently():
     for i in range(len(names)):
         for j in range(i + 1, len(names)):
             assert not np.array_equal(sels[names[i]], sels[names[j]]), (names[i], names[j])
+
+
+
+@pytest.mark.parametrize("N,H,d,dm,L,p,k,dtype", [
+    (8192, 2, 128, 256, 3, 4, 50, torch.bfloat16),
+    (4096, 2, 64, 96, 3, 2, 100, torch.float32),
+    (1000, 2, 64, 64, 1, 2, 0, torch.bfloat16),    # dense, ragged
+])
+def test_layer_with_projections(N, H, d, dm, L, p, k, dtype):
+    # the step around the layer: projections in (rocBLAS GEMMs), the layer,
+    # and the backward to x and W. The projected rows equal x W to within
+    # their rounding to the storage type; from those rows on, the oracle runs
+    # the layer (selection bit-exact, outputs within tolerance) and its
+    # backward, then the projections' adjoint in fp64.
+    from parity import Failures, assert_close, compare_selection, fmt_stats
+    from synth_inputs import make_layer_inputs
+    say("case layer: N=%d H=%d d=%d d_model=%d L=%d p=%d k=%d dtype=%s" % (N, H, d, dm, L, p, k, dtype))
+    x, w = make_layer_inputs(N, dm, H, d, dtype, n_plant=8, seed=61)
+    dout = make_dout(N, H, d, dtype, 62)
+    xc, wc, dc = x.cuda(), w.cuda(), dout.cuda()
+    out, ws = lh.layer_forward(xc, wc, H, d, L, p, k)
+    qkv = lh.layer_qkv(ws, N, H, d, dtype).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    xd, wd = x.double().numpy(), w.double().numpy()
+    ref_qkv = oracle.project(xd, wd, H, d)
+    # one rounding to the storage type (at most an ulp, whatever the GEMM's
+    # rounding mode) plus fp32 accumulation over d_model terms
+    ulp = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -23
+    acc = oracle.project(np.abs(xd), np.abs(wd), H, d)
+    ratio = np.abs(qkv - ref_qkv) / (ulp * np.abs(ref_qkv) + 2.0 ** -20 * acc)
+    say("  projections: max |g - r| %.3g, worst fraction of the bound %.3g" % (np.abs(qkv - ref_qkv).max(),
+                                                                          ratio.max()))
+    assert ratio.max() <= 1.0
+    fwd = oracle.layer_forward(xd, wd, H, d, L, p, k, qkv=qkv)
+    bf = dtype == torch.bfloat16
+    fails = Failures()
+    st = {}
+    # the layer's own workspace follows the projected rows (next 256 bytes)
+    lh_ws = ws[(3 * H * N * d * (2 if bf else 4) + 255) // 256 * 256:]
+    for h in range(H):
+        for l in range(1, L):
+            got = lh.selection(lh_ws, N, H, d, L, p, k, l)[h].cpu().numpy()
+            assert np.array_equal(got, fwd["heads"][h]["sel"][l]), (h, l)
+        fails.check(st, "out%d" % h, out[h].float().cpu().numpy(), fwd["out"][h], "layer head %d out" % h,
+                    stored_bf16=bf)
+    dx, dw = lh.layer_backward(xc, wc, dc, H, d, L, p, k, ws)
+    torch.cuda.synchronize()
+    g = oracle.layer_backward(fwd, xd, wd, dout.double().numpy(), p)
+    fails.check(st, "dx", dx.float().cpu().numpy(), g["dx"], "layer dx", stored_bf16=bf, row_scaled=True)
+    fails.check(st, "dw", dw.float().cpu().numpy(), g["dw"], "layer dw", stored_bf16=bf, row_scaled=True)
+    say("  layer: " + "; ".join("%s %s" % (n, fmt_stats(x_)) for n, x_ in st.items()))
+    fails.raise_if_any()

@@ -367,6 +367,60 @@ def test_backward_rows_match_full():
     assert np.allclose(dv2, dv[keys], rtol=1e-10, atol=1e-12)
 
 
+def test_projection_adjoint_against_autograd():
+    # project() and project_bwd() against torch's fp64 autograd of x @ w
+    rng = np.random.default_rng(22)
+    N, dm, H, d = 40, 24, 2, 8
+    x = rng.standard_normal((N, dm))
+    w = rng.standard_normal((dm, 3 * H * d))
+    tx = torch.tensor(x, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    y = tx @ tw
+    qkv = oracle.project(x, w, H, d)
+    for t in range(3):
+        for h in range(H):
+            assert np.allclose(qkv[t, h], y[:, (t * H + h) * d:(t * H + h + 1) * d].detach().numpy(), rtol=1e-13)
+    dqkv = rng.standard_normal((3, H, N, d))
+    dy = torch.tensor(np.concatenate([dqkv[t, h] for t in range(3) for h in range(H)], axis=1))
+    y.backward(dy)
+    dx, dw = oracle.project_bwd(x, w, dqkv)
+    assert np.allclose(dx, tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dw, tw.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_layer_with_projections_finite_differences():
+    # the whole step (projections, layer) with the selection held fixed:
+    # central differences of sum(out * dout) in x and in W
+    rng = np.random.default_rng(23)
+    N, dm, H, d, L, p, k = 32, 16, 2, 16, 3, 2, 2
+    x = rng.standard_normal((N, dm))
+    w = rng.standard_normal((dm, 3 * H * d)) / 4.0
+    base = oracle.layer_forward(x, w, H, d, L, p, k)
+    sels = [f["sel"] for f in base["heads"]]
+    dout = rng.standard_normal((H, N, d))
+    g = oracle.layer_backward(base, x, w, dout, p)
+
+    def loss(xx, ww):
+        qkv = oracle.project(xx, ww, H, d)
+        out = np.stack([oracle.forward(qkv[0, h], qkv[1, h], qkv[2, h], L, p, k, sel=sels[h])["out"]
+                        for h in range(H)])
+        return float(np.sum(out * dout))
+    eps = 1e-6
+    for _ in range(8):
+        r, c = int(rng.integers(N)), int(rng.integers(dm))
+        xp, xm = x.copy(), x.copy()
+        xp[r, c] += eps
+        xm[r, c] -= eps
+        fd = (loss(xp, w) - loss(xm, w)) / (2 * eps)
+        assert abs(fd - g["dx"][r, c]) <= 1e-6 * max(1.0, abs(fd))
+        r, c = int(rng.integers(dm)), int(rng.integers(3 * H * d))
+        wp, wm = w.copy(), w.copy()
+        wp[r, c] += eps
+        wm[r, c] -= eps
+        fd = (loss(x, wp) - loss(x, wm)) / (2 * eps)
+        assert abs(fd - g["dw"][r, c]) <= 1e-6 * max(1.0, abs(fd))
+
+
 def test_shape_rules():
     with pytest.raises(ValueError):
         oracle.check_shape(102, 64, 3, 2, 4)       # N not a multiple of p^(L-1)
