@@ -54,7 +54,15 @@
  *     atomics anywhere on the layer's path (the top-K's digit histograms and
  *     two per-tile maxima use LDS integer atomics, whose results do not depend
  *     on their order). Calls on distinct workspaces may run concurrently.
- *   - Inputs must be finite.
+ *   - Inputs must be finite, and so must the logits: |q.k| / sqrt(d) below
+ *     2^23 (the softmax keeps its fp32 logits to within one unit, so larger
+ *     ones round by more than the probabilities' fp16 range allows).
+ *
+ * Range. Rows staged in fp16 for the attention (the gathered Q, K, V and
+ * dO_sub) carry one power-of-two scale per head and tensor, chosen from the
+ * head's largest values, and every result is scaled back exactly; inputs and
+ * gradients may use bf16's whole range (pooled rows and gradient sums are
+ * fp32).
  *
  * Precision. Scores are fp32 in the stated order (bit-exact by design).
  * Pooling sums in fp32. The attention runs on fp16 matrix cores with fp32
@@ -65,10 +73,7 @@
  * fp8 (e4m3) copies with one power-of-two scale per head; P, V, dS and the
  * fp16 hi/lo pair of dO_sub
  * feed the other products; row statistics, Delta = rowsum(dO_sub * O_sub) and
- * all sums are fp32. Consequently every input, pooled row, scattered-back
- * gradient sum and attention intermediate must stay within the fp16 range
- * (|x| < 65504); a larger value overflows to inf and shows as a non-finite
- * output. Outputs are rounded once to the input dtype.
+ * all sums are fp32. Outputs are rounded once to the input dtype.
  *
  * Supported shapes: d in {64, 128}; p in {2, 4, 8}; 1 <= L <= 8;
  * 1 <= N <= 2^27, N a multiple of p^(L-1); 1 <= H <= 65535; 0 <= k <= N/p^(L-1);
@@ -272,6 +277,11 @@ lh_status lh_layer_backward(const void *x, const void *w_qkv, const void *dout, 
  *                                      (the natural-log value times log2(e))
  *   LH_R_DOSUB   fp32  [H][S_pad][d]   gradient at the sub-sequence output
  *   LH_R_DQSUB/DKSUB/DVSUB fp32 [H][S_pad][d]  gradients at the gathered rows
+ *   LH_R_EXP     int32 [4][H]          exponents e of the per-head power-of-two
+ *                                      scales 2^e the fp16 rows above are staged
+ *                                      with: Q, K and V (the gathered rows are
+ *                                      2^e times the pooled rows), dO_sub (its
+ *                                      fp16 copy, set by lh_backward)
  * S_pad = S rounded up to a multiple of 256. Returns LH_EINVAL for a bad shape
  * or region id.
  */
@@ -279,7 +289,7 @@ typedef enum {
     LH_R_SCORES = 0, LH_R_SEL, LH_R_SLOT, LH_R_ENT,
     LH_R_QHI, LH_R_QLO, LH_R_KHI, LH_R_KLO, LH_R_V,
     LH_R_QHI_T, LH_R_KHI_T, LH_R_V_T,
-    LH_R_OSUB, LH_R_LSE, LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB,
+    LH_R_OSUB, LH_R_LSE, LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, LH_R_EXP,
     LH_R_COUNT
 } lh_region;
 lh_status lh_region_info(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt,

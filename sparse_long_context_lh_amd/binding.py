@@ -18,12 +18,12 @@ LH_OK, LH_EINVAL, LH_EWORKSPACE, LH_EUNSUPPORTED, LH_EHIP = range(5)
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 SCORERS = ("sum", "product", "query", "key")  # lh_scorer, in order
 REGIONS = ["scores", "sel", "slot", "ent", "qhi", "qlo", "khi", "klo", "v", "qhi_t", "khi_t", "v_t",
-           "osub", "lse", "dosub", "dqsub", "dksub", "dvsub"]
+           "osub", "lse", "dosub", "dqsub", "dksub", "dvsub", "exp"]
 _REGION_DTYPE = {"scores": torch.float32, "sel": torch.int32, "slot": torch.int32, "ent": torch.int32,
                  "qhi": torch.float16, "qlo": torch.float16, "khi": torch.float16, "klo": torch.float16,
                  "v": torch.float16, "qhi_t": torch.float16, "khi_t": torch.float16, "v_t": torch.float16,
                  "osub": torch.float32, "lse": torch.float32, "dosub": torch.float32,
-                 "dqsub": torch.float32, "dksub": torch.float32, "dvsub": torch.float32}
+                 "dqsub": torch.float32, "dksub": torch.float32, "dvsub": torch.float32, "exp": torch.int32}
 
 _lib = None
 

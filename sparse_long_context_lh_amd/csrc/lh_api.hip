@@ -141,6 +141,11 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
         }
     }
 
+    // wave maxima of the inputs, for the per-head fp16 staging scales: four
+    // per front tile (L = 1: the same tiling, read by k_absmax)
+    pl->xmax_tile = tile_rows(d, log2p, front_nc(log2p));
+    pl->nxmax = (N + pl->xmax_tile - 1) / pl->xmax_tile * 4;
+
     // Region sizes. With H <= 2^16, S_pad * d <= 2^30 and N <= 2^27 every
     // product below stays under 2^50; the dS tiles are the one quadratic term
     // and are planned only up to kDsTileBudget bytes (above it the dQ kernel
@@ -169,14 +174,17 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_QLO8] = b[IR_K8] = b[IR_V8] = b[IR_DOLO8] = Hs * Sp * D;
     b[IR_TMAX] = 4 * 4 * Hs * (Sp / 32);
     b[IR_SC8] = 4 * 4 * Hs;
+    b[IR_XMAX] = 4 * 3 * Hs * (size_t)pl->nxmax;
+    b[LH_R_EXP] = 4 * 4 * Hs;
+    b[IR_DOMAX] = 4 * Hs * (Sp / kExpTile);
     // What lh_forward writes comes first (the context the backward reads and
     // the forward's own scratch), so a forward-only caller can pass a
     // workspace that ends there; the regions only lh_backward writes follow.
     static const int kFwdOrder[] = {LH_R_SCORES, LH_R_SEL, LH_R_SLOT, LH_R_ENT, LH_R_QHI, LH_R_QLO, LH_R_KHI,
                                     LH_R_KLO, LH_R_V, LH_R_QHI_T, LH_R_KHI_T, LH_R_V_T, LH_R_OSUB, LH_R_LSE,
-                                    IR_TMAX, IR_SC8, IR_QLO8, IR_K8, IR_POOLED, IR_FPART};
+                                    IR_TMAX, IR_SC8, LH_R_EXP, IR_QLO8, IR_K8, IR_POOLED, IR_FPART, IR_XMAX};
     static const int kBwdOrder[] = {LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, IR_DOHI, IR_DOLO, IR_DOHI_T,
-                                    IR_DELTA, IR_LSE15, IR_SPART, IR_V8, IR_DOLO8, IR_DST};
+                                    IR_DELTA, IR_LSE15, IR_SPART, IR_V8, IR_DOLO8, IR_DOMAX, IR_DST};
     static_assert(sizeof(kFwdOrder) / sizeof(int) + sizeof(kBwdOrder) / sizeof(int) == IR_COUNT,
                   "every region placed once");
     size_t off = 0;
@@ -258,7 +266,23 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
             fa.part_off[l] = pl.fpart_off[l];
         fa.H = H; fa.L = L; fa.log2p = pl.log2p; fa.LT = pl.LT;
         fa.scorer = (int)scorer;
+        fa.xmax = at<float>(ws, pl, IR_XMAX);
+        fa.nxmax = pl.nxmax;
         if (launch_front(pl, fa, s) != hipSuccess)
+            return LH_EHIP;
+    } else { // no front pass: the inputs' maxima on their own
+        AbsMaxArgs ma;
+        ma.x[0] = q; ma.x[1] = k; ma.x[2] = v;
+        ma.xmax = at<float>(ws, pl, IR_XMAX);
+        ma.N = N; ma.nxmax = pl.nxmax; ma.tile = pl.xmax_tile; ma.H = H;
+        if (launch_absmax(pl, ma, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    {
+        HeadExpArgs ea;
+        ea.m = at<float>(ws, pl, IR_XMAX); ea.count = pl.nxmax; ea.nt = 3; ea.H = H; ea.first = 0;
+        ea.ex = at<int32_t>(ws, pl, LH_R_EXP);
+        if (launch_head_exp(ea, s) != hipSuccess)
             return LH_EHIP;
     }
     record(events, 1, s);
@@ -309,6 +333,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.tmax[0] = at<float>(ws, pl, IR_TMAX);
         ga.tmax[1] = ga.tmax[0] + (int64_t)H * (pl.S_pad / 32);
         ga.tmax[2] = ga.tmax[1] + (int64_t)H * (pl.S_pad / 32);
+        ga.ex = at<int32_t>(ws, pl, LH_R_EXP);
         ga.N = N; ga.S = pl.S; ga.S_pad = pl.S_pad; ga.mat_rows = pl.mat_rows; ga.tensor_stride = tensor_stride;
         for (int l = 0; l < kMaxLevels; ++l) {
             ga.mat_off[l] = pl.mat_off[l];
@@ -346,6 +371,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         aa.sc8 = at<int32_t>(ws, pl, IR_SC8);
         aa.o = at<float>(ws, pl, LH_R_OSUB);
         aa.lse = at<float>(ws, pl, LH_R_LSE);
+        aa.ex = at<int32_t>(ws, pl, LH_R_EXP);
         aa.S = pl.S; aa.S_pad = pl.S_pad; aa.H = H;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
         if (launch_attn_fwd(pl, aa, s) != hipSuccess)
@@ -402,6 +428,18 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     }
     record(events, 1, s);
     {
+        // the per-head staging scale of dO_sub, from its tile maxima
+        RowMaxArgs ra;
+        ra.src = dosub; ra.dst = at<float>(ws, pl, IR_DOMAX); ra.S = pl.S; ra.S_pad = pl.S_pad;
+        if (launch_rowmax(pl, ra, s) != hipSuccess)
+            return LH_EHIP;
+        HeadExpArgs ea;
+        ea.m = ra.dst; ea.count = pl.S_pad / kExpTile; ea.nt = 1; ea.H = H; ea.first = 3;
+        ea.ex = at<int32_t>(ws, pl, LH_R_EXP);
+        if (launch_head_exp(ea, s) != hipSuccess)
+            return LH_EHIP;
+    }
+    {
         BwdPrepArgs a;
         a.dosub = dosub; a.osub = at<float>(ws, pl, LH_R_OSUB);
         a.dohi = at<uint16_t>(ws, pl, IR_DOHI); a.dolo = at<uint16_t>(ws, pl, IR_DOLO);
@@ -412,6 +450,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         float *tmax = at<float>(ws, pl, IR_TMAX);
         const int64_t ntile = (int64_t)H * (pl.S_pad / 32);
         a.tmax = pl.dt == LH_BF16 ? tmax + 3 * ntile : nullptr;
+        a.ex = at<int32_t>(ws, pl, LH_R_EXP);
         a.S = pl.S; a.S_pad = pl.S_pad; a.H = H;
         if (launch_bwd_prep(pl, a, s) != hipSuccess)
             return LH_EHIP;
@@ -455,6 +494,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.dv = at<float>(ws, pl, LH_R_DVSUB);
     ab.dst = pl.ds_tiles ? at<uint16_t>(ws, pl, IR_DST) : nullptr; // none: the dQ kernel recomputes S and dP
     ab.dst_head = dst_tiles(pl.S_pad) * 1024;
+    ab.ex = at<int32_t>(ws, pl, LH_R_EXP);
     ab.S = pl.S; ab.S_pad = pl.S_pad; ab.H = H;
     ab.scale = (float)(1.0 / sqrt((double)d));
     ab.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));

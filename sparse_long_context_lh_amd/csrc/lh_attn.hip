@@ -45,6 +45,11 @@
 // dQ kernel (one workgroup per 128 queries) so that no gradient needs atomics
 // and results are bitwise reproducible.
 //
+// Scale: the gathered rows arrive multiplied by per-head powers of two 2^ex
+// (Q, K, V) and dO_sub by 2^ex_do, so that they fit fp16 whatever the inputs'
+// scale: the logits' scale is divided by 2^(ex_q + ex_k), and every output
+// leaves divided by the scales of the operands that formed it (exact).
+//
 // Range: probabilities enter fp16 products multiplied by 2^15 (kPScale), so
 // the many tiny probabilities of a long, sharply peaked row do not underflow
 // fp16 (they would vanish from P.V but stay in the fp32 normaliser, and the
@@ -254,6 +259,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     const uint8_t *k8 = a.k8 + hS * D;
     const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
     constexpr int NM = D / 64; // fp8 products of the logits' lo part (bf16 inputs)
+    // the logits of the staged rows are 2^(ex_q + ex_k) times the true ones
+    const float scale_log2 = ldexpf(a.scale_log2, -(a.ex[h] + a.ex[a.H + h]));
 
     const int64_t kend = min(q0 + BM, a.S);
     const int nkb = (int)((kend + BN - 1) / BN);
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     // maximum is taken on st (a positive scale keeps the order, and rounding
     // is monotonic). Probabilities enter the products as 2^(y - m + 15).
     f32x16_t st = logits(slot(0));
-    float m = jl > 0 ? rowmax(st) * a.scale_log2 : -INFINITY;
+    float m = jl > 0 ? rowmax(st) * scale_log2 : -INFINITY;
 
     // Probabilities of block st relative to m: the fp16 pair of each run of 8
     // keys, and their sum added to lsum. The tile's 16 probabilities are
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         float pr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-            pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], a.scale_log2, -shift));
+            pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], scale_log2, -shift));
         split8_mix(pr, ph[0], pl[0]);
         split8_mix(pr + 8, ph[1], pl[1]);
         lsum += tile_sum(pr);
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         auto expo = [&](int v0, int v1) __attribute__((always_inline)) {
 #pragma unroll
             for (int v = v0; v < v1; ++v)
-                pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -shift));
+                pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], scale_log2, -shift));
         };
         constexpr int HS = NS / 2;
         f32x16_t sn = zero16();
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             o[t] = mfma32(vf[NT + t], ph[1], o[t]);
         float mn = m;
         if constexpr (!LAST)
-            mn = fmaxf(m, rowmax(sn) * a.scale_log2);
+            mn = fmaxf(m, rowmax(sn) * scale_log2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
                 if ((int)(kt0 - qw) + 16 * (v >> 3) + 8 * g + (v & 7) > c32)
                     st[v] = -INFINITY;
         }
-        rescale(fmaxf(m, rowmax(st) * a.scale_log2));
+        rescale(fmaxf(m, rowmax(st) * scale_log2));
         uint4 ph[2], pl[2];
         probs(st, ph, pl);
         accumulate(slot(j), ph, pl);
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         sync(j);
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float inv = 1.0f / ltot;
+    const float inv = ldexpf(1.0f / ltot, -a.ex[2 * a.H + h]); // the staged V is 2^ex_v V
     float *orow = a.o + (hS + qw + c32) * D;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -650,6 +657,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int key = kw + kappa(c32);
     const int S = (int)a.S, S_pad = (int)a.S_pad;
     const int64_t hS = (int64_t)h * S_pad;
+    // staged rows: q 2^ex_q, k 2^ex_k, v 2^ex_v, dO_sub 2^ex_do (delta arrives
+    // times 2^(ex_do + ex_v)); dS is then 2^(ex_do + ex_v) dS
+    const int exq = a.ex[h], exk = a.ex[a.H + h], exv = a.ex[2 * a.H + h], exd = a.ex[3 * a.H + h];
+    const float scale_log2 = ldexpf(a.scale_log2, -(exq + exk));
 
     // Per-lane byte offsets of this thread's chunks inside a stage's tiles
     // (the same for every stage; the stage only moves the uniform base).
@@ -884,7 +895,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float sv = ok(v0 + e) ? st[v0 + e] : -INFINITY; // masked: P = 0
-                    pr[v0 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -lq[e]));
+                    pr[v0 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, scale_log2, -lq[e]));
                 }
             }
             LH_FENCE;
@@ -974,16 +985,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     float *dk = a.dk + (hS + key) * D;
     float *dv = a.dv + (hS + key) * D;
+    const float sk = ldexpf(a.scale, -(exd + exv + exq)), sv = ldexpf(kPScaleInv, -exd);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int dim = 32 * t + 8 * i4 + 4 * g;
-            *reinterpret_cast<float4 *>(dk + dim) = make_float4(dkT[t][4 * i4] * a.scale, dkT[t][4 * i4 + 1] * a.scale,
-                                                                dkT[t][4 * i4 + 2] * a.scale, dkT[t][4 * i4 + 3] * a.scale);
+            *reinterpret_cast<float4 *>(dk + dim) = make_float4(dkT[t][4 * i4] * sk, dkT[t][4 * i4 + 1] * sk,
+                                                                dkT[t][4 * i4 + 2] * sk, dkT[t][4 * i4 + 3] * sk);
             *reinterpret_cast<float4 *>(dv + dim) =
-                make_float4(dvT[t][4 * i4] * kPScaleInv, dvT[t][4 * i4 + 1] * kPScaleInv,
-                            dvT[t][4 * i4 + 2] * kPScaleInv, dvT[t][4 * i4 + 3] * kPScaleInv);
+                make_float4(dvT[t][4 * i4] * sv, dvT[t][4 * i4 + 1] * sv, dvT[t][4 * i4 + 2] * sv, dvT[t][4 * i4 + 3] * sv);
         }
 }
 
@@ -1115,13 +1126,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
 
     const int64_t query = qw + c32;
     float *dq = a.dq + (hS + query) * D;
+    // the tiles hold 2^(ex_do + ex_v) dS, the staged keys 2^ex_k K
+    const float sq = ldexpf(a.scale, -(a.ex[3 * a.H + h] + a.ex[2 * a.H + h] + a.ex[a.H + h]));
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
             *reinterpret_cast<float4 *>(dq + 32 * t + 8 * i4 + 4 * g) =
-                make_float4(dqT[t][4 * i4] * a.scale, dqT[t][4 * i4 + 1] * a.scale, dqT[t][4 * i4 + 2] * a.scale,
-                            dqT[t][4 * i4 + 3] * a.scale);
+                make_float4(dqT[t][4 * i4] * sq, dqT[t][4 * i4 + 1] * sq, dqT[t][4 * i4 + 2] * sq, dqT[t][4 * i4 + 3] * sq);
 }
 
 // ============================================================== backward: dQ, recomputed
@@ -1242,6 +1254,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
         vs = a.sc8[2 * a.H + h];
         ds8 = a.sc8[3 * a.H + h];
     }
+    const int exq = a.ex[h], exk = a.ex[a.H + h], exv = a.ex[2 * a.H + h], exd = a.ex[3 * a.H + h];
+    const float scale_log2 = ldexpf(a.scale_log2, -(exq + exk)); // staged rows: see the dK/dV kernel
     const float lq = a.lse[hS + qw + c32];   // log2-domain LSE - 15 of this lane's query
     const float dq8 = a.delta[hS + qw + c32]; // delta * 2^-15
     // consume the loads here (see the forward kernel)
@@ -1300,7 +1314,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const bool ok = rel + 16 * (v >> 3) + 8 * g + (v & 7) <= c32;
-            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], a.scale_log2, -lq)) : 0.0f;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], scale_log2, -lq)) : 0.0f;
             ds[v] = pr * __builtin_fmaf(dp[v], kPScaleInv, -dq8);
         }
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
@@ -1311,13 +1325,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
         }
     }
     float *dqr = a.dq + qrow;
+    const float sq = ldexpf(a.scale, -(exd + exv + exk));
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
             *reinterpret_cast<float4 *>(dqr + 32 * t + 8 * i4 + 4 * g) =
-                make_float4(dq[t][4 * i4] * a.scale, dq[t][4 * i4 + 1] * a.scale, dq[t][4 * i4 + 2] * a.scale,
-                            dq[t][4 * i4 + 3] * a.scale);
+                make_float4(dq[t][4 * i4] * sq, dq[t][4 * i4 + 1] * sq, dq[t][4 * i4 + 2] * sq, dq[t][4 * i4 + 3] * sq);
 }
 
 template <int D>

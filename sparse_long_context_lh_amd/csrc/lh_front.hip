@@ -117,6 +117,38 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a)
         }
     }
 
+    // largest |q| and |k| element and largest v row norm of this wave's rows
+    // (the per-head fp16 staging scales of the gather are taken from them)
+    {
+        float mx[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float x[8];
+            unraw(rq[r], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx[0] = fmaxf(mx[0], fabsf(x[e]));
+            unraw(rk[r], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx[1] = fmaxf(mx[1], fabsf(x[e]));
+            unraw(rv[r], x);
+            mx[2] = fmaxf(mx[2], row_norm2<LANES>(x));
+        }
+        mx[2] = sqrtf(mx[2]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], o));
+        }
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                a.xmax[((int64_t)t * a.H + h) * a.nxmax + (int64_t)blockIdx.x * 4 + threadIdx.x / 64] = mx[t];
+        }
+    }
+
     // token scores, then their maxima over the run's windows
     float s[R];
 #pragma unroll
@@ -402,6 +434,112 @@ hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s)
     if (pl.d == 128)
         return pl.dt == LH_BF16 ? launch_front_p<128, LH_BF16>(pl, a, s) : launch_front_p<128, LH_F32>(pl, a, s);
     return pl.dt == LH_BF16 ? launch_front_p<64, LH_BF16>(pl, a, s) : launch_front_p<64, LH_F32>(pl, a, s);
+}
+
+// ---------------------------------------------------------------- fp16 staging scales
+// Largest |q| and |k| element and v row norm of each wave's rows when the
+// front pass does not run (L = 1), in the front pass's layout: tile T rows
+// per workgroup, one value per wave.
+template <int D, lh_dtype DT>
+__global__ __launch_bounds__(256) void k_absmax(AbsMaxArgs a)
+{
+    typedef typename Elem<DT>::T T;
+    constexpr int LANES = D / 8, G = 64 / LANES; // lane groups per wave
+    const int lane = threadIdx.x % LANES, wave = threadIdx.x / 64, gw = (threadIdx.x % 64) / LANES;
+    const int h = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * a.tile, rows = a.tile / 4; // each wave a quarter of the tile
+    float mx[3] = {0.0f, 0.0f, 0.0f};
+    for (int64_t r = r0 + wave * rows + gw; r < min(r0 + (wave + 1) * rows, a.N); r += G) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            Raw8<DT> raw;
+            ld_raw(reinterpret_cast<const T *>(a.x[t]) + ((int64_t)h * a.N + r) * D + lane * 8, raw);
+            float x[8];
+            unraw(raw, x);
+            if (t < 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    mx[t] = fmaxf(mx[t], fabsf(x[e]));
+            } else {
+                mx[2] = fmaxf(mx[2], row_norm2<LANES>(x));
+            }
+        }
+    }
+    mx[2] = sqrtf(mx[2]);
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            a.xmax[((int64_t)t * a.H + h) * a.nxmax + (int64_t)blockIdx.x * 4 + wave] = mx[t];
+    }
+}
+
+hipError_t launch_absmax(const Plan &pl, const AbsMaxArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(pl.nxmax / 4), (unsigned)pl.H);
+    if (pl.d == 128) {
+        if (pl.dt == LH_BF16)
+            hipLaunchKernelGGL((k_absmax<128, LH_BF16>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_absmax<128, LH_F32>), grid, dim3(256), 0, s, a);
+    } else {
+        if (pl.dt == LH_BF16)
+            hipLaunchKernelGGL((k_absmax<64, LH_BF16>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_absmax<64, LH_F32>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+// Exponent e of a head's staging scale 2^e: the head's largest magnitude m
+// times 2^e lies in [2^(t-1), 2^t) (frexp: m = f 2^E, f in [0.5, 1), so
+// e = t - E); 0 for a head that is all zeros. One workgroup per (head,
+// tensor), four independent maxima per thread so the loads stay in flight.
+__global__ __launch_bounds__(1024) void k_head_exp(HeadExpArgs a)
+{
+    __shared__ float s_m[16];
+    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    const float *m = a.m + ((int64_t)t * a.H + h) * a.count;
+    float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t i = tid;
+    for (; i + 3 * 1024 < a.count; i += 4 * 1024) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            x[u] = fmaxf(x[u], m[i + u * 1024]);
+    }
+    for (; i < a.count; i += 1024)
+        x[0] = fmaxf(x[0], m[i]);
+    float y = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        y = fmaxf(y, __shfl_xor(y, o));
+    if ((tid & 63) == 0)
+        s_m[tid >> 6] = y;
+    __syncthreads();
+    if (tid == 0) {
+        float mm = s_m[0];
+        for (int w = 1; w < 16; ++w)
+            mm = fmaxf(mm, s_m[w]);
+        int e = 0;
+        if (mm > 0.0f && mm <= 3.0e38f) {
+            int E;
+            frexpf(mm, &E);
+            e = kExpTarget[a.first + t] - E;
+            e = e < -96 ? -96 : (e > 96 ? 96 : e);
+        }
+        a.ex[(a.first + t) * a.H + h] = e;
+    }
+}
+
+hipError_t launch_head_exp(const HeadExpArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_head_exp, dim3((unsigned)a.H, (unsigned)a.nt), dim3(1024), 0, s, a);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- sqrt self-test

@@ -10,7 +10,9 @@
 // attention kernels read as MFMA operands: queries and keys as an fp16 pair
 // (hi = fp16(x), lo = fp16(x - hi)) so the logits keep about 22 bits of the
 // pooled value, values as one fp16; row-major [S_pad][d] and, through an LDS
-// tile, the hi parts transposed [d][S_pad]. Positions past S are zero.
+// tile, the hi parts transposed [d][S_pad]. Positions past S are zero. Every
+// row is staged times its head's power-of-two scale 2^ex (see kExpTarget), so
+// that no input scale overflows fp16; the attention kernels undo it.
 #include "lh_device.h"
 #include "lh_internal.h"
 
@@ -103,6 +105,10 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
         const int64_t off = ((int64_t)h * a.S_pad + s) * D + lane * 8;
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
+            const float sc = ldexpf(1.0f, a.ex[t * a.H + h]); // exact: a power of two
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x[t][e] *= sc;
             uint4 hi, lo;
             if (t < 2) {
                 split8_f16(x[t], hi, lo);

@@ -44,8 +44,21 @@ enum InternalRegion {
     IR_DOLO8,               // e4m3 [H][S_pad/32][32 d] (bf16 inputs): lo part of dO_sub, fp8 tiles
     IR_TMAX,                // fp32 [4][H][S_pad/32]: largest magnitude of each Q lo / K hi / V / dO lo tile
     IR_SC8,                 // int32 [4][H]: scale of a head's fp8 Q lo / K / V / dO lo tiles (127 + exponent)
+    IR_XMAX,                // fp32 [3][H][nxmax]: largest |q|, |k| element and |v| row norm of each wave's input rows
+    IR_DOMAX,               // fp32 [H][S_pad/64]: largest dO_sub row norm of each 64-row tile
     IR_COUNT
 };
+
+// Per-head power-of-two scales of the rows staged in fp16 (gathered Q, K, V;
+// dO_sub; LH_R_EXP): a head's largest Q or K element, and its largest V or
+// dO_sub row norm, is brought into [2^(t-1), 2^t) with t = kExpTarget[...],
+// so every value stays inside fp16's range whatever the inputs' scale.
+// Scaling by a power of two commutes with rounding, so away from fp16's
+// subnormals the products are the same up to that factor. The targets bound
+// |dP| = |dO_sub . V| <= 2^9 2^5 and |dS| = |P (dP - delta)| <= 2^15 (fp16
+// holds 65504); pooled rows are means, so the inputs' maxima bound them.
+constexpr int kExpTarget[4] = {12, 12, 5, 9}; // Q, K (element), V, dO_sub (row norm)
+constexpr int kExpTile = 64;                   // rows per tile of the dO_sub maxima
 
 // Row tiles of the front pass and of the scatter-back adjoint. A lane group
 // (d/8 lanes, 8 elements each) owns R = p^NC consecutive rows; a workgroup of
@@ -87,6 +100,8 @@ struct Plan {
     int64_t spart_n[kMaxLevels];   // u-space windows of level l kept in IR_SPART (l >= LT)
     int64_t spart_off[kMaxLevels];
     int64_t spart_rows;
+    int64_t xmax_tile;           // input rows per front tile (four wave maxima each)
+    int64_t nxmax;               // wave maxima per head and tensor
     bool ds_tiles;               // the dK/dV kernel stores dS tiles for the dQ kernel (else dQ recomputes)
     size_t off[IR_COUNT], bytes[IR_COUNT];
     size_t fwd_total;            // end of the regions lh_forward writes
@@ -116,6 +131,8 @@ struct FrontArgs {
     int64_t part_off[kMaxLevels];
     int H, L, log2p, LT;
     int scorer; // lh_scorer
+    float *xmax;     // IR_XMAX: largest |q|, |k|, |v| of each wave's rows, [3][H][nxmax]
+    int64_t nxmax;
 };
 
 struct TopkArgs {
@@ -148,6 +165,7 @@ struct GatherArgs {
     uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
     uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
     float *tmax[3];            // (bf16 inputs) per-tile maxima of the Q lo part, of K hi and of V
+    const int32_t *ex;         // LH_R_EXP: the rows are staged as x * 2^ex[t][h]
     int64_t N, S, S_pad, mat_rows, tensor_stride;
     int64_t mat_off[kMaxLevels];
     int64_t n[kMaxLevels];
@@ -169,6 +187,7 @@ struct AttnFwdArgs {
     const int32_t *sc8;                         // ... and their scales [2][H]
     float *o;                           // [H][S_pad][d]
     float *lse;                         // [H][S_pad]
+    const int32_t *ex;                  // LH_R_EXP: staged rows are q 2^ex_q, k 2^ex_k, v 2^ex_v
     int64_t S, S_pad;
     int H;
     float scale_log2; // log2(e) / sqrt(d)
@@ -184,6 +203,7 @@ struct AttnBwdArgs {
     float *dq, *dk, *dv;                             // [H][S_pad][d]
     uint16_t *dst;     // IR_DST: tile (qt, kt), kt <= qt, at (qt(qt+1)/2 + kt) * 1024 in a head's block
     int64_t dst_head;  // elements per head of IR_DST
+    const int32_t *ex; // LH_R_EXP: staged rows are the true rows times 2^ex (Q, K, V, dO_sub)
     int64_t S, S_pad;
     int H;
     float scale_log2; // log2(e) / sqrt(d)
@@ -218,8 +238,28 @@ struct BwdPrepArgs {
     const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
     float *lse15;              // [H][S_pad]: lse - 15
     float *tmax;               // bf16 inputs: [H][S_pad/32] maxima of the lo part's tiles (else null)
+    const int32_t *ex;         // LH_R_EXP: dO_sub is staged times 2^ex_do; delta is kept times 2^(ex_do + ex_v)
     int64_t S, S_pad;
     int H;
+};
+
+// Largest magnitudes and the per-head exponents of the fp16 staging.
+struct AbsMaxArgs {
+    const void *x[3];   // [H][N][d] inputs (L = 1: the front pass does not run)
+    float *xmax;        // [3][H][nxmax]
+    int64_t N, nxmax, tile;
+    int H;
+};
+struct RowMaxArgs {
+    const float *src;   // [H][S_pad][d] dO_sub
+    float *dst;         // [H][S_pad/64]
+    int64_t S, S_pad;
+};
+struct HeadExpArgs {
+    const float *m;     // [nt][H][count] maxima
+    int64_t count;
+    int nt, H, first;   // exponents go to ex[first + t][h]
+    int32_t *ex;        // [4][H]
 };
 
 struct PoolBwdArgs {
@@ -243,6 +283,9 @@ hipError_t launch_bwd_prep(const Plan &pl, const BwdPrepArgs &a, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_t s);
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s);
 hipError_t launch_pool_bwd(const Plan &pl, const PoolBwdArgs &a, hipStream_t s);
+hipError_t launch_absmax(const Plan &pl, const AbsMaxArgs &a, hipStream_t s);
+hipError_t launch_rowmax(const Plan &pl, const RowMaxArgs &a, hipStream_t s);
+hipError_t launch_head_exp(const HeadExpArgs &a, hipStream_t s);
 hipError_t launch_selftest_sqrt(uint32_t first, uint32_t count, uint32_t *mismatches, hipStream_t s);
 
 } // namespace lh

@@ -460,6 +460,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kPrepTile;
     const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
+    // dO_sub is staged times 2^ex_do; delta then is 2^ex_do delta, and it is
+    // kept times 2^(ex_v - 15) (as the dS products see V times 2^ex_v)
+    const float sdo = ldexpf(1.0f, a.ex[3 * a.H + h]);
+    const float sdelta = ldexpf(1.0f, a.ex[2 * a.H + h] - 15);
     if (threadIdx.x < kPrepTile / 32)
         s_amax[threadIdx.x] = 0u;
     __syncthreads();
@@ -470,6 +474,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         if (s < a.S) {
             load8(a.dosub + off, x);
             load8(a.osub + off, o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x[e] *= sdo;
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         for (int off2 = LANES / 2; off2 >= 1; off2 >>= 1)
             dot += __shfl_xor(dot, off2, LANES);
         if (lane == 0) {
-            a.delta[(int64_t)h * a.S_pad + s] = dot * (1.0f / 32768.0f);
+            a.delta[(int64_t)h * a.S_pad + s] = dot * sdelta;
             a.lse15[(int64_t)h * a.S_pad + s] = s < a.S ? a.lse[(int64_t)h * a.S_pad + s] - 15.0f : 0.0f;
         }
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
@@ -522,6 +529,51 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         *reinterpret_cast<uint4 *>(a.dohi_t + ((int64_t)h * D + dim) * a.S_pad + s0 + sc * 8) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
+}
+
+// Largest dO_sub row norm of each 64-row tile of a head (rows past S are
+// zero): the per-head staging scale of dO_sub is taken from them.
+template <int D>
+__global__ __launch_bounds__(256) void k_rowmax(RowMaxArgs a)
+{
+    constexpr int LANES = D / 8, NLG = 256 / LANES;
+    __shared__ float s_m[4];
+    const int h = blockIdx.y;
+    const int64_t s0 = (int64_t)blockIdx.x * kExpTile;
+    const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
+    float m = 0.0f;
+    for (int r = lg; r < kExpTile; r += NLG) {
+        if (s0 + r >= a.S)
+            break;
+        float x[8], n2 = 0.0f;
+        load8(a.src + (((int64_t)h * a.S_pad + s0 + r) * D + lane * 8), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            n2 = __builtin_fmaf(x[e], x[e], n2);
+#pragma unroll
+        for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
+            n2 += __shfl_xor(n2, o, LANES);
+        m = fmaxf(m, n2);
+    }
+    m = sqrtf(m);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0)
+        s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        a.dst[(int64_t)h * (a.S_pad / kExpTile) + blockIdx.x] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+}
+
+hipError_t launch_rowmax(const Plan &pl, const RowMaxArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(pl.S_pad / kExpTile), pl.H);
+    if (pl.d == 128)
+        hipLaunchKernelGGL((k_rowmax<128>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_rowmax<64>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_prep(const Plan &pl, const BwdPrepArgs &a, hipStream_t s)

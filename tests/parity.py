@@ -190,60 +190,73 @@ class Failures:
             raise AssertionError("%d comparison(s) failed:\n" % len(self.msgs) + "\n".join(self.msgs))
 
 
-def compare_forward(run: GpuRun, h: int, ref: dict, tag: str = "", fails: Failures | None = None) -> dict:
+def compare_forward(run: GpuRun, h: int, ref: dict, tag: str = "", fails: Failures | None = None,
+                    scale: dict | None = None) -> dict:
+    """``scale`` (per tensor name) multiplies the absolute term of the bound:
+    for inputs that are a unit-scale problem times known powers of two, whose
+    outputs are then that problem's outputs times known powers of two."""
     S = run.S
+    scale = scale or {}
     own = fails is None
     fails = Failures() if own else fails
     stats = {}
-    for pre, key in (("q", "qt"), ("k", "kt")):
+    # the gathered rows are staged times per-head powers of two (Q, K, V)
+    ex = run.region("exp").view(4, run.H)[:, h].cpu().numpy()
+    for t, (pre, key) in enumerate((("q", "qt"), ("k", "kt"))):
         hi = run.head(pre + "hi", h)[:S].double().numpy()
         lo = run.head(pre + "lo", h)[:S].double().numpy()
-        r = ref[key]
-        # 2^-22: a few quanta of the fp16 subnormal range, where lo of a small value lands
-        bad = np.abs(hi + lo - r) > 2.0 ** -18 * np.abs(r) + 2.0 ** -22
+        r = ref[key] * 2.0 ** int(ex[t])
+        # 2^-18 relative: the pair's 22 bits; 2^-22 (before the staging scale):
+        # the fp32 rounding of a pooled sum whose terms cancel, and the fp16
+        # subnormal quanta where the lo part of a small value lands
+        bad = np.abs(hi + lo - r) > 2.0 ** -18 * np.abs(r) + 2.0 ** (int(ex[t]) - 22)
         if bad.any():
             i, c = np.argwhere(bad)[0]
-            raise AssertionError("%s head %d: gathered %s rows: %d elements off, first [%d, %d] (level %d): "
-                                 "exact %r hi %r lo %r" % (tag, h, pre, bad.sum(), i, c, ref["ent_level"][i],
-                                                           r[i, c], hi[i, c], lo[i, c]))
+            raise AssertionError("%s head %d: gathered %s rows (staged times 2^%d): %d elements off, first [%d, %d] "
+                                 "(level %d): exact %r hi %r lo %r" % (tag, h, pre, int(ex[t]), bad.sum(), i, c,
+                                                                       ref["ent_level"][i], r[i, c], hi[i, c],
+                                                                       lo[i, c]))
         assert np.array_equal(run.head(pre + "hi_t", h)[:, :S].numpy(), run.head(pre + "hi", h)[:S].numpy().T)
     v = run.head("v", h)[:S].double().numpy()
-    assert np.all(np.abs(v - ref["vt"]) <= 2.0 ** -11 * np.abs(ref["vt"]) + 2.0 ** -24), \
-        "%s head %d: gathered v rows" % (tag, h)
+    vr = ref["vt"] * 2.0 ** int(ex[2])
+    assert np.all(np.abs(v - vr) <= 2.0 ** -11 * np.abs(vr) + 2.0 ** -24), "%s head %d: gathered v rows" % (tag, h)
     assert np.array_equal(run.head("v_t", h)[:, :S].numpy(), run.head("v", h)[:S].numpy().T)
     bf = run.dtype == torch.bfloat16
-    fails.check(stats, "osub", run.head("osub", h)[:S].numpy(), ref["ot"], "%s head %d O_sub" % (tag, h))
+    fails.check(stats, "osub", run.head("osub", h)[:S].numpy(), ref["ot"], "%s head %d O_sub" % (tag, h),
+                atol=ATOL * scale.get("out", 1.0))
     # the library keeps the log-sum-exp in the log2 domain
     fails.check(stats, "lse", run.head("lse", h)[:S].numpy(), ref["lse"] / np.log(2.0), "%s head %d LSE" % (tag, h))
     fails.check(stats, "out", run.out[h].float().cpu().numpy(), ref["out"], "%s head %d output" % (tag, h),
-                stored_bf16=bf)
+                stored_bf16=bf, atol=ATOL * scale.get("out", 1.0))
     if own:
         fails.raise_if_any()
     return stats
 
 
 def compare_backward(run: GpuRun, h: int, ref: dict, gref: dict, tag: str = "",
-                     fails: Failures | None = None) -> dict:
+                     fails: Failures | None = None, scale: dict | None = None) -> dict:
     S = run.S
+    scale = scale or {}
     own = fails is None
     fails = Failures() if own else fails
     stats = {}
     bf = run.dtype == torch.bfloat16
     fails.check(stats, "dosub", run.head("dosub", h)[:S].numpy(), gref["dot"], "%s head %d dO_sub" % (tag, h),
-                atol=1e-4, rtol=1e-5, mean_rel=1e-6)
+                atol=1e-4 * scale.get("dout", 1.0), rtol=1e-5, mean_rel=1e-6)
     for name, key in (("dqsub", "dqt"), ("dksub", "dkt"), ("dvsub", "dvt")):
         fails.check(stats, name, run.head(name, h)[:S].numpy(), gref[key], "%s head %d %s" % (tag, h, name),
-                    row_scaled=name in ROW_SCALED)
+                    row_scaled=name in ROW_SCALED, atol=ATOL * scale.get(name[:2], 1.0))
     for i, key in enumerate(("dq", "dk", "dv")):
         fails.check(stats, key, run.grads[i][h].float().cpu().numpy(), gref[key], "%s head %d %s" % (tag, h, key),
-                    stored_bf16=bf, row_scaled=key in ROW_SCALED)
+                    stored_bf16=bf, row_scaled=key in ROW_SCALED, atol=ATOL * scale.get(key, 1.0))
     if own:
         fails.raise_if_any()
     return stats
 
 
-def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum"):
-    """Whole-path parity of one case on the listed heads (default: all)."""
+def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum", scales=None):
+    """Whole-path parity of one case on the listed heads (default: all);
+    ``scales(h)`` gives head h's absolute-term factors (see compare_forward)."""
     run = GpuRun(q, k, v, L, p, kk, dout, scorer=scorer)
     heads = range(run.H) if heads is None else heads
     out = {}
@@ -252,10 +265,11 @@ def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum"):
         qh, kh, vh = head_inputs(q, h), head_inputs(k, h), head_inputs(v, h)
         ref = oracle.forward(qh, kh, vh, L, p, kk, scorer=scorer)
         compare_selection(run, h, ref)
-        out[h] = compare_forward(run, h, ref, tag, fails)
+        sc = scales(h) if scales is not None else None
+        out[h] = compare_forward(run, h, ref, tag, fails, scale=sc)
         if dout is not None:
             gref = oracle.backward(ref, head_inputs(dout, h), p)
-            out[h].update(compare_backward(run, h, ref, gref, tag, fails))
+            out[h].update(compare_backward(run, h, ref, gref, tag, fails, scale=sc))
         say("  %s head %d: %s" % (tag, h, "; ".join("%s %s" % (k2, fmt_stats(v2)) for k2, v2 in out[h].items())))
     fails.raise_if_any()
     return run, out

@@ -334,3 +334,28 @@ def test_layer_with_projections(N, H, d, dm, L, p, k, dtype):
     fails.check(st, "dw", dw.float().cpu().numpy(), g["dw"], "layer dw", stored_bf16=bf, row_scaled=True)
     say("  layer: " + "; ".join("%s %s" % (n, fmt_stats(x_)) for n, x_ in st.items()))
     fails.raise_if_any()
+
+
+@pytest.mark.parametrize("N,L,p,k", [(16384, 3, 4, 64), (1000, 1, 2, 0)])
+def test_heads_scaled_far_outside_fp16(N, L, p, k):
+    # head 0 has Q, V and dO times 2^12 and K times 2^-12, head 1 the reverse
+    # (powers of two: exact in bf16; the logits q.k are those of the seeded
+    # inputs). Without per-head staging scales the fp16 rows of head 0 (|q|,
+    # |v| up to 7e4, dO_sub sums beyond 1e6) would overflow and those of head 1
+    # (|q|, |v|, |dO| around 1e-4) would lose their low bits to fp16's
+    # subnormals. For any fixed selection such a head is the unit-scale
+    # problem with its outputs multiplied by powers of two: out and dv by f,
+    # dq by f_do f_v f_k = f, dk by f_do f_v f_q = f^3 (f = 2^12 or 2^-12);
+    # the bound's absolute term is carried over by the same factors.
+    H, d = 2, 128
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 8, 71)
+    dout = make_dout(N, H, d, torch.bfloat16, 72)
+    f = torch.tensor([2.0 ** 12, 2.0 ** -12]).view(H, 1, 1)
+    q, v, dout = ((x.float() * f).to(torch.bfloat16) for x in (q, v, dout))
+    kk = (kk.float() / f).to(torch.bfloat16)
+    say("case heads scaled by 2^12 and 2^-12: N=%d H=%d d=%d L=%d p=%d k=%d" % (N, H, d, L, p, k))
+
+    def factors(h):
+        fh = float(f[h])
+        return {"out": fh, "dout": fh, "dq": fh, "dv": fh, "dk": fh ** 3}
+    check_case(q.cuda(), kk.cuda(), v.cuda(), L, p, k, dout.cuda(), tag="scaled-2^12", scales=factors)
