@@ -21,7 +21,7 @@ constexpr int kMaxHeads = 65535; // heads run along the grid's y dimension
 // causal half of S x S per head, fp16). Above it the dQ kernel recomputes S
 // and dP from the gathered rows instead, and the workspace stays O(S d). The
 // process-wide value is set with lh_set_ds_tile_budget.
-constexpr size_t kDsTileBudgetDefault = size_t(8) << 30;
+constexpr size_t kDsTileBudgetDefault = size_t(16) << 30;
 size_t ds_tile_budget();
 // Largest workspace a plan may ask for (64 TiB): shapes beyond it are reported
 // as unsupported rather than sized.
