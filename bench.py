@@ -16,7 +16,10 @@ With the default workload the same JSON line also carries the rest of the
 metric's range ("workloads": 1M tokens forward + backward, 128K and 64K
 forward, each with its dominant stage's roofline) and dense causal attention
 over the same 512K tokens ("dense_512k": L = 1, S = N, one warmup and one
-timed step), with the layer's speedup over it, forward and forward+backward.
+timed step), with the layer's speedup over it, forward and forward+backward,
+and the step around the layer ("projection_layer_512k": Q/K/V projections of
+an input with d_model = 2048 in, the backward to the input and the weights;
+the projections' share is that step minus the layer's own).
 
 Per-kernel timing: the library records caller-created HIP events between its
 stages on the launch stream (lh_forward_timed / lh_backward_timed), so every
@@ -342,6 +345,50 @@ def summary(r, steps, warmup, backward):
     return d
 
 
+def measure_layer(lh, steps=3, warmup=1, d_model=2048):
+    """The step around the layer at the headline shape (N = 512K, H = 16,
+    d = 128, L = 5, p = 4, k = 512): Q/K/V projections of x [N, d_model] by
+    W [d_model, 3 H d] (rocBLAS), the layer, and the backward to x and W;
+    wall time of `steps` calls after `warmup`, bracketed by synchronisations."""
+    import torch
+    from synth_inputs import make_dout, make_layer_inputs, by_name
+    w = by_name("lh-fwdbwd-512k")
+    x, W = make_layer_inputs(w.N, d_model, w.H, w.d, w.dtype, w.n_plant, seed=0, device="cuda")
+    dout = make_dout(w.N, w.H, w.d, w.dtype, seed=1, device="cuda")
+    n = lh.layer_workspace_bytes(w.N, w.H, w.d, d_model, w.L, w.p, w.k, w.dtype)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(w.H, w.N, w.d, dtype=w.dtype, device="cuda")
+    dx, dW = torch.empty_like(x), torch.empty_like(W)
+
+    def fwd():
+        lh.layer_forward(x, W, w.H, w.d, w.L, w.p, w.k, ws=ws, out=out)
+
+    def bwd():
+        lh.layer_backward(x, W, dout, w.H, w.d, w.L, w.p, w.k, ws, dx=dx, dw=dW)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    t_f = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t_fb = (time.perf_counter() - t0) / steps
+    gemm_fwd = 2.0 * w.N * d_model * 3 * w.H * w.d  # x W
+    del ws, x, W, dout, out, dx, dW
+    return {"N": w.N, "H": w.H, "d": w.d, "d_model": d_model, "L": w.L, "p": w.p, "k": w.k, "steps": steps,
+            "warmup": warmup, "fwd_ms": round(t_f * 1e3, 3), "fwd_tokens_per_s": round(w.N / t_f, 1),
+            "fwdbwd_ms": round(t_fb * 1e3, 3), "fwdbwd_tokens_per_s": round(w.N / t_fb, 1),
+            "gemm_tflop_fwd": round(gemm_fwd / 1e12, 2), "gemm_tflop_fwdbwd": round(3 * gemm_fwd / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,6 +487,15 @@ def main():
         dense["speedup_fwd"] = round(r["fwd_ms"] / head["fwd_ms"], 2)
         dense["speedup_fwdbwd"] = round(r["ms_per_step"] / head["ms_per_step"], 2)
         res["dense_512k"] = dense
+        torch.cuda.empty_cache()
+        lay = measure_layer(lh)
+        # the projections' share: the step minus the layer's own step above
+        g_f = lay["fwd_ms"] - head["fwd_ms"]
+        g_fb = lay["fwdbwd_ms"] - head["ms_per_step"]
+        lay["gemm_ms_fwd"] = round(g_f, 3)
+        lay["gemm_ms_fwdbwd"] = round(g_fb, 3)
+        lay["gemm_tflops_fwdbwd"] = round(lay["gemm_tflop_fwdbwd"] / (g_fb / 1e3), 1) if g_fb > 0 else None
+        res["projection_layer_512k"] = lay
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 

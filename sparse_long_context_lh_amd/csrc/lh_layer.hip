@@ -9,8 +9,12 @@
 //
 // Layouts (row-major): x [N][d_model]; W [d_model][3 H d], columns
 // [Q heads 0..H-1 | K heads | V heads], d per head; the projected rows
-// [3][H][N][d] (one strided-batched GEMM writes them in the layer's layout);
-// out and dout [H][N][d]; dx [N][d_model]; dW like W.
+// [3][H][N][d] in the layer's layout; out and dout [H][N][d]; dx [N][d_model];
+// dW like W. Every GEMM is one large GEMM over all heads (Y = x W, dW =
+// x^T dY, dx = dY W^T with Y and dY as [N][3 H d]); a copy kernel moves rows
+// between [N][3 H d] and the layer's [3][H][N][d] (a strided-batched GEMM per
+// head block writing the layer's layout directly ran at 0.6 of these GEMMs'
+// rate).
 #include <string.h>
 
 #include <mutex>
@@ -84,11 +88,12 @@ static lh_status layer_plan(int64_t N, int H, int d, int dm, int L, int p, int k
 
 static rocblas_datatype blas_type(lh_dtype dt) { return dt == LH_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r; }
 
-// [3][H][N][d] -> [N][3 H d] (row n of the result is token n's gradient at
-// every projected column), 16 bytes per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void k_heads_to_rows(const T *__restrict__ src, T *__restrict__ dst, int64_t N,
-                                                        int HB, int d)
+// Rows between the layer's [3][H][N][d] ("heads") and [N][3 H d] ("rows",
+// row n is token n at every projected column), 16 bytes per thread in the
+// order of the rows layout (so one of the two sides is always contiguous).
+template <typename T, bool TO_ROWS>
+__global__ __launch_bounds__(256) void k_relayout(const T *__restrict__ src, T *__restrict__ dst, int64_t N, int HB,
+                                                  int d)
 {
     constexpr int V = 16 / sizeof(T);
     const int per_row = d / V; // 16-byte pieces of one head row
@@ -100,22 +105,32 @@ __global__ __launch_bounds__(256) void k_heads_to_rows(const T *__restrict__ src
     const int64_t rest = i / per_row;
     const int b = (int)(rest % HB); // head of the [3][H] block
     const int64_t n = rest / HB;
-    const uint4 val = *reinterpret_cast<const uint4 *>(src + ((int64_t)b * N + n) * d + c * V);
-    *reinterpret_cast<uint4 *>(dst + (n * HB + b) * d + c * V) = val;
+    const int64_t heads = ((int64_t)b * N + n) * d + c * V, rows = (n * HB + b) * d + c * V;
+    const uint4 val = *reinterpret_cast<const uint4 *>(src + (TO_ROWS ? heads : rows));
+    *reinterpret_cast<uint4 *>(dst + (TO_ROWS ? rows : heads)) = val;
 }
 
-static hipError_t launch_heads_to_rows(const void *src, void *dst, int64_t N, int HB, int d, lh_dtype dt,
-                                       hipStream_t s)
+static hipError_t launch_relayout(const void *src, void *dst, int64_t N, int HB, int d, lh_dtype dt, bool to_rows,
+                                  hipStream_t s)
 {
     const int V = dt == LH_BF16 ? 8 : 4;
     const int64_t total = N * HB * (d / V);
     const dim3 grid((unsigned)((total + 255) / 256));
-    if (dt == LH_BF16)
-        hipLaunchKernelGGL((k_heads_to_rows<uint16_t>), grid, dim3(256), 0, s, (const uint16_t *)src, (uint16_t *)dst,
-                           N, HB, d);
-    else
-        hipLaunchKernelGGL((k_heads_to_rows<float>), grid, dim3(256), 0, s, (const float *)src, (float *)dst, N, HB,
-                           d);
+    if (dt == LH_BF16) {
+        if (to_rows)
+            hipLaunchKernelGGL((k_relayout<uint16_t, true>), grid, dim3(256), 0, s, (const uint16_t *)src,
+                               (uint16_t *)dst, N, HB, d);
+        else
+            hipLaunchKernelGGL((k_relayout<uint16_t, false>), grid, dim3(256), 0, s, (const uint16_t *)src,
+                               (uint16_t *)dst, N, HB, d);
+    } else {
+        if (to_rows)
+            hipLaunchKernelGGL((k_relayout<float, true>), grid, dim3(256), 0, s, (const float *)src, (float *)dst,
+                               N, HB, d);
+        else
+            hipLaunchKernelGGL((k_relayout<float, false>), grid, dim3(256), 0, s, (const float *)src, (float *)dst,
+                               N, HB, d);
+    }
     return hipGetLastError();
 }
 
@@ -146,26 +161,26 @@ lh_status lh_layer_forward(const void *x, const void *w_qkv, int64_t N, int H, i
         return LH_EWORKSPACE;
     char *w = static_cast<char *>(ws);
     const hipStream_t s = (hipStream_t)stream;
+    const int HB = 3 * H;
     {
-        // [3H] x ([N][d] = x [N][dm] . W[:, b d .. b d + d)); column-major:
-        // C_b (d x N, ld d) = A_b (the d rows b d.. of W^T, ld 3Hd) . x^T (dm x N, ld dm)
+        // Y = x W as [N][3Hd] in the (still free) gradient region; column-major:
+        // Y^T (3Hd x N, ld 3Hd) = W^T (stored 3Hd x dm, ld 3Hd) . x^T (dm x N, ld dm)
         std::lock_guard<std::mutex> lock(g_blas_mu);
         rocblas_handle hb;
         if ((st = blas_handle(&hb)) != LH_OK)
             return st;
         const float one = 1.0f, zero = 0.0f;
-        const int HB = 3 * H;
         if (rocblas_set_stream(hb, s) != rocblas_status_success ||
             rocblas_set_workspace(hb, w + lp.blas_off, kBlasWorkspace) != rocblas_status_success)
             return LH_EHIP;
         const rocblas_datatype t = blas_type(dt);
-        if (rocblas_gemm_strided_batched_ex(hb, rocblas_operation_none, rocblas_operation_none, d, (int)N, d_model,
-                                            &one, w_qkv, t, HB * d, d, x, t, d_model, 0, &zero, w + lp.qkv_off, t, d,
-                                            (int64_t)N * d, w + lp.qkv_off, t, d, (int64_t)N * d, HB,
-                                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
-                                            0) != rocblas_status_success)
+        if (rocblas_gemm_ex(hb, rocblas_operation_none, rocblas_operation_none, HB * d, (int)N, d_model, &one, w_qkv,
+                            t, HB * d, x, t, d_model, &zero, w + lp.dqkv_off, t, HB * d, w + lp.dqkv_off, t, HB * d,
+                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
             return LH_EHIP;
     }
+    if (launch_relayout(w + lp.dqkv_off, w + lp.qkv_off, N, HB, d, dt, false, s) != hipSuccess)
+        return LH_EHIP;
     const size_t plane = (size_t)H * (size_t)N * (size_t)d * lp.elem;
     return lh_forward(w + lp.qkv_off, w + lp.qkv_off + plane, w + lp.qkv_off + 2 * plane, N, H, d, L, p, k_sel, dt,
                       out, w + lp.lh_off, lp.lh.total, stream);
@@ -194,7 +209,7 @@ lh_status lh_layer_backward(const void *x, const void *w_qkv, const void *dout, 
     const int HB = 3 * H;
     // the projected rows are no longer needed: their place takes the
     // gradients as rows of 3 H d columns, the operand of dx's single GEMM
-    if (launch_heads_to_rows(dqkv, w + lp.qkv_off, N, HB, d, dt, s) != hipSuccess)
+    if (launch_relayout(dqkv, w + lp.qkv_off, N, HB, d, dt, true, s) != hipSuccess)
         return LH_EHIP;
     std::lock_guard<std::mutex> lock(g_blas_mu);
     rocblas_handle hb;
@@ -205,12 +220,11 @@ lh_status lh_layer_backward(const void *x, const void *w_qkv, const void *dout, 
         rocblas_set_workspace(hb, w + lp.blas_off, kBlasWorkspace) != rocblas_status_success)
         return LH_EHIP;
     const rocblas_datatype t = blas_type(dt);
-    // dW[:, b d .. b d + d) = x^T . dX_b; column-major: C_b (d x dm, rows b d.. of
-    // dW^T, ld 3Hd) = dX_b (d x N, ld d) . x (N x dm: x^T stored dm x N, transposed)
-    if (rocblas_gemm_strided_batched_ex(hb, rocblas_operation_none, rocblas_operation_transpose, d, d_model, (int)N,
-                                        &one, dqkv, t, d, (int64_t)N * d, x, t, d_model, 0, &zero, dw_qkv, t, HB * d,
-                                        d, dw_qkv, t, HB * d, d, HB, rocblas_datatype_f32_r,
-                                        rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
+    // dW = x^T dY; column-major: dW^T (3Hd x dm, ld 3Hd) = dY^T (3Hd x N, ld 3Hd)
+    // . x (N x dm: x^T stored dm x N, transposed)
+    if (rocblas_gemm_ex(hb, rocblas_operation_none, rocblas_operation_transpose, HB * d, d_model, (int)N, &one,
+                        w + lp.qkv_off, t, HB * d, x, t, d_model, &zero, dw_qkv, t, HB * d, dw_qkv, t, HB * d,
+                        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
         return LH_EHIP;
     // dx = dX_rows [N][3Hd] . W^T; column-major: dx^T (dm x N, ld dm) =
     // W^T^T (W^T stored 3Hd x dm, transposed) . dX_rows^T (3Hd x N, ld 3Hd)
