@@ -55,16 +55,17 @@ MFMA_STAGES = {"attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"}
 
 # rocprofv3 kernel names -> stages of the path
 KERNEL_STAGES = [
-    (r"lh::k_front(_up)?<", "front"),
+    (r"lh::k_(front(_up)?|absmax)<", "front"),
+    (r"lh::k_head_exp\(", "head_exp"),      # once in the forward, once in the backward
     (r"lh::k_topk\(", "topk"),
     (r"lh::k_index\(", "index"),
     (r"lh::k_(gather<|lo8<\d+, 0>)", "gather"),
     (r"lh::k_attn_fwd<", "attn_fwd"),
     (r"lh::k_pull<\d+, [^,]+, 1, 1,", "scatter"),
     (r"lh::k_scatter_bwd(_up)?<", "scatter_bwd"),
-    (r"lh::k_(bwd_prep<|lo8<\d+, 1>)", "bwd_prep"),
+    (r"lh::k_(bwd_prep<|rowmax<|lo8<\d+, 1>)", "bwd_prep"),
     (r"lh::k_attn_bwd_dkdv<", "attn_bwd_dkdv"),
-    (r"lh::k_attn_bwd_dq<", "attn_bwd_dq"),
+    (r"lh::k_attn_bwd_dq(_rc)?<", "attn_bwd_dq"),
     (r"lh::k_pull<\d+, [^,]+, 3, 0,", "pool_bwd"),
 ]
 CALIB_BYTES = 1 << 30        # the calibration kernel reads and writes this many bytes
@@ -262,10 +263,11 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
             f.write("\n")
 
 
-def measure(lh, hip, w0, steps, warmup, backward=True):
+def measure(lh, hip, w0, steps, warmup, backward=True, nograd=False):
     """Time `steps` calls of the layer on workload w0 (forward + backward, or
-    forward alone) after `warmup` untimed ones; per-stage times from the HIP
-    events the library records between its kernels on the launch stream."""
+    forward alone; nograd: lh_forward_nograd, the forward no backward follows)
+    after `warmup` untimed ones; per-stage times from the HIP events the
+    library records between its kernels on the launch stream."""
     import torch
     from synth_inputs import make_dout, make_qkv
 
@@ -282,8 +284,11 @@ def measure(lh, hip, w0, steps, warmup, backward=True):
     grads = tuple(torch.empty_like(q) for _ in range(3)) if backward else None
     stream = torch.cuda.current_stream()
 
+    assert not (backward and nograd)
+    fwd = lh.forward_nograd if nograd else lh.forward
+
     def step(evf=None, evb=None):
-        lh.forward(q, k, v, w.L, w.p, w.k, ws=ws, out=out, stream=stream, events=evf)
+        fwd(q, k, v, w.L, w.p, w.k, ws=ws, out=out, stream=stream, events=evf)
         if backward:
             lh.backward(dout, w.L, w.p, w.k, ws, *grads, stream=stream, events=evb)
 
@@ -464,6 +469,13 @@ def main():
         "roofline": head["roofline"],
         "stages": head["stages"],
     }
+    if not args.no_extra and w0.backward:
+        # the forward alone, as a call no backward follows (lh_forward_nograd)
+        r = measure(lh, hip, w0, args.steps, args.warmup, backward=False, nograd=True)
+        r.pop("inputs")
+        res["nograd_fwd_ms"] = round(r["fwd_ms"], 4)
+        res["nograd_fwd_tokens_per_s"] = round(w.N / (r["fwd_ms"] / 1000.0), 1)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         q, k, v, dout = head["inputs"]
         res["cpu_baseline"] = cpu_baseline(q, k, v, dout, w)
@@ -480,6 +492,11 @@ def main():
             r.pop("inputs")
             extra[name] = summary(r, steps, warm, bwd)
             torch.cuda.empty_cache()
+            if not bwd:  # and as a call no backward follows
+                r = measure(lh, hip, by_name(name), steps, warm, backward=False, nograd=True)
+                r.pop("inputs")
+                extra[name]["nograd"] = summary(r, steps, warm, False)
+                torch.cuda.empty_cache()
         res["workloads"] = extra
         r = measure(lh, hip, by_name("dense-fwdbwd-512k"), 1, 1, backward=True)
         r.pop("inputs")

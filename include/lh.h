@@ -166,6 +166,22 @@ lh_status lh_forward_scored(const void *q, const void *k, const void *v,
                             void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * lh_forward for calls that no backward follows (evaluation, a loss without
+ * gradients). Same arguments, workspace and out; the sub-sequence attention
+ * multiplies V by the fp16-rounded probabilities alone, where lh_forward
+ * also adds the product with their fp16 residual so that O_sub agrees with
+ * the probabilities the backward recomputes (delta = rowsum(dO_sub * O_sub)).
+ * Each probability then carries a relative error up to 2^-11 (fp16 rounding)
+ * before the fp32 accumulation; out stays within the forward's tolerance.
+ * The context it leaves differs from lh_forward's only in O_sub; lh_backward
+ * on it runs, but its gradients are not covered by the stated tolerance:
+ * call lh_forward before a backward.
+ */
+lh_status lh_forward_nograd(const void *q, const void *k, const void *v,
+                            int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
+                            void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Backward pass with the indices of the preceding lh_forward held fixed
  * (the top-K is non-differentiable; aitrends summary, 핵심 기여): given dout =
  * dLoss/dout, writes dq, dk, dv. Needs only the context lh_forward left in ws,
@@ -219,6 +235,9 @@ const char *lh_stage_name(int backward, int stage);
 lh_status lh_forward_timed(const void *q, const void *k, const void *v,
                            int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
                            void *out, void *ws, size_t ws_bytes, void *stream, void *const *events);
+lh_status lh_forward_nograd_timed(const void *q, const void *k, const void *v,
+                                  int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
+                                  void *out, void *ws, size_t ws_bytes, void *stream, void *const *events);
 lh_status lh_backward_timed(const void *dout,
                             int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt,
                             void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream,

@@ -9,6 +9,6 @@ causal-safe shifted range. ``forward`` / ``backward`` call liblh.so; see
 include/lh.h for the ABI.
 """
 from .binding import (LighthouseError, alloc_workspace, backward, check_shape, ds_tile_budget, forward,  # noqa: F401
-                      forward_static, forward_workspace_bytes, layer_backward, layer_forward,
+                      forward_nograd, forward_static, forward_workspace_bytes, layer_backward, layer_forward,
                       layer_qkv, layer_workspace_bytes, lib, padded_subseq_len, region, selection, selftest_sqrt, set_ds_tile_budget,
                       stage_names, static_scratch_bytes, subseq_len, workspace_bytes)

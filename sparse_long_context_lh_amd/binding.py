@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "lh_forward_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
         "lh_forward_static": (i32, [vp, vp, vp] + shape + [vp, vp]),
         "lh_forward_scored": (i32, [vp, vp, vp] + shape + [i32, vp, vp, sz, vp]),
+        "lh_forward_nograd": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp]),
+        "lh_forward_nograd_timed": (i32, [vp, vp, vp] + shape + [vp, vp, sz, vp, vp]),
         "lh_static_scratch_bytes": (sz, []),
         "lh_set_ds_tile_budget": (None, [sz]),
         "lh_layer_workspace_bytes": (sz, [i64, i32, i32, i32, i32, i32, i32, i32]),
@@ -174,6 +176,29 @@ def forward(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
         _check(lib().lh_forward(*args), "lh_forward")
     else:
         _check(lib().lh_forward_timed(*args, events), "lh_forward_timed")
+    return out, ws
+
+
+def forward_nograd(q, k, v, L: int, p: int, k_sel: int, ws: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, stream=None, events=None):
+    """lh_forward_nograd: the forward for calls no backward follows; returns
+    (out, ws). A new workspace is sized for the forward alone."""
+    N, H, d = _shape_of(q)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if ws is None:
+        ws = alloc_workspace(N, H, d, L, p, k_sel, q.dtype, q.device, forward_only=True)
+    _check_ws(ws, q)
+    if out is None:
+        out = torch.empty_like(q)
+    _like(out, q, "out")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), N, H, d, L, p, k_sel, _dt(q.dtype),
+            out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    if events is None:
+        _check(lib().lh_forward_nograd(*args), "lh_forward_nograd")
+    else:
+        _check(lib().lh_forward_nograd_timed(*args, events), "lh_forward_nograd_timed")
     return out, ws
 
 

@@ -230,7 +230,7 @@ static const char *kBwdStages[] = {"scatter_bwd", "bwd_prep", "attn_bwd_dkdv", "
 
 static lh_status forward_impl(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
                               int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, hipStream_t s,
-                              void *const *events, lh_scorer scorer = LH_SCORE_SUM)
+                              void *const *events, lh_scorer scorer = LH_SCORE_SUM, bool for_backward = true)
 {
     Plan pl;
     lh_status st = make_plan(N, H, d, L, p, k_sel, dt, &pl);
@@ -373,6 +373,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         aa.lse = at<float>(ws, pl, LH_R_LSE);
         aa.ex = at<int32_t>(ws, pl, LH_R_EXP);
         aa.S = pl.S; aa.S_pad = pl.S_pad; aa.H = H;
+        aa.p_lo = for_backward ? 1 : 0;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
         if (launch_attn_fwd(pl, aa, s) != hipSuccess)
             return LH_EHIP;
@@ -663,6 +664,13 @@ lh_status lh_forward_scored(const void *q, const void *k, const void *v, int64_t
     return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr, scorer);
 }
 
+lh_status lh_forward_nograd(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
+                            int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, nullptr,
+                        LH_SCORE_SUM, false);
+}
+
 lh_status lh_forward_static(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L, int p,
                             int k_sel, lh_dtype dt, void *out, void *stream)
 {
@@ -696,6 +704,16 @@ lh_status lh_forward_timed(const void *q, const void *k, const void *v, int64_t 
     if (!events)
         return LH_EINVAL;
     return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, events);
+}
+
+lh_status lh_forward_nograd_timed(const void *q, const void *k, const void *v, int64_t N, int H, int d, int L,
+                                  int p, int k_sel, lh_dtype dt, void *out, void *ws, size_t ws_bytes, void *stream,
+                                  void *const *events)
+{
+    if (!events)
+        return LH_EINVAL;
+    return forward_impl(q, k, v, N, H, d, L, p, k_sel, dt, out, ws, ws_bytes, (hipStream_t)stream, events,
+                        LH_SCORE_SUM, false);
 }
 
 lh_status lh_backward(const void *dout, int64_t N, int H, int d, int L, int p, int k_sel, lh_dtype dt, void *dq,

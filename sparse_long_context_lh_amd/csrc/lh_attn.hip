@@ -238,7 +238,11 @@ __device__ __forceinline__ float max_pair(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, bool KLO>
+// PLO = false (forward-only calls): P.V takes the fp16 P alone. Its lo
+// product exists so that O_sub, and with it delta = rowsum(dO_sub * O_sub),
+// agrees with the P the backward recomputes; O itself needs only the fp16
+// P (relative rounding error up to 2^-11 per probability).
+template <int D, bool KLO, bool PLO>
 __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 {
     typedef FwdStage<D, KLO> St;
@@ -391,14 +395,21 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     // one, probabilities far below the running sum's half-ulp would all be
     // rounded away, a systematic loss in the normaliser that the backward's
     // dS = P (dP - delta) amplifies.
+    // the fp16 pair of 8 probabilities (PLO), or their fp16 values alone
+    auto split = [&](const float *x, uint4 &hi, uint4 &lo) __attribute__((always_inline)) {
+        if constexpr (PLO)
+            split8_mix(x, hi, lo);
+        else
+            hi = pack8h(x);
+    };
     auto probs = [&](const f32x16_t &sv, uint4 (&ph)[2], uint4 (&pl)[2]) __attribute__((always_inline)) {
         const float shift = m - kPScaleLog2; // p * 2^15 <= 2^15: within fp16
         float pr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             pr[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], scale_log2, -shift));
-        split8_mix(pr, ph[0], pl[0]);
-        split8_mix(pr + 8, ph[1], pl[1]);
+        split(pr, ph[0], pl[0]);
+        split(pr + 8, ph[1], pl[1]);
         lsum += tile_sum(pr);
     };
     // O^T += V^T P^T for block kb
@@ -410,7 +421,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             for (int t = 0; t < NT; ++t) {
                 const uint4 vv = sV[64 * (hh * NT + t) + lane];
                 o[t] = mfma32(vv, ph[hh], o[t]);
-                o[t] = mfma32(vv, pl[hh], o[t]);
+                if constexpr (PLO)
+                    o[t] = mfma32(vv, pl[hh], o[t]);
             }
     };
     // rescale O and the running sum when some row's maximum moved (a factor
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             if (s < HS)
                 expo(8 * s / HS, 8 * (s + 1) / HS);
             else if (s == HS)
-                split8_mix(pr, ph[0], pl[0]);
+                split(pr, ph[0], pl[0]);
             else
                 expo(8 + 8 * (s - HS - 1) / (NS - HS - 1), 8 + 8 * (s - HS) / (NS - HS - 1));
             __builtin_amdgcn_sched_barrier(0);
@@ -504,11 +516,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             o[t] = mfma32(vf[t], ph[0], o[t]);
-        split8_mix(pr + 8, ph[1], pl[1]);
+        split(pr + 8, ph[1], pl[1]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PLO) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            o[t] = mfma32(vf[t], pl[0], o[t]);
+            for (int t = 0; t < NT; ++t)
+                o[t] = mfma32(vf[t], pl[0], o[t]);
+        }
         lsum += tile_sum(pr);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -518,9 +532,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         if constexpr (!LAST)
             mn = fmaxf(m, rowmax(sn) * scale_log2);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PLO) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            o[t] = mfma32(vf[NT + t], pl[1], o[t]);
+            for (int t = 0; t < NT; ++t)
+                o[t] = mfma32(vf[NT + t], pl[1], o[t]);
+        }
         st = sn;
         if constexpr (!LAST)
             rescale(mn);
@@ -579,6 +595,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         a.lse[hS + qw + c32] = m + (__log2f(ltot) - kPScaleLog2); // log2 domain
 }
 
+template <int D, bool KLO>
+static void launch_fwd_t(const dim3 grid, const AttnFwdArgs &a, hipStream_t s)
+{
+    if (a.p_lo)
+        hipLaunchKernelGGL((k_attn_fwd<D, KLO, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_attn_fwd<D, KLO, false>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
 {
     const unsigned nqb = (unsigned)((pl.S + 127) / 128);
@@ -586,14 +611,14 @@ hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s)
     const bool klo = pl.dt == LH_F32; // see the precision note at the top of this file
     if (pl.d == 128) {
         if (klo)
-            hipLaunchKernelGGL((k_attn_fwd<128, true>), grid, dim3(256), 0, s, a);
+            launch_fwd_t<128, true>(grid, a, s);
         else
-            hipLaunchKernelGGL((k_attn_fwd<128, false>), grid, dim3(256), 0, s, a);
+            launch_fwd_t<128, false>(grid, a, s);
     } else {
         if (klo)
-            hipLaunchKernelGGL((k_attn_fwd<64, true>), grid, dim3(256), 0, s, a);
+            launch_fwd_t<64, true>(grid, a, s);
         else
-            hipLaunchKernelGGL((k_attn_fwd<64, false>), grid, dim3(256), 0, s, a);
+            launch_fwd_t<64, false>(grid, a, s);
     }
     return hipGetLastError();
 }

@@ -190,6 +190,7 @@ struct AttnFwdArgs {
     const int32_t *ex;                  // LH_R_EXP: staged rows are q 2^ex_q, k 2^ex_k, v 2^ex_v
     int64_t S, S_pad;
     int H;
+    int p_lo;         // 1: P.V with the fp16 pair of P (the context of a backward); 0: forward-only
     float scale_log2; // log2(e) / sqrt(d)
 };
 

@@ -105,10 +105,14 @@ class GpuRun:
     """One forward (and optionally backward) through the C ABI, with views of
     the intermediates it leaves in the workspace."""
 
-    def __init__(self, q, k, v, L, p, kk, dout=None, scorer="sum"):
+    def __init__(self, q, k, v, L, p, kk, dout=None, scorer="sum", nograd=False):
         self.H, self.N, self.d = q.shape
         self.L, self.p, self.k, self.dtype = L, p, kk, q.dtype
-        self.out, self.ws = lh.forward(q, k, v, L, p, kk, scorer=scorer)
+        if nograd:  # lh_forward_nograd: the forward no backward follows
+            assert dout is None and scorer == "sum"
+            self.out, self.ws = lh.forward_nograd(q, k, v, L, p, kk)
+        else:
+            self.out, self.ws = lh.forward(q, k, v, L, p, kk, scorer=scorer)
         self.grads = None
         if dout is not None:
             self.grads = lh.backward(dout, L, p, kk, self.ws)
@@ -254,10 +258,10 @@ def compare_backward(run: GpuRun, h: int, ref: dict, gref: dict, tag: str = "",
     return stats
 
 
-def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum", scales=None):
+def check_case(q, k, v, L, p, kk, dout=None, heads=None, tag="", scorer="sum", scales=None, nograd=False):
     """Whole-path parity of one case on the listed heads (default: all);
     ``scales(h)`` gives head h's absolute-term factors (see compare_forward)."""
-    run = GpuRun(q, k, v, L, p, kk, dout, scorer=scorer)
+    run = GpuRun(q, k, v, L, p, kk, dout, scorer=scorer, nograd=nograd)
     heads = range(run.H) if heads is None else heads
     out = {}
     fails = Failures()

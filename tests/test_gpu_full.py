@@ -18,11 +18,22 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("w", WORKLOADS[1:], ids=lambda w: w.name)
 def test_full_size_workload(w):
-    say("workload %s: N=%d H=%d d=%d L=%d p=%d k=%d S=%d bwd=%s"
-        % (w.name, w.N, w.H, w.d, w.L, w.p, w.k, oracle.subseq_len(w.N, w.L, w.p, w.k), w.backward))
+    _full_size(w, nograd=False)
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("w", [w for w in WORKLOADS[1:] if not w.backward], ids=lambda w: w.name)
+def test_full_size_forward_nograd(w):
+    # the forward-only workloads through lh_forward_nograd, as timed beside lh_forward
+    _full_size(w, nograd=True)
+
+
+def _full_size(w, nograd):
+    say("workload %s: N=%d H=%d d=%d L=%d p=%d k=%d S=%d bwd=%s nograd=%s"
+        % (w.name, w.N, w.H, w.d, w.L, w.p, w.k, oracle.subseq_len(w.N, w.L, w.p, w.k), w.backward, nograd))
     q, k, v = make_qkv(w.N, w.H, w.d, w.dtype, w.n_plant, seed=0, device="cuda")
     dout = make_dout(w.N, w.H, w.d, w.dtype, seed=1, device="cuda") if w.backward else None
-    run = GpuRun(q, k, v, w.L, w.p, w.k, dout)
+    run = GpuRun(q, k, v, w.L, w.p, w.k, dout, nograd=nograd)
     for h in range(w.H):
         qh, kh = head_inputs(q, h), head_inputs(k, h)
         sc = oracle.score_pyramid(oracle.token_scores(qh, kh), w.L, w.p)

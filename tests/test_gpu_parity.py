@@ -183,6 +183,34 @@ def test_single_token():
     assert torch.equal(run.grads[2], dout)
 
 
+@pytest.mark.parametrize("N,H,d,L,p,k,dtype", [
+    (8192, 2, 128, 3, 2, 300, torch.bfloat16),   # ragged tail, strata
+    (16384, 2, 128, 4, 4, 40, torch.bfloat16),
+    (4096, 2, 64, 3, 2, 256, torch.float32),      # fp32: the K lo product stays
+    (3000, 2, 128, 1, 2, 0, torch.bfloat16),      # dense, ragged
+    (2048, 1, 64, 3, 8, 0, torch.bfloat16),       # top level only
+])
+def test_forward_nograd(N, H, d, L, p, k, dtype):
+    # the forward no backward follows: whole-path parity with the oracle, the
+    # same selection, order and staged rows as lh_forward bit for bit, and an
+    # output within a few fp16 roundings of the probabilities of lh_forward's
+    tag = "nograd N=%d L=%d p=%d k=%d %s d=%d" % (N, L, p, k, dtype, d)
+    say("case %s" % tag)
+    q, kk, v = (x.cuda() for x in make_qkv(N, H, d, dtype, 8, 5))
+    run, _ = check_case(q, kk, v, L, p, k, tag=tag, nograd=True)
+    full = GpuRun(q, kk, v, L, p, k)
+    names = ["ent", "qhi", "qlo", "khi", "klo", "v", "lse"] + (["scores", "sel", "slot"] if L > 1 else [])
+    for h in range(H):
+        for name in names:
+            a, b = run.head(name, h), full.head(name, h)
+            if name in ("ent", "lse", "qhi", "qlo", "khi", "klo", "v"):
+                a, b = a[:run.S], b[:run.S]
+            assert torch.equal(a, b), (name, h)
+    diff = (run.out.float() - full.out.float()).abs().max().item()
+    say("  nograd vs lh_forward: max |out difference| %.3g" % diff)
+    assert diff <= 2.0 ** -8 * max(1.0, full.out.float().abs().max().item())
+
+
 def test_selection_hook_and_forward_only_workspace():
     # lh_selection points at the selection lh_forward made (level by level,
     # [H, k], equal to the oracle's); a forward given only the forward's
