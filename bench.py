@@ -401,6 +401,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lh-fwdbwd-512k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--nograd", action="store_true",
+                    help="forward workloads: time lh_forward_nograd (the forward no backward follows)")
     ap.add_argument("--no-extra", action="store_true",
                     help="time the headline workload only (no other sizes, no dense denominator)")
     ap.add_argument("--sweep", action="store_true",
@@ -446,7 +448,9 @@ def main():
             torch.cuda.empty_cache()
         return
     w0 = by_name(args.workload)
-    head = measure(lh, hip, w0, args.steps, args.warmup, backward=w0.backward)
+    if args.nograd and w0.backward:
+        raise SystemExit("--nograd applies to forward workloads")
+    head = measure(lh, hip, w0, args.steps, args.warmup, backward=w0.backward, nograd=args.nograd)
     w = head["w"]
     res = {
         "metric": METRIC,
@@ -462,7 +466,8 @@ def main():
         "dtype": "bf16" if w0.dtype == torch.bfloat16 else "fp32",
         "data": "synthetic",
         "config": {"workload": w0.name, "N": w.N, "H": w.H, "d": w.d, "L": w.L, "p": w.p, "k": w.k, "S": head["S"],
-                   "step": "forward+backward" if w0.backward else "forward", "parallelism": "none (1 GPU)"},
+                   "step": "forward+backward" if w0.backward else ("forward (nograd)" if args.nograd else "forward"),
+                   "parallelism": "none (1 GPU)"},
         "fwd_tokens_per_s": round(w.N / (head["fwd_ms"] / 1000.0), 1),
         "fwd_ms": round(head["fwd_ms"], 4),
         "bwd_ms": round(head["bwd_ms"], 4),
