@@ -350,6 +350,42 @@ def summary(r, steps, warmup, backward):
     return d
 
 
+def measure_ceilings():
+    """What library kernels reach on this GPU right now, as context for the
+    roofline fractions (which are taken against the datasheet peaks): an fp16
+    GEMM of 8192^3 (torch.mm, hipBLASLt) under sustained load, where the chip
+    lowers its clock, and a 2 GiB device copy and read (torch). torch's own
+    stream and events time torch's own kernels."""
+    import torch
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+    out = {}
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.float16)
+    c = torch.empty_like(a)
+    ms = timed(lambda: torch.mm(a, b, out=c), 20)
+    out["gemm_fp16_8192_tflops"] = round(2.0 * 8192 ** 3 / (ms / 1e3) / 1e12, 1)
+    del a, b, c
+    src = torch.ones(1 << 29, device="cuda", dtype=torch.float32)  # 2 GiB
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 4
+    out["copy_2gib_gbs"] = round(2.0 * nbytes / (timed(lambda: dst.copy_(src), 5) / 1e3) / 1e9, 1)
+    out["read_2gib_gbs"] = round(nbytes / (timed(lambda: src.sum(), 5) / 1e3) / 1e9, 1)
+    del src, dst
+    out["note"] = "copy counts bytes read + written; roofline fractions are against the datasheet peaks"
+    return out
+
+
 def measure_layer(lh, steps=3, warmup=1, d_model=2048):
     """The step around the layer at the headline shape (N = 512K, H = 16,
     d = 128, L = 5, p = 4, k = 512): Q/K/V projections of x [N, d_model] by
@@ -518,6 +554,8 @@ def main():
         lay["gemm_ms_fwdbwd"] = round(g_fb, 3)
         lay["gemm_tflops_fwdbwd"] = round(lay["gemm_tflop_fwdbwd"] / (g_fb / 1e3), 1) if g_fb > 0 else None
         res["projection_layer_512k"] = lay
+        torch.cuda.empty_cache()
+        res["ceilings"] = measure_ceilings()
         torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
