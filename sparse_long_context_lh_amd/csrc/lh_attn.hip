@@ -634,19 +634,28 @@ template <int D>
 struct DkdvStage {
     static constexpr int BQ = 32;
     static constexpr int RCH = D / 8;  // chunks per row-major row
-    static constexpr int TCH = BQ / 8; // chunks per transposed row
     static constexpr int ROWS = BQ * RCH;
-    static constexpr int COLS = D * TCH;
-    static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS, QT = 4 * ROWS, DT = 4 * ROWS + COLS;
+    static constexpr int QH = 0, QL = ROWS, DH = 2 * ROWS, DL = 3 * ROWS;
     // row statistics: 64 chunks per wave, the first 4 of them used (wave 0:
     // lse of queries 0-15, 1: lse 16-31, 2: delta 0-15, 3: delta 16-31); a
     // whole wave's transfer fills them, so none is predicated
-    static constexpr int LS = 4 * ROWS + 2 * COLS;
+    static constexpr int LS = 4 * ROWS;
     static constexpr int SIZE = LS + 4 * 64; // in 16-byte chunks
     static constexpr int NBUF = 3;
-    // global_load_lds instructions one wave issues per stage
-    static constexpr int LOADS = 4 * (ROWS / 256) + 2 * (COLS / 256) + 1;
 };
+
+// gfx950's transposing LDS read (16-bit elements): in each group of 16 lanes,
+// lane 4R + m supplies 4 consecutive elements a[4R + m][0..3], and lane j
+// receives a[4R + j/4][j%4] for R = 0..3 as its 4 elements. With lane 4R + m
+// addressing row r_R, columns c + 4m .. c + 4m + 3 of a row-major tile, lane
+// j receives column c + j of rows r_0 .. r_3: a column read.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const uint4 *tile, uint32_t byte_off)
+{
+    const uint32_t off = (uint32_t)(size_t)tile + byte_off; // low word of a generic LDS address = LDS offset
+    typedef s16x4_t __attribute__((address_space(3))) *ptr_t;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ptr_t)(size_t)off));
+}
 
 // Keeps the compiler from moving instructions across this point: used to
 // interleave each matrix product with the LDS read of a later operand.
@@ -662,13 +671,13 @@ template <int D, bool KLO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_bwd_dkdv(AttnBwdArgs a)
 {
     typedef DkdvStage<D> St;
-    constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH, TCH = St::TCH;
+    constexpr int BK = 128, BQ = St::BQ, RCH = St::RCH;
     constexpr int NS = D / 16, NT = D / 32;
-    constexpr int RU = St::ROWS / 256, TU = St::COLS / 256; // load rounds per tile
+    constexpr int RU = St::ROWS / 256; // load rounds per tile
     constexpr int NM = D / 64; // fp8 products of the lo parts (bf16 inputs)
     // transfers one wave issues per stage (bf16 inputs: the Q lo and dO lo
     // tiles are fp8 tiles, one transfer per thread each)
-    constexpr int LOADS = 2 * RU + 2 * (KLO ? RU : 1) + 2 * TU + 1;
+    constexpr int LOADS = 2 * RU + 2 * (KLO ? RU : 1) + 1;
     __shared__ uint4 ring[St::NBUF * St::SIZE];
 
     const int h = blockIdx.x % a.H;
@@ -689,28 +698,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // Per-lane byte offsets of this thread's chunks inside a stage's tiles
     // (the same for every stage; the stage only moves the uniform base).
-    uint32_t roff[RU], toff[TU];
+    uint32_t roff[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int c = 256 * u + tid, r = c / RCH;
         roff[u] = 2u * (uint32_t)(r * D + swzg<RCH>(r, c % RCH) * 8);
     }
+    // Byte offsets of this lane's transposing reads of the row-major Q and dO
+    // hi tiles: the operand of dV (dO^T) and dK (Q^T) for dimensions
+    // 32t .. 32t+31 and queries 16hh .. 16hh+15 is two reads (queries
+    // 16hh + 8g + 4n .. +3, n = 0, 1), lane 16G + 4R + m addressing query
+    // 16hh + 8(G/2) + 4n + R, dimensions 32t + 16(G%2) + 4m .. +3.
+    uint32_t toff[2][2][NT];
 #pragma unroll
-    for (int u = 0; u < TU; ++u) {
-        const int c = 256 * u + tid, dim = c / TCH;
-        toff[u] = 2u * ((uint32_t)dim * (uint32_t)S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8));
-    }
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int G = lane >> 4, R = (lane >> 2) & 3, m = lane & 3;
+                const int q = 16 * hh + 8 * (G >> 1) + 4 * n + R, dim = 32 * t + 16 * (G & 1) + 4 * m;
+                toff[hh][n][t] = 2u * (uint32_t)(q * D + swzg<RCH>(q, dim >> 3) * 8 + (dim & 7));
+            }
     const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
-    const uint16_t *const cols[2] = {a.qhi_t, a.dohi_t};
     // each wave fetches 4 of the 16 lse / delta chunks (lanes 4..63 repeat
     // them), so every wave issues the same number of loads per stage (St::LOADS)
     const float *stat = wave < 2 ? a.lse : a.delta;
     const uint32_t stat_off = 16u * (uint32_t)(4 * (wave & 1) + (lane & 3));
 
     // A stage's transfers in five parts (the four row-major tiles, then the
-    // two transposed tiles and the statistics), issued at spread-out points
-    // of the previous stage's math: issued in one burst, their LDS writes
-    // stall the operand reads of the products.
+    // statistics), issued at spread-out points of the previous stage's math:
+    // issued in one burst, their LDS writes stall the operand reads of the
+    // products.
     auto issue_rows = [&](int q0, const uint4 *base, int t) {
         if (!KLO && (t == 1 || t == 3)) { // fp8 Q lo / dO lo tile, stored in operand order: a linear copy
             dma16((t == 1 ? a.qlo8 : a.dolo8) + (hS + q0) * D, 16u * (uint32_t)(tid % (2 * D)),
@@ -722,21 +741,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int u = 0; u < RU; ++u)
             dma16(rb, roff[u], base + 64 * wave + t * St::ROWS + 256 * u);
     };
-    auto issue_cols = [&](int q0, const uint4 *base) {
+    auto issue_stats = [&](int q0, const uint4 *base) {
         dma16(stat + hS + q0, stat_off, base + St::LS + 64 * wave);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint16_t *cb = cols[t] + (int64_t)h * D * S_pad + q0;
-#pragma unroll
-            for (int u = 0; u < TU; ++u)
-                dma16(cb, toff[u], base + 64 * wave + St::QT + t * St::COLS + 256 * u);
-        }
     };
     auto issue = [&](int q0, const uint4 *base) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             issue_rows(q0, base, t);
-        issue_cols(q0, base);
+        issue_stats(q0, base);
     };
 
     uint4 kh[NS], vf[NS], klf[KLO ? NS : 1], k8r[KLO ? 1 : NM][2], v8r[KLO ? 1 : NM][2];
@@ -826,10 +838,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int at = ql * RCH + swzg<RCH>(ql, 2 * s + g);
             return base[(i == 0 ? St::QH : i == 1 ? St::QL : i == 2 ? St::DH : St::DL) + at];
         };
+        // operand of dV (i = 0, 1: dO^T) or dK (i = 2, 3: Q^T), dimensions
+        // 32t .. 32t+31, queries 16(i%2) .. +15: transposing reads of the
+        // row-major hi tile
         auto gfrag = [&](int t, int i) {
-            const int dim = 32 * t + c32;
-            const int c = dim * TCH + swzg<TCH>(dim, (i & 1) * 2 + g);
-            return base[(i < 2 ? St::DT : St::QT) + c];
+            const uint4 *tile = base + (i < 2 ? St::DH : St::QH);
+            const uint2 lo = lds_tr16(tile, toff[i & 1][0][t]), hi = lds_tr16(tile, toff[i & 1][1][t]);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
         };
         // statistics of 4 queries: register v holds query 16(v/8) + 8g + v%8
         auto stat4 = [&](const float *p, int v0) { // queries 16(v0/8) + 8g + v0%8 .. +3
@@ -931,7 +946,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             ga[0][i] = gfrag(0, i);
-        issue_cols(q2, ahead);
+        issue_stats(q2, ahead);
         LH_FENCE;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
