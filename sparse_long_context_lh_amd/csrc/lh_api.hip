@@ -165,7 +165,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[LH_R_DOSUB] = 4 * Hs * Sp * D;
     b[LH_R_DQSUB] = b[LH_R_DKSUB] = b[LH_R_DVSUB] = 4 * Hs * Sp * D;
     b[IR_POOLED] = 4 * 3 * Hs * (size_t)pl->mat_rows * D;
-    b[IR_DOHI] = b[IR_DOLO] = b[IR_DOHI_T] = 2 * Hs * Sp * D;
+    b[IR_DOHI] = b[IR_DOLO] = 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
     b[IR_LSE15] = 4 * Hs * Sp;
     b[IR_DST] = pl->ds_tiles ? ds_bytes : 0;
@@ -183,7 +183,7 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     static const int kFwdOrder[] = {LH_R_SCORES, LH_R_SEL, LH_R_SLOT, LH_R_ENT, LH_R_QHI, LH_R_QLO, LH_R_KHI,
                                     LH_R_KLO, LH_R_V, LH_R_QHI_T, LH_R_KHI_T, LH_R_V_T, LH_R_OSUB, LH_R_LSE,
                                     IR_TMAX, IR_SC8, LH_R_EXP, IR_QLO8, IR_K8, IR_POOLED, IR_FPART, IR_XMAX};
-    static const int kBwdOrder[] = {LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, IR_DOHI, IR_DOLO, IR_DOHI_T,
+    static const int kBwdOrder[] = {LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, IR_DOHI, IR_DOLO,
                                     IR_DELTA, IR_LSE15, IR_SPART, IR_V8, IR_DOLO8, IR_DOMAX, IR_DST};
     static_assert(sizeof(kFwdOrder) / sizeof(int) + sizeof(kBwdOrder) / sizeof(int) == IR_COUNT,
                   "every region placed once");
@@ -444,7 +444,6 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         BwdPrepArgs a;
         a.dosub = dosub; a.osub = at<float>(ws, pl, LH_R_OSUB);
         a.dohi = at<uint16_t>(ws, pl, IR_DOHI); a.dolo = at<uint16_t>(ws, pl, IR_DOLO);
-        a.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
         a.delta = at<float>(ws, pl, IR_DELTA);
         a.lse = at<float>(ws, pl, LH_R_LSE);
         a.lse15 = at<float>(ws, pl, IR_LSE15);
@@ -483,11 +482,9 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.v8 = at<uint8_t>(ws, pl, IR_V8);
     ab.dolo8 = at<uint8_t>(ws, pl, IR_DOLO8);
     ab.sc8 = at<int32_t>(ws, pl, IR_SC8);
-    ab.qhi_t = at<uint16_t>(ws, pl, LH_R_QHI_T);
     ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);
     ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);
     ab.dolo = at<uint16_t>(ws, pl, IR_DOLO);
-    ab.dohi_t = at<uint16_t>(ws, pl, IR_DOHI_T);
     ab.lse = at<float>(ws, pl, IR_LSE15);
     ab.delta = at<float>(ws, pl, IR_DELTA);
     ab.dq = at<float>(ws, pl, LH_R_DQSUB);

@@ -32,7 +32,6 @@ enum InternalRegion {
     IR_POOLED = LH_R_COUNT, // fp32 [3][H][mat_rows][d]: materialized pooled levels
     IR_DOHI,                // fp16 [H][S_pad][d]: hi part of dO_sub
     IR_DOLO,                // fp16 [H][S_pad][d]: lo part of dO_sub
-    IR_DOHI_T,              // fp16 [H][d][S_pad]: transpose of the hi part
     IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub) * 2^-15
     IR_LSE15,               // fp32 [H][S_pad]: log2-domain LSE - 15
     IR_DST,                 // fp16 [H][T(T+1)/2][32][32], T = S_pad/32: dS tiles (query-major), causal half
@@ -198,8 +197,8 @@ struct AttnBwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
     const uint8_t *qlo8, *k8, *v8, *dolo8;       // bf16 inputs: fp8 tiles of the Q lo part, K, V, dO lo part
     const int32_t *sc8;                          // ... and their scales [4][H]
-    const uint16_t *qhi_t, *khi_t;              // fp16 [H][d][S_pad]
-    const uint16_t *dohi, *dolo, *dohi_t;       // fp16 pair of dO_sub, and the hi transpose
+    const uint16_t *khi_t;                      // fp16 [H][d][S_pad]
+    const uint16_t *dohi, *dolo;                // fp16 pair of dO_sub
     const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
     float *dq, *dk, *dv;                             // [H][S_pad][d]
     uint16_t *dst;     // IR_DST: tile (qt, kt), kt <= qt, at (qt(qt+1)/2 + kt) * 1024 in a head's block
@@ -234,7 +233,7 @@ struct ScatterBwdArgs {
 
 struct BwdPrepArgs {
     const float *dosub, *osub;       // [H][S_pad][d]
-    uint16_t *dohi, *dolo, *dohi_t;  // fp16 pair, and the hi transpose
+    uint16_t *dohi, *dolo;           // fp16 pair
     float *delta;              // [H][S_pad]: rowsum * 2^-15
     const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
     float *lse15;              // [H][S_pad]: lse - 15

@@ -442,8 +442,9 @@ hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream
 }
 
 // ---------------------------------------------------------------- backward prep
-// fp16 pair of dO_sub (hi = fp16(x), lo = fp16(x - hi)) row-major, the hi part
-// transposed (MFMA operands of the attention backward), and
+// fp16 pair of dO_sub (hi = fp16(x), lo = fp16(x - hi)) row-major (MFMA
+// operands of the attention backward, which reads the hi part's transpose out
+// of LDS), and
 // delta_s = sum_d (hi + lo)[s][d] * O_sub[s][d], the row term of the softmax
 // gradient, from the same values the dP products see. Rows past S are zero.
 // The attention backward works with probabilities scaled by 2^15 (kept out of
@@ -454,8 +455,7 @@ hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
 {
-    constexpr int LANES = D / 8, NLG = 256 / LANES, LD = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kPrepTile * LD];
+    constexpr int LANES = D / 8, NLG = 256 / LANES;
     __shared__ uint32_t s_amax[kPrepTile / 32]; // largest |lo| per 32-row tile (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kPrepTile;
@@ -500,7 +500,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         }
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
         *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
-        *reinterpret_cast<uint4 *>(&tile[r * LD + lane * 8]) = hi;
         if (a.tmax) {
             float m8 = 0.0f;
 #pragma unroll
@@ -516,19 +515,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
     __syncthreads();
     if (a.tmax && threadIdx.x < kPrepTile / 32)
         a.tmax[(int64_t)h * (a.S_pad / 32) + s0 / 32 + threadIdx.x] = __uint_as_float(s_amax[threadIdx.x]);
-    constexpr int CH = kPrepTile / 8;
-    for (int c = threadIdx.x; c < D * CH; c += 256) {
-        const int dim = c / CH, sc = c - (c / CH) * CH;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo16 = tile[(sc * 8 + 2 * e) * LD + dim];
-            const uint32_t hi16 = tile[(sc * 8 + 2 * e + 1) * LD + dim];
-            w[e] = lo16 | (hi16 << 16);
-        }
-        *reinterpret_cast<uint4 *>(a.dohi_t + ((int64_t)h * D + dim) * a.S_pad + s0 + sc * 8) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-    }
 }
 
 // Largest dO_sub row norm of each 64-row tile of a head (rows past S are
