@@ -657,6 +657,15 @@ __device__ __forceinline__ uint2 lds_tr16(const uint4 *tile, uint32_t byte_off)
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((ptr_t)(size_t)off));
 }
 
+// A 16-byte non-temporal store (the dS tiles: too large to stay cached until
+// the dQ kernel reads them, so they should not evict the stream of Q and dO).
+__device__ __forceinline__ void store16_stream(uint16_t *p, uint4 v)
+{
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4u *>(p));
+}
+
 // Keeps the compiler from moving instructions across this point: used to
 // interleave each matrix product with the LDS read of a later operand.
 #define LH_FENCE __builtin_amdgcn_sched_barrier(0)
@@ -993,11 +1002,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     t8[e] = tr[e];
-                *reinterpret_cast<uint4 *>(row) = pack8h(t8);
+                store16_stream(row, pack8h(t8));
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     t8[e] = tr[8 + e];
-                *reinterpret_cast<uint4 *>(row + 16) = pack8h(t8);
+                store16_stream(row + 16, pack8h(t8));
             }
             LH_FENCE;
         }

@@ -98,6 +98,21 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8])
     reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// Non-temporal stores, for outputs no later pass of the step reads.
+__device__ __forceinline__ void store8_stream(uint16_t *p, const float (&x)[8])
+{
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(p));
+}
+__device__ __forceinline__ void store8_stream(float *p, const float (&x)[8])
+{
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<v4f *>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<v4f *>(p) + 1);
+}
+
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // A piece kept in its storage format until it is summed (fewer registers
@@ -111,6 +126,24 @@ __device__ __forceinline__ void ld_raw(const float *p, Raw8<LH_F32> &r)
 {
     r.a = reinterpret_cast<const float4 *>(p)[0];
     r.b = reinterpret_cast<const float4 *>(p)[1];
+}
+// The same for data no later pass reads again (the upstream gradient): a
+// non-temporal load, which does not keep the lines in the caches. (The
+// inputs Q, K, V are read again by the gather after the front pass, which
+// finds part of them still cached: the front pass reads them normally.)
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void ld_stream(const uint16_t *p, Raw8<LH_BF16> &r)
+{
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    r.u = make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void ld_stream(const float *p, Raw8<LH_F32> &r)
+{
+    const f32x4_nt a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt *>(p));
+    const f32x4_nt b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt *>(p) + 1);
+    r.a = make_float4(a.x, a.y, a.z, a.w);
+    r.b = make_float4(b.x, b.y, b.z, b.w);
 }
 __device__ __forceinline__ void zero_raw(Raw8<LH_BF16> &r) { r.u = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void zero_raw(Raw8<LH_F32> &r)

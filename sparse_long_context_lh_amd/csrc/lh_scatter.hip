@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void k_pull(PullArgs a)
         if (t >= 0 && t < a.N)
 #pragma unroll
             for (int u = 0; u < NT; ++u)
-                store8(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, coarse[u]);
+                store8_stream(reinterpret_cast<T *>(a.dst[u]) + ((int64_t)h * a.N + t) * D + col, coarse[u]);
     } else {
         // tensor after tensor (the finer levels' partial sums of one tensor
         // live at a time, which keeps the register count and with it the
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void k_pull(PullArgs a)
                 }
                 const int64_t t = x - OFF;
                 if (t >= 0 && t < a.N)
-                    store8(dst + t * D, o);
+                    store8_stream(dst + t * D, o);
             }
         }
     }
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void k_scatter_bwd(ScatterBwdArgs a)
     for (int r = 0; r < R; ++r) {
         const int64_t u = ug + r;
         if (u >= 1 && u <= a.N)
-            ld_raw(dout + (u - 1) * D, rows[r]);
+            ld_stream(dout + (u - 1) * D, rows[r]);
         else
             zero_raw(rows[r]);
     }
