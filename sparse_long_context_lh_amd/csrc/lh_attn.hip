@@ -130,6 +130,17 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t off_bytes, cons
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off_bytes), "s"(sb)
                  : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once (the dS tiles).
+__device__ __forceinline__ void dma16_nt(const void *base, uint32_t off_bytes, const uint4 *lds_wave_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds_wave_base);
+    const uint64_t b = (uint64_t)(size_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0), "v"(off_bytes), "s"(sb)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_async() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -1132,8 +1143,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
             if (live && ktile <= qt) {
                 const uint16_t *tb = dsrow + (int64_t)ktile * 1024;
                 const uint4 *lb = base + St::DS + wave * St::DSW + j * 128;
-                dma16(tb, doff0, lb);
-                dma16(tb, doff1, lb + 64);
+                dma16_nt(tb, doff0, lb);
+                dma16_nt(tb, doff1, lb + 64);
             }
         }
     };
