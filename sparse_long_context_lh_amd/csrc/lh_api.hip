@@ -373,7 +373,7 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         aa.lse = at<float>(ws, pl, LH_R_LSE);
         aa.ex = at<int32_t>(ws, pl, LH_R_EXP);
         aa.S = pl.S; aa.S_pad = pl.S_pad; aa.H = H;
-        aa.p_lo = for_backward ? 1 : 0;
+        aa.for_bwd = for_backward ? 1 : 0;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
         if (launch_attn_fwd(pl, aa, s) != hipSuccess)
             return LH_EHIP;

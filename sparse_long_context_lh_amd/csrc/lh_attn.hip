@@ -249,11 +249,13 @@ __device__ __forceinline__ float max_pair(float x)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// PLO = false (forward-only calls): P.V takes the fp16 P alone. Its lo
-// product exists so that O_sub, and with it delta = rowsum(dO_sub * O_sub),
-// agrees with the P the backward recomputes; O itself needs only the fp16
-// P (relative rounding error up to 2^-11 per probability).
-template <int D, bool KLO, bool PLO>
+// BWD = false (calls no backward follows): P.V takes the fp16 P alone. Its
+// lo product exists so that O_sub, and with it delta = rowsum(dO_sub *
+// O_sub), agrees with the P the backward recomputes (dS = P (dP - delta)
+// cancels heavily); O itself needs only the fp16 P (relative rounding error
+// up to 2^-11 per probability). The query's lo part stays: without it a few
+// outputs of the 64K-token workload leave the stated tolerance.
+template <int D, bool KLO, bool BWD>
 __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 {
     typedef FwdStage<D, KLO> St;
@@ -274,6 +276,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     const uint8_t *k8 = a.k8 + hS * D;
     const uint16_t *vt = a.vt + (int64_t)h * D * a.S_pad;
     constexpr int NM = D / 64; // fp8 products of the logits' lo part (bf16 inputs)
+    constexpr bool Q8 = !KLO; // the logits' lo part as those fp8 products
     // the logits of the staged rows are 2^(ex_q + ex_k) times the true ones
     const float scale_log2 = ldexpf(a.scale_log2, -(a.ex[h] + a.ex[a.H + h]));
 
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             if constexpr (KLO)
                 dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
         }
-        if constexpr (!KLO) // the fp8 tile is stored in operand order: a linear copy
+        if constexpr (Q8) // the fp8 tile is stored in operand order: a linear copy
             dma16(k8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::KL + 64 * wave);
 #pragma unroll
         for (int u = 0; u < St::VU; ++u)
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
     }
     int qs = 0, ks = 0; // scales of the head's fp8 Q lo and K tiles
-    if constexpr (!KLO) {
+    if constexpr (Q8) {
         const uint8_t *qt8 = a.qlo8 + (hS + qw) * D + 16 * (kappa(c32) + 32 * g);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         if constexpr (KLO)
             asm volatile("" ::"v"(ql[s].x));
     }
-    if constexpr (!KLO) {
+    if constexpr (Q8) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
             asm volatile("" ::"v"(q8[m][0].x), "v"(q8[m][1].x), "v"(qs), "v"(ks));
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
                 st = mfma32(kh, ql[s], st);
             }
         }
-        if constexpr (!KLO) {
+        if constexpr (Q8) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 st = mfma8(base[St::KL + 128 * m + lane], base[St::KL + 128 * m + 64 + lane], q8[m][0], q8[m][1], st,
@@ -406,9 +409,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     // one, probabilities far below the running sum's half-ulp would all be
     // rounded away, a systematic loss in the normaliser that the backward's
     // dS = P (dP - delta) amplifies.
-    // the fp16 pair of 8 probabilities (PLO), or their fp16 values alone
+    // the fp16 pair of 8 probabilities (BWD), or their fp16 values alone
     auto split = [&](const float *x, uint4 &hi, uint4 &lo) __attribute__((always_inline)) {
-        if constexpr (PLO)
+        if constexpr (BWD)
             split8_mix(x, hi, lo);
         else
             hi = pack8h(x);
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             for (int t = 0; t < NT; ++t) {
                 const uint4 vv = sV[64 * (hh * NT + t) + lane];
                 o[t] = mfma32(vv, ph[hh], o[t]);
-                if constexpr (PLO)
+                if constexpr (BWD)
                     o[t] = mfma32(vv, pl[hh], o[t]);
             }
     };
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
                 for (int f = (s - HS) * NT / (NS - HS); f < (s - HS + 1) * NT / (NS - HS); ++f)
                     read_v(f);
             }
-            if (!KLO && s == NS - 2) {
+            if (Q8 && s == NS - 2) {
 #pragma unroll
                 for (int mm = 0; mm < NM; ++mm) {
                     k8f[mm][0] = lds_ld(kb, St::KL + 128 * mm);
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             if constexpr (KLO) {
                 sn = mfma32(kl[s], qh[s], sn);
                 sn = mfma32(kf[s], ql[s], sn);
-            } else if (s == NS - 1) { // the lo part, as block-scaled fp8 products
+            } else if (Q8 && s == NS - 1) { // the lo part, as block-scaled fp8 products
 #pragma unroll
                 for (int mm = 0; mm < NM; ++mm)
                     sn = mfma8(k8f[mm][0], k8f[mm][1], q8[mm][0], q8[mm][1], sn, ks, qs);
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
             o[t] = mfma32(vf[t], ph[0], o[t]);
         split(pr + 8, ph[1], pl[1]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PLO) {
+        if constexpr (BWD) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 o[t] = mfma32(vf[t], pl[0], o[t]);
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         if constexpr (!LAST)
             mn = fmaxf(m, rowmax(sn) * scale_log2);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PLO) {
+        if constexpr (BWD) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 o[t] = mfma32(vf[NT + t], pl[1], o[t]);
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 template <int D, bool KLO>
 static void launch_fwd_t(const dim3 grid, const AttnFwdArgs &a, hipStream_t s)
 {
-    if (a.p_lo)
+    if (a.for_bwd)
         hipLaunchKernelGGL((k_attn_fwd<D, KLO, true>), grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((k_attn_fwd<D, KLO, false>), grid, dim3(256), 0, s, a);

@@ -189,7 +189,7 @@ struct AttnFwdArgs {
     const int32_t *ex;                  // LH_R_EXP: staged rows are q 2^ex_q, k 2^ex_k, v 2^ex_v
     int64_t S, S_pad;
     int H;
-    int p_lo;         // 1: P.V with the fp16 pair of P (the context of a backward); 0: forward-only
+    int for_bwd;      // 1: the lo products the backward's context needs; 0: a call no backward follows
     float scale_log2; // log2(e) / sqrt(d)
 };
 

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import sparse_long_context_lh_amd as lh
-from parity import GpuRun, check_case, say
+from parity import ATOL, RTOL, GpuRun, check_case, say
 from synth_inputs import make_dout, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -191,9 +191,9 @@ def test_single_token():
     (2048, 1, 64, 3, 8, 0, torch.bfloat16),       # top level only
 ])
 def test_forward_nograd(N, H, d, L, p, k, dtype):
-    # the forward no backward follows: whole-path parity with the oracle, the
-    # same selection, order and staged rows as lh_forward bit for bit, and an
-    # output within a few fp16 roundings of the probabilities of lh_forward's
+    # the forward no backward follows: whole-path parity with the oracle, and
+    # the same selection, order, staged rows and log-sum-exp as lh_forward
+    # bit for bit (only O_sub differs)
     tag = "nograd N=%d L=%d p=%d k=%d %s d=%d" % (N, L, p, k, dtype, d)
     say("case %s" % tag)
     q, kk, v = (x.cuda() for x in make_qkv(N, H, d, dtype, 8, 5))
@@ -206,9 +206,11 @@ def test_forward_nograd(N, H, d, L, p, k, dtype):
             if name in ("ent", "lse", "qhi", "qlo", "khi", "klo", "v"):
                 a, b = a[:run.S], b[:run.S]
             assert torch.equal(a, b), (name, h)
-    diff = (run.out.float() - full.out.float()).abs().max().item()
-    say("  nograd vs lh_forward: max |out difference| %.3g" % diff)
-    assert diff <= 2.0 ** -8 * max(1.0, full.out.float().abs().max().item())
+    # both outputs are within the element-wise bound of the oracle's, so
+    # within twice that bound of each other
+    a, b = run.out.float(), full.out.float()
+    say("  nograd vs lh_forward: max |out difference| %.3g" % (a - b).abs().max().item())
+    assert bool(((a - b).abs() <= 2 * (ATOL + RTOL * b.abs())).all())
 
 
 def test_selection_hook_and_forward_only_workspace():
