@@ -709,8 +709,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: LDS bases stay scalar
     const int kw = k0 + wave * 32;
-    // lane c32 owns key kw + kappa(c32): then the transposed dS tile (below)
-    // leaves the MFMA as runs of 8 consecutive keys per lane
+    // lane c32 owns key kw + kappa(c32): the lane position the forward's fp8
+    // K tile gives that key, so the lane reads its own fragment of it
     const int key = kw + kappa(c32);
     const int S = (int)a.S, S_pad = (int)a.S_pad;
     const int64_t hS = (int64_t)h * S_pad;
@@ -813,20 +813,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dkT[t] = zero16();
     }
     const int ql = kappa(c32);
-    // fp16 identity columns: lane (c32, g) holds 1.0 at k-value e when query
-    // 8g + e (first half of the stage) or 16 + 8g + e (second half) is c32
-    uint4 eye0, eye1;
-    {
-        uint32_t w0[4], w1[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int qa = 8 * g + 2 * e2;
-            w0[e2] = (c32 == qa ? 0x3c00u : 0u) | (c32 == qa + 1 ? 0x3c000000u : 0u);
-            w1[e2] = (c32 == qa + 16 ? 0x3c00u : 0u) | (c32 == qa + 17 ? 0x3c000000u : 0u);
-        }
-        eye0 = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-        eye1 = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-    }
     uint16_t *const dst_head = a.dst + (a.dst != nullptr ? (int64_t)h * a.dst_head : 0);
     const int kt = kw / 32; // this wave's key tile
     const int nst = (S - k0 + BQ - 1) / BQ;
@@ -992,14 +978,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             LH_FENCE;
         }
         const uint4 db0 = pack8h(ds), db1 = pack8h(ds + 8);
-        // dS of the tile (queries q0.., keys kw..) for the dQ kernel, query-major:
-        // C = dS^T(as rows keys) x identity puts query c32 in lane c32 with keys
-        // 16(v/8) + 8g + v%8 in register v (exact: fp16 times 1, fp32 sums of one
-        // term); then dK, with the tile's store behind its last products
+        // dK, with the stage's dS tile (queries q0.., keys kw..) stored for
+        // the dQ kernel behind its last products: key-major, the lane's key
+        // row of 32 queries is its two fp16 runs (queries 8g.. and 16 + 8g..)
         ga[0][2] = gfrag(0, 2);
         ga[0][3] = gfrag(0, 3);
-        f32x16_t tr = mfma32(db0, eye0, zero16());
-        tr = mfma32(db1, eye1, tr);
         LH_FENCE;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1009,18 +992,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             dkT[t] = mfma32(ga[t & 1][2], db0, dkT[t]);
             dkT[t] = mfma32(ga[t & 1][3], db1, dkT[t]);
-            if (t == NT - 1 && a.dst != nullptr) { // (the transposes have finished by now)
+            if (t == NT - 1 && a.dst != nullptr) {
                 const int qt = q0 / 32;
-                uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + c32 * 32 + 8 * g;
-                float t8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    t8[e] = tr[e];
-                store16_stream(row, pack8h(t8));
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    t8[e] = tr[8 + e];
-                store16_stream(row + 16, pack8h(t8));
+                uint16_t *row = dst_head + ((int64_t)qt * (qt + 1) / 2 + kt) * 1024 + ql * 32 + 8 * g;
+                store16_stream(row, db0);
+                store16_stream(row + 16, db1);
             }
             LH_FENCE;
         }
@@ -1083,17 +1059,18 @@ hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_
 }
 
 // ============================================================== backward: dQ
-// dQ = scale * dS K from the dS tiles the dK/dV kernel stored (query-major,
+// dQ = scale * dS K from the dS tiles the dK/dV kernel stored (key-major,
 // fp16: the values it used itself), so S and dP are not recomputed. One
 // workgroup per 128 queries (32 per wave), two workgroups per CU; K^T of 64
 // keys per stage (shared) and each wave's own dS tiles of the stage go
-// through a two-stage LDS ring. Per 32x32 tile: dQ^T += K^T dS^T, 8 MFMAs.
+// through a two-stage LDS ring. Per 32x32 tile: dQ^T += K^T dS^T, 8 MFMAs,
+// the dS^T operands read down the key-major tile's columns.
 template <int D>
 struct DqStage {
     static constexpr int BN = 64;
     static constexpr int TCH = BN / 8;          // chunks per K^T row
     static constexpr int KT = 0, KSIZE = D * TCH; // K^T [D][BN]
-    static constexpr int DS = KSIZE;            // dS: [wave][subtile][32 queries][4 chunks]
+    static constexpr int DS = KSIZE;            // dS: [wave][subtile][32 keys][32 queries]
     static constexpr int DSW = 2 * 32 * 4;      // chunks per wave
     static constexpr int SIZE = KSIZE + 4 * DSW;
     static constexpr int KU = KSIZE / 256;      // K^T load rounds
@@ -1128,12 +1105,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     const uint16_t *const kht = a.khi_t + (int64_t)h * D * a.S_pad;
     // this wave's dS tiles (qt, kt) are contiguous in kt; lane chunk = 16 B
     const uint16_t *const dsrow = a.dst + (int64_t)h * a.dst_head + (int64_t)qt * (qt + 1) / 2 * 1024;
-    // a 32x32 tile is 128 chunks (32 query rows of 4): two DMA rounds, the
-    // physical chunk of (row, c) is 4 row + (c ^ ((row >> 2) & 3)): the 16
-    // lanes an LDS read serves together (rows r..r+15 of one chunk column)
-    // then hit 16 distinct 16-byte bank groups
-    const uint32_t doff0 = 16u * (uint32_t)((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 4) & 3)));
-    const uint32_t doff1 = doff0 + 16u * 64u;
+    // a 32x32 tile is 128 chunks (32 key rows of 64 B): two DMA rounds, in
+    // order. The dS^T operand of lane (c32, g) is query c32 of keys 8g .. 8g+7
+    // (and 16 + 8g ..): two transposing reads each, lane 4R + m of 16-lane
+    // group G addressing key 8g + 4n + R (g = G >> 1), queries 16(G & 1) + 4m
+    // .. +3; a half wave reads four whole rows, so no bank is hit twice
+    const uint32_t doff0 = 16u * (uint32_t)lane, doff1 = doff0 + 16u * 64u;
+    uint32_t troff[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+        troff[n] = 64u * (uint32_t)(8 * g + 4 * n + ((lane >> 2) & 3)) + 2u * (uint32_t)(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     auto issue = [&](int64_t k0, const uint4 *base) {
 #pragma unroll
@@ -1172,9 +1153,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
             if (!live || ktile > qt)
                 break;
             // dS^T operand: query c32, keys 8g.. and 16 + 8g.. of the tile
-            const uint4 *dt = base + St::DS + wave * St::DSW + j * 128 + c32 * 4;
-            const int sw = (c32 >> 2) & 3;
-            const uint4 ds0 = dt[g ^ sw], ds1 = dt[(2 + g) ^ sw];
+            const uint4 *dt = base + St::DS + wave * St::DSW + j * 128;
+            const uint2 r0 = lds_tr16(dt, troff[0]), r1 = lds_tr16(dt, troff[1]);
+            const uint2 r2 = lds_tr16(dt, troff[0] + 1024u), r3 = lds_tr16(dt, troff[1] + 1024u);
+            const uint4 ds0 = make_uint4(r0.x, r0.y, r1.x, r1.y), ds1 = make_uint4(r2.x, r2.y, r3.x, r3.y);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int dim = 32 * t + c32;

@@ -34,7 +34,7 @@ enum InternalRegion {
     IR_DOLO,                // fp16 [H][S_pad][d]: lo part of dO_sub
     IR_DELTA,               // fp32 [H][S_pad]: rowsum(dO_sub * O_sub) * 2^-15
     IR_LSE15,               // fp32 [H][S_pad]: log2-domain LSE - 15
-    IR_DST,                 // fp16 [H][T(T+1)/2][32][32], T = S_pad/32: dS tiles (query-major), causal half
+    IR_DST,                 // fp16 [H][T(T+1)/2][32][32], T = S_pad/32: dS tiles (key-major), causal half
     IR_FPART,               // fp32 window sums [3][H][fpart_rows][d], then maxima [H][fpart_rows]
     IR_SPART,               // fp32 [H][spart_rows][d]: dO window sums (u-space)
     IR_QLO8,                // e4m3 [H][S_pad/32][32 d] (bf16 inputs): Q lo part, fp8 tiles
