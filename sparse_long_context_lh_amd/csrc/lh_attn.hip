@@ -821,7 +821,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // One stage in four phases, each a group of MFMAs with the vector work
     // that does not depend on them placed behind them (scheduling barriers
     // keep the order): S; dP with P = exp2(...) of the finished S; dV with
-    // dS = P (dP - delta); the dS transposes and dK with the dS tile store.
+    // dS = P (dP - delta); dK with the dS tile store.
     // MODE 0: every query of the stage precedes this wave's keys (nothing to
     // compute); 1: interior stage; 2: masked (diagonal, or reaching past S).
     auto stage = [&](int it, auto mode_flag) __attribute__((always_inline)) {
