@@ -366,6 +366,26 @@ def test_layer_with_projections(N, H, d, dm, L, p, k, dtype):
     fails.raise_if_any()
 
 
+def test_values_sharing_one_direction():
+    # Every value row is 16 c + v / 8 for one fixed row c: the values a query
+    # attends to nearly agree, so dP - delta, dS and dq are small by
+    # cancellation while |delta| is not, and the dq bound is mostly its
+    # absolute term. What P's fp16 rounding leaves in O_sub, and so in delta,
+    # is then what that bound sees: the precision study
+    # (tests/precision_study.py, emulating every row of this case) puts dQ_sub
+    # at 0.34-0.48 of the bound with the fp16 pair of P in the forward and at
+    # 1.4-1.9, 12-36 elements over, without its lo half. Top-level windows of
+    # 256 tokens, so dO_sub rows sum up to 256 rows of dO.
+    N, H, d, L, p, k = 65536, 2, 128, 5, 4, 256
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 8, 81)
+    c = torch.randn(d, generator=torch.Generator().manual_seed(7))
+    v = (16.0 * c + v.float() / 8).to(torch.bfloat16)
+    dout = make_dout(N, H, d, torch.bfloat16, 82)
+    say("case values sharing one direction: N=%d H=%d d=%d L=%d p=%d k=%d S=%d"
+        % (N, H, d, L, p, k, oracle.subseq_len(N, L, p, k)))
+    check_case(q.cuda(), kk.cuda(), v.cuda(), L, p, k, dout.cuda(), tag="shared-v")
+
+
 @pytest.mark.parametrize("N,L,p,k", [(16384, 3, 4, 64), (1000, 1, 2, 0)])
 def test_heads_scaled_far_outside_fp16(N, L, p, k):
     # head 0 has Q, V and dO times 2^12 and K times 2^-12, head 1 the reverse
