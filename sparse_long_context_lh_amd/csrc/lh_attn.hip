@@ -1061,28 +1061,32 @@ hipError_t launch_attn_bwd_dkdv(const Plan &pl, const AttnBwdArgs &a, hipStream_
 // ============================================================== backward: dQ
 // dQ = scale * dS K from the dS tiles the dK/dV kernel stored (key-major,
 // fp16: the values it used itself), so S and dP are not recomputed. One
-// workgroup per 128 queries (32 per wave), two workgroups per CU; K^T of 64
-// keys per stage (shared) and each wave's own dS tiles of the stage go
-// through a two-stage LDS ring. Per 32x32 tile: dQ^T += K^T dS^T, 8 MFMAs,
-// the dS^T operands read down the key-major tile's columns.
+// workgroup per 256 queries (eight waves of 32, one workgroup per CU): K^T of
+// 64 keys per stage, shared by the eight waves, and each wave's own dS tiles
+// of the stage go through a three-slot LDS ring with two stages in flight.
+// Per 32x32 tile: dQ^T += K^T dS^T, 8 MFMAs, the dS^T operands read down the
+// key-major tile's columns.
 template <int D>
 struct DqStage {
+    static constexpr int NW = 8;                  // waves per workgroup
     static constexpr int BN = 64;
-    static constexpr int TCH = BN / 8;          // chunks per K^T row
+    static constexpr int TCH = BN / 8;            // chunks per K^T row
     static constexpr int KT = 0, KSIZE = D * TCH; // K^T [D][BN]
-    static constexpr int DS = KSIZE;            // dS: [wave][subtile][32 keys][32 queries]
-    static constexpr int DSW = 2 * 32 * 4;      // chunks per wave
-    static constexpr int SIZE = KSIZE + 4 * DSW;
-    static constexpr int KU = KSIZE / 256;      // K^T load rounds
+    static constexpr int DS = KSIZE;              // dS: [wave][subtile][32 keys][32 queries]
+    static constexpr int DSW = 2 * 32 * 4;        // chunks per wave
+    static constexpr int SIZE = KSIZE + NW * DSW;
+    static constexpr int KU = KSIZE / (64 * NW);  // K^T load rounds
+    static constexpr int LOADS = KU + 4;          // transfers per thread and stage
+    static constexpr int NSLOT = 3;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a)
 {
     typedef DqStage<D> St;
-    constexpr int BM = 128, BN = St::BN, TCH = St::TCH;
+    constexpr int BM = 32 * St::NW, BN = St::BN, TCH = St::TCH;
     constexpr int NT = D / 32;
-    __shared__ uint4 ring[2 * St::SIZE];
+    __shared__ uint4 ring[St::NSLOT * St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -1099,7 +1103,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     uint32_t koff[St::KU];
 #pragma unroll
     for (int u = 0; u < St::KU; ++u) {
-        const int c = 256 * u + tid, dim = c / TCH;
+        const int c = 64 * St::NW * u + tid, dim = c / TCH;
         koff[u] = 2u * ((uint32_t)dim * (uint32_t)a.S_pad + (uint32_t)(swzg<TCH>(dim, c % TCH) * 8));
     }
     const uint16_t *const kht = a.khi_t + (int64_t)h * D * a.S_pad;
@@ -1116,20 +1120,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
     for (int n = 0; n < 2; ++n)
         troff[n] = 64u * (uint32_t)(8 * g + 4 * n + ((lane >> 2) & 3)) + 2u * (uint32_t)(16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-    auto issue = [&](int64_t k0, const uint4 *base) {
+    const int64_t kend = min(q0 + BM, a.S);
+    const int nkb = (int)((kend + BN - 1) / BN);
+    auto slot = [&](int kb) { return ring + (kb % St::NSLOT) * St::SIZE; };
+    // Every thread issues St::LOADS transfers per stage, so a count of the
+    // transfers in flight tells which stage has landed: past the last stage
+    // the last one is loaded again, and a wave whose query tile ends before a
+    // key tile loads its own diagonal tile (never read) in its place.
+    auto issue = [&](int kb) {
+        const uint4 *base = slot(kb);
+        const int kc = min(kb, nkb - 1);
 #pragma unroll
         for (int u = 0; u < St::KU; ++u)
-            dma16(kht + k0, koff[u], base + St::KT + 256 * u + 64 * wave);
-        // own dS tiles of the stage: key tiles k0/32 and k0/32 + 1, if at or before qt
+            dma16(kht + (int64_t)kc * BN, koff[u], base + St::KT + 64 * St::NW * u + 64 * wave);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int ktile = (int)(k0 / 32) + j;
-            if (live && ktile <= qt) {
-                const uint16_t *tb = dsrow + (int64_t)ktile * 1024;
-                const uint4 *lb = base + St::DS + wave * St::DSW + j * 128;
-                dma16_nt(tb, doff0, lb);
-                dma16_nt(tb, doff1, lb + 64);
-            }
+            const uint16_t *tb = dsrow + (int64_t)min(2 * kc + j, qt) * 1024;
+            const uint4 *lb = base + St::DS + wave * St::DSW + j * 128;
+            dma16_nt(tb, doff0, lb);
+            dma16_nt(tb, doff1, lb + 64);
         }
     };
 
@@ -1137,19 +1146,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         dqT[t] = zero16();
-    const int64_t kend = min(q0 + BM, a.S);
-    const int nkb = (int)((kend + BN - 1) / BN);
 
-    auto stage = [&](int kb) __attribute__((always_inline)) {
-        const uint4 *base = ring + (kb & 1) * St::SIZE;
-        const int64_t k0 = (int64_t)kb * BN;
-        wait_async();
-        lds_barrier(); // stage kb is visible to all waves; the other slot is free
-        if (kb + 1 < nkb)
-            issue(k0 + BN, ring + ((kb + 1) & 1) * St::SIZE);
+    issue(0);
+    issue(1);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const uint4 *base = slot(kb);
+        wait_async_n<St::LOADS>(); // stage kb has landed (kb + 1 may be in flight)
+        lds_barrier();             // ... visible to all waves; stage kb - 1's slot is free
+        issue(kb + 2);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int ktile = (int)(k0 / 32) + j;
+            const int ktile = 2 * kb + j;
             if (!live || ktile > qt)
                 break;
             // dS^T operand: query c32, keys 8g.. and 16 + 8g.. of the tile
@@ -1164,10 +1171,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnBwdArgs a)
                 dqT[t] = mfma32(base[St::KT + dim * TCH + swzg<TCH>(dim, 4 * j + 2 + g)], ds1, dqT[t]);
             }
         }
-    };
-    issue(0, ring);
-    for (int kb = 0; kb < nkb; ++kb)
-        stage(kb);
+    }
+    wait_async(); // the transfers past the last stage
 
     const int64_t query = qw + c32;
     float *dq = a.dq + (hS + query) * D;
@@ -1380,11 +1385,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
 }
 
 template <int D>
-static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, bool tiles, bool klo, hipStream_t s)
+static void launch_dq_t(const Plan &pl, const AttnBwdArgs &a, bool klo, hipStream_t s)
 {
-    if (tiles)
-        hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(256), 0, s, a);
-    else if (klo)
+    if (pl.ds_tiles) { // 32 * DqStage::NW queries per workgroup
+        constexpr int BM = 32 * DqStage<D>::NW;
+        const dim3 grid((unsigned)((pl.S + BM - 1) / BM) * pl.H);
+        hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(64 * DqStage<D>::NW), 0, s, a);
+        return;
+    }
+    const dim3 grid((unsigned)((pl.S + 127) / 128) * pl.H); // 128 queries per workgroup
+    if (klo)
         hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, true>), grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, false>), grid, dim3(256), 0, s, a);
@@ -1392,13 +1402,11 @@ static void launch_dq_t(const dim3 grid, const AttnBwdArgs &a, bool tiles, bool 
 
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
 {
-    const unsigned nqb = (unsigned)((pl.S + 127) / 128);
-    const dim3 grid(nqb * pl.H);
     const bool klo = pl.dt == LH_F32;
     if (pl.d == 128)
-        launch_dq_t<128>(grid, a, pl.ds_tiles, klo, s);
+        launch_dq_t<128>(pl, a, klo, s);
     else
-        launch_dq_t<64>(grid, a, pl.ds_tiles, klo, s);
+        launch_dq_t<64>(pl, a, klo, s);
     return hipGetLastError();
 }
 
