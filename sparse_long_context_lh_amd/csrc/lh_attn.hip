@@ -42,8 +42,8 @@
 // operands.
 //
 // The backward is split into a dK/dV kernel (one workgroup per 128 keys) and a
-// dQ kernel (one workgroup per 128 queries) so that no gradient needs atomics
-// and results are bitwise reproducible.
+// dQ kernel (one workgroup per block of queries) so that no gradient needs
+// atomics and results are bitwise reproducible.
 //
 // Scale: the gathered rows arrive multiplied by per-head powers of two 2^ex
 // (Q, K, V) and dO_sub by 2^ex_do, so that they fit fp16 whatever the inputs'
