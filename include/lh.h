@@ -129,7 +129,7 @@ int64_t lh_subseq_len(int64_t N, int L, int p, int k);
 /* Bytes of device workspace lh_forward + lh_backward need for this shape;
  * 0 if the shape is invalid. The dS tiles the backward stores for its dQ
  * kernel (the causal half of S x S per head, fp16: H * T(T+1)/2 * 2 KiB,
- * T = S_pad/32) are planned only while they fit the dS tile budget (16 GiB
+ * T = S_pad/32) are planned only while they fit the dS tile budget (32 GiB
  * unless set otherwise); beyond it the dQ kernel recomputes the logits and
  * dP instead, and the workspace grows as O(H S d) only. */
 size_t lh_workspace_bytes(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt);

@@ -18,10 +18,12 @@ constexpr int kSubseqAlign = 256;   // S is padded to this for the attention til
 constexpr int64_t kMaxN = int64_t(1) << 27;
 constexpr int kMaxHeads = 65535; // heads run along the grid's y dimension
 // Default largest workspace share of the backward's stored dS tiles (the
-// causal half of S x S per head, fp16). Above it the dQ kernel recomputes S
-// and dP from the gathered rows instead, and the workspace stays O(S d). The
-// process-wide value is set with lh_set_ds_tile_budget.
-constexpr size_t kDsTileBudgetDefault = size_t(16) << 30;
+// causal half of S x S per head, fp16; 32 GiB is about a ninth of the card's
+// memory, and at 16 heads holds the tiles up to S of about 46K). Above it the
+// dQ kernel recomputes S and dP from the gathered rows instead, and the
+// workspace stays O(S d). The process-wide value is set with
+// lh_set_ds_tile_budget.
+constexpr size_t kDsTileBudgetDefault = size_t(32) << 30;
 size_t ds_tile_budget();
 // Largest workspace a plan may ask for (64 TiB): shapes beyond it are reported
 // as unsupported rather than sized.

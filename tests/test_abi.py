@@ -193,7 +193,7 @@ def test_ds_tile_budget_sizes_the_workspace(L):
     T = S_pad // 32
     tiles = 2 * 16 * (T * (T + 1) // 2) * 1024
     old = L.lh_ds_tile_budget()
-    assert old == 16 << 30
+    assert old == 32 << 30
     full = L.lh_workspace_bytes(*shape)
     fwd = L.lh_forward_workspace_bytes(*shape)
     try:
