@@ -155,6 +155,23 @@ __device__ __forceinline__ int swzg(int row, int ch)
     return ch ^ ((row / (16 / NCH)) & (NCH - 1));
 }
 
+// The dK/dV kernel's row-major Q and dO tiles are read two ways: 16 lanes
+// read one chunk of 16 rows (operands of S and dP), and a transposing read
+// takes, per half wave, the same 4 consecutive chunks of 4 consecutive rows
+// (operands of dV and dK). XOR-ing a row's chunks with a rotation of its
+// 256-byte window index (the low bits, which differ between consecutive
+// rows, moved to the top) serves both: distinct windows of 16 rows get
+// distinct offsets, and 4 consecutive rows send their group of 4 chunks to 4
+// different groups, so neither read meets a bank conflict. (NCH: 16 chunks
+// per row at d = 128, 8 at d = 64.)
+template <int NCH>
+__device__ __forceinline__ int swzt(int row, int ch)
+{
+    constexpr int BITS = NCH == 16 ? 4 : 3, LOW = NCH == 16 ? 2 : 1;
+    const int x = (row / (16 / NCH)) & (NCH - 1);
+    return ch ^ (((x & ((1 << LOW) - 1)) << (BITS - LOW)) | (x >> LOW));
+}
+
 // ============================================================== forward
 // One workgroup per 128 queries (32 per wave, Q hi / lo fragments in
 // registers); keys stream through LDS 32 at a time in a three-stage ring
@@ -725,7 +742,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int c = 256 * u + tid, r = c / RCH;
-        roff[u] = 2u * (uint32_t)(r * D + swzg<RCH>(r, c % RCH) * 8);
+        roff[u] = 2u * (uint32_t)(r * D + swzt<RCH>(r, c % RCH) * 8);
     }
     // Byte offsets of this lane's transposing reads of the row-major Q and dO
     // hi tiles: the operand of dV (dO^T) and dK (Q^T) for dimensions
@@ -741,7 +758,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int t = 0; t < NT; ++t) {
                 const int G = lane >> 4, R = (lane >> 2) & 3, m = lane & 3;
                 const int q = 16 * hh + 8 * (G >> 1) + 4 * n + R, dim = 32 * t + 16 * (G & 1) + 4 * m;
-                toff[hh][n][t] = 2u * (uint32_t)(q * D + swzg<RCH>(q, dim >> 3) * 8 + (dim & 7));
+                toff[hh][n][t] = 2u * (uint32_t)(q * D + swzt<RCH>(q, dim >> 3) * 8 + (dim & 7));
             }
     const uint16_t *const rows[4] = {a.qhi, a.qlo, a.dohi, a.dolo};
     // each wave fetches 4 of the 16 lse / delta chunks (lanes 4..63 repeat
@@ -844,7 +861,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float *sL = reinterpret_cast<const float *>(base + St::LS);
         const float *sDel = sL + 2 * 256; // (waves 2, 3 of the statistics area)
         auto rd = [&](int s, int i) {
-            const int at = ql * RCH + swzg<RCH>(ql, 2 * s + g);
+            const int at = ql * RCH + swzt<RCH>(ql, 2 * s + g);
             return base[(i == 0 ? St::QH : i == 1 ? St::QL : i == 2 ? St::DH : St::DL) + at];
         };
         // operand of dV (i = 0, 1: dO^T) or dK (i = 2, 3: Q^T), dimensions
