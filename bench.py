@@ -59,11 +59,11 @@ KERNEL_STAGES = [
     (r"lh::k_head_exp\(", "head_exp"),      # once in the forward, once in the backward
     (r"lh::k_topk\(", "topk"),
     (r"lh::k_index\(", "index"),
-    (r"lh::k_(gather<|lo8<\d+, 0>)", "gather"),
+    (r"lh::k_gather<", "gather"),
     (r"lh::k_attn_fwd<", "attn_fwd"),
     (r"lh::k_pull<\d+, [^,]+, 1, 1,", "scatter"),
     (r"lh::k_scatter_bwd(_up)?<", "scatter_bwd"),
-    (r"lh::k_(bwd_prep<|rowmax<|lo8<\d+, 1>)", "bwd_prep"),
+    (r"lh::k_(bwd_prep<|rowmax<)", "bwd_prep"),
     (r"lh::k_attn_bwd_dkdv<", "attn_bwd_dkdv"),
     (r"lh::k_attn_bwd_dq(_rc)?<", "attn_bwd_dq"),
     (r"lh::k_pull<\d+, [^,]+, 3, 0,", "pool_bwd"),
@@ -110,14 +110,16 @@ def algorithmic(stage: str, w, S: int) -> float:
         return 4.0 * (lvl - N) * H + 4.0 * (w.L - 1) * w.k * H
     if stage == "index":           # read the selection; write order and slots of S entries
         return 4.0 * (w.L - 1) * w.k * H + 8.0 * S * H
-    if stage == "gather":          # read the gathered rows once, write the fp16 operands
-        return sub * s_io * 3.0 + sub * 2.0 * 8
+    if stage == "gather":          # read the gathered rows once, write the fp16 operands (Q, K pairs, V;
+        # Q hi, K hi, V transposed) and, for bf16 inputs, the e4m3 Q lo, K and V tiles
+        return sub * s_io * 3.0 + sub * 2.0 * 8 + (sub * 3.0 if w.dtype_name == "bf16" else 0.0)
     if stage == "scatter":         # read O_sub, write O
         return sub * 4.0 + N * d * H * s_io
     if stage == "scatter_bwd":     # read dO, write dO_sub
         return N * d * H * s_io + sub * 4.0
-    if stage == "bwd_prep":        # read dO_sub and O_sub, write the fp16 operands
-        return sub * 8.0 + sub * 2.0 * 3
+    if stage == "bwd_prep":        # read dO_sub, O_sub and the LSE; write the fp16 pair of dO_sub,
+        # delta and LSE - 15 and, for bf16 inputs, the e4m3 tile of the lo part
+        return sub * 8.0 + sub * 2.0 * 2 + 12.0 * S * H + (sub * 1.0 if w.dtype_name == "bf16" else 0.0)
     if stage == "pool_bwd":        # read dQ/dK/dV_sub, write dq, dk, dv
         return sub * 4.0 * 3 + 3.0 * N * d * H * s_io
     raise KeyError(stage)

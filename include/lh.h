@@ -51,9 +51,9 @@
  *     nothing. LH_EHIP means a launch failed; faults inside kernels surface at
  *     the caller's next synchronisation, as with any HIP call.
  *   - Results are deterministic and bitwise reproducible: no global-memory
- *     atomics anywhere on the layer's path (the top-K's digit histograms and
- *     two per-tile maxima use LDS integer atomics, whose results do not depend
- *     on their order). Calls on distinct workspaces may run concurrently.
+ *     atomics anywhere on the layer's path (the top-K's digit histograms use
+ *     LDS integer atomics, whose results do not depend on their order). Calls
+ *     on distinct workspaces may run concurrently.
  *   - Inputs must be finite, and so must the logits: |q.k| / sqrt(d) below
  *     2^23 (the softmax keeps its fp32 logits to within one unit, so larger
  *     ones round by more than the probabilities' fp16 range allows).
@@ -70,7 +70,8 @@
  * 22 significant bits, so pooled rows are not truncated before the softmax)
  * and fp16 key rows, plus the key's lo part for fp32 inputs; with bf16 inputs
  * the query lo product and the dO_sub lo product of dP run on block-scaled
- * fp8 (e4m3) copies with one power-of-two scale per head; P, V, dS and the
+ * fp8 (e4m3) copies with one fixed power-of-two scale per tensor (the
+ * per-head staging bounds their magnitudes); P, V, dS and the
  * fp16 hi/lo pair of dO_sub
  * feed the other products; row statistics, Delta = rowsum(dO_sub * O_sub) and
  * all sums are fp32. Outputs are rounded once to the input dtype.

@@ -172,8 +172,6 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[IR_FPART] = 4 * Hs * (size_t)pl->fpart_rows * (3 * D + 1);
     b[IR_SPART] = 4 * Hs * (size_t)pl->spart_rows * D;
     b[IR_QLO8] = b[IR_K8] = b[IR_V8] = b[IR_DOLO8] = Hs * Sp * D;
-    b[IR_TMAX] = 4 * 4 * Hs * (Sp / 32);
-    b[IR_SC8] = 4 * 4 * Hs;
     b[IR_XMAX] = 4 * 3 * Hs * (size_t)pl->nxmax;
     b[LH_R_EXP] = 4 * 4 * Hs;
     b[IR_DOMAX] = 4 * Hs * (Sp / kExpTile);
@@ -182,9 +180,9 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     // workspace that ends there; the regions only lh_backward writes follow.
     static const int kFwdOrder[] = {LH_R_SCORES, LH_R_SEL, LH_R_SLOT, LH_R_ENT, LH_R_QHI, LH_R_QLO, LH_R_KHI,
                                     LH_R_KLO, LH_R_V, LH_R_QHI_T, LH_R_KHI_T, LH_R_V_T, LH_R_OSUB, LH_R_LSE,
-                                    IR_TMAX, IR_SC8, LH_R_EXP, IR_QLO8, IR_K8, IR_POOLED, IR_FPART, IR_XMAX};
+                                    LH_R_EXP, IR_QLO8, IR_K8, IR_V8, IR_POOLED, IR_FPART, IR_XMAX};
     static const int kBwdOrder[] = {LH_R_DOSUB, LH_R_DQSUB, LH_R_DKSUB, LH_R_DVSUB, IR_DOHI, IR_DOLO,
-                                    IR_DELTA, IR_LSE15, IR_SPART, IR_V8, IR_DOLO8, IR_DOMAX, IR_DST};
+                                    IR_DELTA, IR_LSE15, IR_SPART, IR_DOLO8, IR_DOMAX, IR_DST};
     static_assert(sizeof(kFwdOrder) / sizeof(int) + sizeof(kBwdOrder) / sizeof(int) == IR_COUNT,
                   "every region placed once");
     size_t off = 0;
@@ -330,9 +328,11 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.hi_t[0] = at<uint16_t>(ws, pl, LH_R_QHI_T);
         ga.hi_t[1] = at<uint16_t>(ws, pl, LH_R_KHI_T);
         ga.hi_t[2] = at<uint16_t>(ws, pl, LH_R_V_T);
-        ga.tmax[0] = at<float>(ws, pl, IR_TMAX);
-        ga.tmax[1] = ga.tmax[0] + (int64_t)H * (pl.S_pad / 32);
-        ga.tmax[2] = ga.tmax[1] + (int64_t)H * (pl.S_pad / 32);
+        if (dt == LH_BF16) { // e4m3 copies for the fp8 products: Q lo and K hi (logits), V (dP)
+            ga.t8[0] = at<uint8_t>(ws, pl, IR_QLO8);
+            ga.t8[1] = at<uint8_t>(ws, pl, IR_K8);
+            ga.t8[2] = at<uint8_t>(ws, pl, IR_V8);
+        }
         ga.ex = at<int32_t>(ws, pl, LH_R_EXP);
         ga.N = N; ga.S = pl.S; ga.S_pad = pl.S_pad; ga.mat_rows = pl.mat_rows; ga.tensor_stride = tensor_stride;
         for (int l = 0; l < kMaxLevels; ++l) {
@@ -342,21 +342,6 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.H = H; ga.L = L; ga.log2p = pl.log2p;
         if (launch_gather(pl, ga, s) != hipSuccess)
             return LH_EHIP;
-        if (dt == LH_BF16) { // fp8 copies for the lo products of the logits
-            Lo8Args la;
-            la.src[0] = ga.lo[0];
-            la.src[1] = ga.hi[1];
-            la.tmax[0] = ga.tmax[0];
-            la.tmax[1] = ga.tmax[1];
-            la.dst[0] = at<uint8_t>(ws, pl, IR_QLO8);
-            la.dst[1] = at<uint8_t>(ws, pl, IR_K8);
-            la.sc[0] = at<int32_t>(ws, pl, IR_SC8);
-            la.sc[1] = la.sc[0] + H;
-            la.S_pad = pl.S_pad;
-            la.H = H;
-            if (launch_lo8(pl, la, 0, s) != hipSuccess)
-                return LH_EHIP;
-        }
     }
     record(events, 4, s);
     {
@@ -368,7 +353,6 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         aa.vt = at<uint16_t>(ws, pl, LH_R_V_T);
         aa.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
         aa.k8 = at<uint8_t>(ws, pl, IR_K8);
-        aa.sc8 = at<int32_t>(ws, pl, IR_SC8);
         aa.o = at<float>(ws, pl, LH_R_OSUB);
         aa.lse = at<float>(ws, pl, LH_R_LSE);
         aa.ex = at<int32_t>(ws, pl, LH_R_EXP);
@@ -447,28 +431,11 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
         a.delta = at<float>(ws, pl, IR_DELTA);
         a.lse = at<float>(ws, pl, LH_R_LSE);
         a.lse15 = at<float>(ws, pl, IR_LSE15);
-        float *tmax = at<float>(ws, pl, IR_TMAX);
-        const int64_t ntile = (int64_t)H * (pl.S_pad / 32);
-        a.tmax = pl.dt == LH_BF16 ? tmax + 3 * ntile : nullptr;
+        a.dolo8 = pl.dt == LH_BF16 ? at<uint8_t>(ws, pl, IR_DOLO8) : nullptr; // e4m3 copy of the lo part
         a.ex = at<int32_t>(ws, pl, LH_R_EXP);
         a.S = pl.S; a.S_pad = pl.S_pad; a.H = H;
         if (launch_bwd_prep(pl, a, s) != hipSuccess)
             return LH_EHIP;
-        if (pl.dt == LH_BF16) { // fp8 copies for the lo product of dP: the dO_sub lo part and V
-            Lo8Args la;
-            la.src[0] = a.dolo;
-            la.src[1] = at<uint16_t>(ws, pl, LH_R_V);
-            la.tmax[0] = tmax + 3 * ntile;
-            la.tmax[1] = tmax + 2 * ntile;
-            la.dst[0] = at<uint8_t>(ws, pl, IR_DOLO8);
-            la.dst[1] = at<uint8_t>(ws, pl, IR_V8);
-            la.sc[0] = at<int32_t>(ws, pl, IR_SC8) + 3 * H;
-            la.sc[1] = at<int32_t>(ws, pl, IR_SC8) + 2 * H;
-            la.S_pad = pl.S_pad;
-            la.H = H;
-            if (launch_lo8(pl, la, 1, s) != hipSuccess)
-                return LH_EHIP;
-        }
     }
     record(events, 2, s);
     AttnBwdArgs ab;
@@ -481,7 +448,6 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.k8 = at<uint8_t>(ws, pl, IR_K8);
     ab.v8 = at<uint8_t>(ws, pl, IR_V8);
     ab.dolo8 = at<uint8_t>(ws, pl, IR_DOLO8);
-    ab.sc8 = at<int32_t>(ws, pl, IR_SC8);
     ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);
     ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);
     ab.dolo = at<uint16_t>(ws, pl, IR_DOLO);

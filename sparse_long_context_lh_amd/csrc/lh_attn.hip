@@ -24,9 +24,10 @@
 // Precision: a logit is q_hi.k_hi + q_lo.k_hi over the fp16 pair q = hi + lo
 // of the gathered query row, plus q_hi.k_lo when the inputs are fp32. With
 // bf16 inputs the correction q_lo.k_hi runs on block-scaled fp8 copies of
-// q_lo and k_hi (one power-of-two scale per head and tensor): it carries the
-// query's low bits, and its own error sits about 2^-15 below the largest
-// |q_lo| |k| of the head, far under the fp16 hi product's. A
+// q_lo and k_hi (one fixed power-of-two scale per tensor, which the staging
+// bounds make safe: see kFp8Exp): it carries the query's low bits, and its own
+// error sits about 2^-15 below the largest |q_lo| |k| of the head, far under
+// the fp16 hi product's. A
 // query's rounding error shifts every logit of its row coherently, so its lo
 // part is needed; keys' rounding errors are independent and average out over
 // a row, except on the level-0 keys the selection concentrates attention on,
@@ -34,7 +35,7 @@
 // backward form the same logits, so both see the same P. dP uses the pair
 // of dO_sub: its hi part in fp16 products, its lo part as fp16 (fp32 inputs)
 // or, with bf16 inputs, as a block-scaled fp8 product against an e4m3 copy of
-// V (per-head scales again); the forward's P.V uses an fp16 pair of
+// V (fixed scales again); the forward's P.V uses an fp16 pair of
 // P (two products), so O_sub, and with it delta = rowsum(dO_sub * O_sub),
 // agree with the P the backward recomputes (dS = P (dP - delta) cancels
 // heavily when |dO_sub| is large). dS, V, the backward's P, dO_sub's hi part
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
         if constexpr (KLO)
             ql[s] = ld16(a.qlo + (hS + qw + c32) * D + 16 * s + 8 * g);
     }
-    int qs = 0, ks = 0; // scales of the head's fp8 Q lo and K tiles
+    int qs = 0, ks = 0; // scale bytes of the e4m3 Q lo and K tiles
     if constexpr (Q8) {
         const uint8_t *qt8 = a.qlo8 + (hS + qw) * D + 16 * (kappa(c32) + 32 * g);
 #pragma unroll
@@ -360,8 +361,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 q8[m][q] = *reinterpret_cast<const uint4 *>(qt8 + 2048 * m + 1024 * q);
-        qs = a.sc8[h];
-        ks = a.sc8[a.H + h];
+        qs = 127 + kFp8Exp[0];
+        ks = 127 + kFp8Exp[1];
     }
     // Consume the fragments here: otherwise the compiler waits for them at
     // their first use inside the key loop, in every iteration, and those
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_fwd(AttnFwdArgs a)
     if constexpr (Q8) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-            asm volatile("" ::"v"(q8[m][0].x), "v"(q8[m][1].x), "v"(qs), "v"(ks));
+            asm volatile("" ::"v"(q8[m][0].x), "v"(q8[m][1].x));
     }
     wait_async(); // stage 0 (its transfers were issued before the fragments)
     issue(1);
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     // bf16 inputs: this wave's fp8 K and V tiles as operand B (the tiles keep
     // key kw + kappa(c32) at lane position c32 + 32g: this lane's own position)
-    int ks = 0, qs = 0, vs = 0, ds8 = 0; // scales of the head's fp8 K, Q lo, V, dO lo tiles
+    int ks = 0, qs = 0, vs = 0, ds8 = 0; // scale bytes of the e4m3 K, Q lo, V, dO lo tiles
     if constexpr (!KLO) {
         const uint8_t *kt8 = a.k8 + (hS + kw) * D + 16 * lane;
         const uint8_t *vt8 = a.v8 + (hS + kw) * D + 16 * lane;
@@ -813,15 +814,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 k8r[m][q] = *reinterpret_cast<const uint4 *>(kt8 + 2048 * m + 1024 * q);
                 v8r[m][q] = *reinterpret_cast<const uint4 *>(vt8 + 2048 * m + 1024 * q);
             }
-        qs = a.sc8[h];
-        ks = a.sc8[a.H + h];
-        vs = a.sc8[2 * a.H + h];
-        ds8 = a.sc8[3 * a.H + h];
+        qs = 127 + kFp8Exp[0];
+        ks = 127 + kFp8Exp[1];
+        vs = 127 + kFp8Exp[2];
+        ds8 = 127 + kFp8Exp[3];
         // consume them here (see the forward kernel)
 #pragma unroll
         for (int m = 0; m < NM; ++m)
             asm volatile("" ::"v"(k8r[m][0].x), "v"(k8r[m][1].x), "v"(v8r[m][0].x), "v"(v8r[m][1].x));
-        asm volatile("" ::"v"(ks), "v"(qs), "v"(vs), "v"(ds8));
     }
     f32x16_t dvT[NT], dkT[NT];
 #pragma unroll
@@ -1316,10 +1316,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
                 q8[m][q] = *reinterpret_cast<const uint4 *>(a.qlo8 + t8 + 2048 * m + 1024 * q);
                 d8[m][q] = *reinterpret_cast<const uint4 *>(a.dolo8 + t8 + 2048 * m + 1024 * q);
             }
-        qs = a.sc8[h];
-        ks = a.sc8[a.H + h];
-        vs = a.sc8[2 * a.H + h];
-        ds8 = a.sc8[3 * a.H + h];
+        qs = 127 + kFp8Exp[0];
+        ks = 127 + kFp8Exp[1];
+        vs = 127 + kFp8Exp[2];
+        ds8 = 127 + kFp8Exp[3];
     }
     const int exq = a.ex[h], exk = a.ex[a.H + h], exv = a.ex[2 * a.H + h], exd = a.ex[3 * a.H + h];
     const float scale_log2 = ldexpf(a.scale_log2, -(exq + exk)); // staged rows: see the dK/dV kernel

@@ -10,7 +10,9 @@
 // attention kernels read as MFMA operands: queries and keys as an fp16 pair
 // (hi = fp16(x), lo = fp16(x - hi)) so the logits keep about 22 bits of the
 // pooled value, values as one fp16; row-major [S_pad][d] and, through an LDS
-// tile, the hi parts transposed [d][S_pad]. Positions past S are zero. Every
+// tile, the hi parts transposed [d][S_pad]; with bf16 inputs also e4m3
+// copies of the query's lo part, the key and the value rows, in operand-order
+// 32-row tiles with the fixed scales kFp8Exp. Positions past S are zero. Every
 // row is staged times its head's power-of-two scale 2^ex (see kExpTarget), so
 // that no input scale overflows fp16; the attention kernels undo it.
 #include "lh_device.h"
@@ -29,10 +31,9 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     constexpr int LD = D + 8; // LDS row pitch in bf16 (16 B pad)
     constexpr int CHUNK = 4;  // window rows in flight per tensor
     constexpr int NR = kGatherTile / NLG; // rows per lane group
-    constexpr bool F8 = DT == LH_BF16;    // fp8 tiles for the lo products (see lh_device.h)
+    constexpr bool F8 = DT == LH_BF16;    // e4m3 tiles for the lo products (see lh_device.h)
     __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
     __shared__ int32_t s_ent[kGatherTile];
-    __shared__ uint32_t s_amax[3][2]; // [Q lo, K hi, V][32-row tile]: largest magnitude (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
     const int lane = threadIdx.x % LANES;
@@ -41,8 +42,6 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
                        reinterpret_cast<const T *>(a.v)};
     if (threadIdx.x < kGatherTile)
         s_ent[threadIdx.x] = a.ent[(int64_t)h * a.S_pad + s0 + threadIdx.x];
-    if (threadIdx.x < 6)
-        s_amax[threadIdx.x >> 1][threadIdx.x & 1] = 0u;
     __syncthreads();
 
 #pragma unroll
@@ -116,28 +115,18 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
             } else {
                 hi = pack8_f16(x[t]);
             }
-            if constexpr (F8) { // largest magnitude of the fp16 lo part of Q, of K hi and of V
-                float v8[8], m8 = 0.0f;
+            if constexpr (F8) { // the e4m3 copy of the Q lo part, of K hi and of V, x * 2^-kFp8Exp[t]
+                float v8[8];
                 unpack8_f16(t == 0 ? lo : hi, v8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m8 = fmaxf(m8, fabsf(v8[e]));
-#pragma unroll
-                for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
-                    m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
-                if (lane == 0 && m8 > 0.0f) // (32-row tile NLG * ri / 32 of row r)
-                    atomicMax(&s_amax[t][NLG * ri / 32], __float_as_uint(m8));
+                const int64_t tile0 = ((int64_t)h * a.S_pad + (s & ~int64_t(31))) * D;
+                *reinterpret_cast<uint2 *>(a.t8[t] + tile0 + fp8_tile_offset((int)(s & 31), lane)) =
+                    pack8_fp8(v8, ldexpf(1.0f, -kFp8Exp[t]));
             }
             *reinterpret_cast<uint4 *>(a.hi[t] + off) = hi;
             *reinterpret_cast<uint4 *>(&tile[t][r * LD + lane * 8]) = hi;
         }
     }
     __syncthreads();
-
-    // per 32-row tile maxima for the fp8 copies (bf16 inputs; k_lo8 below)
-    if (F8 && threadIdx.x < 6)
-        a.tmax[threadIdx.x >> 1][(int64_t)h * (a.S_pad / 32) + s0 / 32 + (threadIdx.x & 1)] =
-            __uint_as_float(s_amax[threadIdx.x >> 1][threadIdx.x & 1]);
 
     // Transposed copy: 8 consecutive positions of one dimension per 16-byte store.
     constexpr int CH = kGatherTile / 8;
@@ -156,69 +145,6 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
         *reinterpret_cast<uint4 *>(a.hi_t[t] + ((int64_t)h * D + dim) * a.S_pad + s0 + sc * 8) =
             make_uint4(w[0], w[1], w[2], w[3]);
     }
-}
-
-// fp8 copies of two fp16 tensors for the block-scaled lo products (bf16
-// inputs; see lh_device.h): the gathered Q lo part and K hi part (logits), or
-// the dO_sub lo part and V (dP). One scale per head and tensor, from the
-// largest magnitude over the head's tile maxima; tiles of 32 rows in operand
-// order. One workgroup per 32-row tile of a head.
-template <int D, int WHICH> // (0: Q lo / K hi for the logits, 1: dO lo / V for dP; the same work)
-__global__ __launch_bounds__(256) void k_lo8(Lo8Args a)
-{
-    __shared__ float s_m[2][4];
-    const int h = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
-    const int ntile = (int)(a.S_pad / 32);
-    float m[2] = {0.0f, 0.0f};
-    for (int i = tid; i < ntile; i += 256)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            m[t] = fmaxf(m[t], a.tmax[t][(int64_t)h * ntile + i]);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            m[t] = fmaxf(m[t], __shfl_xor(m[t], o));
-        if ((tid & 63) == 0)
-            s_m[t][tid >> 6] = m[t];
-    }
-    __syncthreads();
-    int ex[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        ex[t] = fp8_scale_exp(fmaxf(fmaxf(s_m[t][0], s_m[t][1]), fmaxf(s_m[t][2], s_m[t][3])));
-    if (tile == 0 && tid < 2)
-        a.sc[tid][h] = 127 + ex[tid]; // every tile computes the same value
-    // 32 rows x D elements of each tensor, 8 elements per thread and step
-    constexpr int CH = D / 8;
-    for (int c = tid; c < 32 * CH; c += 256) {
-        const int rr = c / CH, ch = c % CH;
-        const int64_t row = (int64_t)h * a.S_pad + 32 * tile + rr;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float v8[8];
-            unpack8_f16(*reinterpret_cast<const uint4 *>(a.src[t] + row * D + 8 * ch), v8);
-            uint8_t *tb = a.dst[t] + ((int64_t)h * a.S_pad + 32 * tile) * D;
-            *reinterpret_cast<uint2 *>(tb + fp8_tile_offset(rr, ch)) = pack8_fp8(v8, ldexpf(1.0f, -ex[t]));
-        }
-    }
-}
-
-hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, int which, hipStream_t s)
-{
-    const dim3 grid((unsigned)(pl.S_pad / 32), pl.H);
-    if (pl.d == 128) {
-        if (which == 0)
-            hipLaunchKernelGGL((k_lo8<128, 0>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_lo8<128, 1>), grid, dim3(256), 0, s, a);
-    } else {
-        if (which == 0)
-            hipLaunchKernelGGL((k_lo8<64, 0>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_lo8<64, 1>), grid, dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
 }
 
 hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s)

@@ -43,8 +43,6 @@ enum InternalRegion {
     IR_K8,                  // e4m3 [H][S_pad/32][32 d] (bf16 inputs): K hi part, fp8 tiles
     IR_V8,                  // e4m3 [H][S_pad/32][32 d] (bf16 inputs): V, fp8 tiles
     IR_DOLO8,               // e4m3 [H][S_pad/32][32 d] (bf16 inputs): lo part of dO_sub, fp8 tiles
-    IR_TMAX,                // fp32 [4][H][S_pad/32]: largest magnitude of each Q lo / K hi / V / dO lo tile
-    IR_SC8,                 // int32 [4][H]: scale of a head's fp8 Q lo / K / V / dO lo tiles (127 + exponent)
     IR_XMAX,                // fp32 [3][H][nxmax]: largest |q|, |k| element and |v| row norm of each wave's input rows
     IR_DOMAX,               // fp32 [H][S_pad/64]: largest dO_sub row norm of each 64-row tile
     IR_COUNT
@@ -59,6 +57,15 @@ enum InternalRegion {
 // |dP| = |dO_sub . V| <= 2^9 2^5 and |dS| = |P (dP - delta)| <= 2^15 (fp16
 // holds 65504); pooled rows are means, so the inputs' maxima bound them.
 constexpr int kExpTarget[4] = {12, 12, 5, 9}; // Q, K (element), V, dO_sub (row norm)
+
+// The e4m3 copies of staged operands (bf16 inputs: the query's lo part, the
+// key rows, the value rows, dO_sub's lo part) hold x * 2^-e with a fixed e:
+// the staging above bounds each of them, and e takes that bound to 2^8 = 256,
+// inside e4m3's largest value 448. A staged query element is below 2^12, so
+// its lo part is at most half an fp16 ulp there, 2^0; keys are below 2^12;
+// values below 2^5 (their row norm is); dO_sub elements below 2^9, so its lo
+// part is at most 2^-3. The MFMA takes 127 + e as the scale byte.
+constexpr int kFp8Exp[4] = {kExpTarget[0] - 20, kExpTarget[1] - 8, kExpTarget[2] - 8, kExpTarget[3] - 20};
 constexpr int kExpTile = 64;                   // rows per tile of the dO_sub maxima
 
 // Row tiles of the front pass and of the scatter-back adjoint. A lane group
@@ -165,7 +172,7 @@ struct GatherArgs {
     uint16_t *hi[3];           // fp16 [H][S_pad][d]: Q hi, K hi, V
     uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
     uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
-    float *tmax[3];            // (bf16 inputs) per-tile maxima of the Q lo part, of K hi and of V
+    uint8_t *t8[3];            // bf16 inputs: e4m3 tiles of the Q lo part, K hi and V (else null)
     const int32_t *ex;         // LH_R_EXP: the rows are staged as x * 2^ex[t][h]
     int64_t N, S, S_pad, mat_rows, tensor_stride;
     int64_t mat_off[kMaxLevels];
@@ -173,19 +180,9 @@ struct GatherArgs {
     int H, L, log2p;
 };
 
-struct Lo8Args {
-    const uint16_t *src[2]; // fp16 [H][S_pad][d]: Q lo part and K hi part, or V and the dO_sub lo part
-    const float *tmax[2];   // [H][S_pad/32] tile maxima
-    uint8_t *dst[2];        // fp8 tiles [H][S_pad/32][32 d]
-    int32_t *sc[2];         // [H] each
-    int64_t S_pad;
-    int H;
-};
-
 struct AttnFwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *vt; // fp16 gathered rows (vt: [H][d][S_pad])
-    const uint8_t *qlo8, *k8;                   // bf16 inputs: fp8 tiles of the Q lo part and of K
-    const int32_t *sc8;                         // ... and their scales [2][H]
+    const uint8_t *qlo8, *k8;                   // bf16 inputs: e4m3 tiles of the Q lo part and of K (kFp8Exp)
     float *o;                           // [H][S_pad][d]
     float *lse;                         // [H][S_pad]
     const int32_t *ex;                  // LH_R_EXP: staged rows are q 2^ex_q, k 2^ex_k, v 2^ex_v
@@ -197,8 +194,7 @@ struct AttnFwdArgs {
 
 struct AttnBwdArgs {
     const uint16_t *qhi, *qlo, *khi, *klo, *v;   // fp16 gathered rows [H][S_pad][d]
-    const uint8_t *qlo8, *k8, *v8, *dolo8;       // bf16 inputs: fp8 tiles of the Q lo part, K, V, dO lo part
-    const int32_t *sc8;                          // ... and their scales [4][H]
+    const uint8_t *qlo8, *k8, *v8, *dolo8;       // bf16 inputs: e4m3 tiles of the Q lo part, K, V, dO lo part (kFp8Exp)
     const uint16_t *khi_t;                      // fp16 [H][d][S_pad]
     const uint16_t *dohi, *dolo;                // fp16 pair of dO_sub
     const float *lse, *delta;                        // [H][S_pad]: log2 LSE - 15, rowsum(dO o O) * 2^-15
@@ -239,7 +235,7 @@ struct BwdPrepArgs {
     float *delta;              // [H][S_pad]: rowsum * 2^-15
     const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
     float *lse15;              // [H][S_pad]: lse - 15
-    float *tmax;               // bf16 inputs: [H][S_pad/32] maxima of the lo part's tiles (else null)
+    uint8_t *dolo8;            // bf16 inputs: e4m3 tiles of the lo part (kFp8Exp[3]; else null)
     const int32_t *ex;         // LH_R_EXP: dO_sub is staged times 2^ex_do; delta is kept times 2^(ex_do + ex_v)
     int64_t S, S_pad;
     int H;
@@ -277,7 +273,6 @@ hipError_t launch_front(const Plan &pl, const FrontArgs &a, hipStream_t s);
 hipError_t launch_topk(const Plan &pl, const TopkArgs &a, hipStream_t s);
 hipError_t launch_index(const Plan &pl, const IndexArgs &a, hipStream_t s);
 hipError_t launch_gather(const Plan &pl, const GatherArgs &a, hipStream_t s);
-hipError_t launch_lo8(const Plan &pl, const Lo8Args &a, int which, hipStream_t s);
 hipError_t launch_attn_fwd(const Plan &pl, const AttnFwdArgs &a, hipStream_t s);
 hipError_t launch_scatter(const Plan &pl, const ScatterArgs &a, hipStream_t s);
 hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream_t s);

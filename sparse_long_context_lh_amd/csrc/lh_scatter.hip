@@ -450,13 +450,12 @@ hipError_t launch_scatter_bwd(const Plan &pl, const ScatterBwdArgs &a, hipStream
 // The attention backward works with probabilities scaled by 2^15 (kept out of
 // the fp16 underflow range): it reads delta_s * 2^-15 (an exact scaling) and
 // the log2-domain LSE minus 15, so that one fma gives the scaled exponent.
-// With bf16 inputs it also records the largest magnitude of the lo part in
-// each 32-row tile (for its fp8 copy, see k_lo8).
+// With bf16 inputs it also writes the e4m3 copy of the lo part (operand-order
+// 32-row tiles, fixed scale kFp8Exp[3]) for the block-scaled dP products.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
 {
     constexpr int LANES = D / 8, NLG = 256 / LANES;
-    __shared__ uint32_t s_amax[kPrepTile / 32]; // largest |lo| per 32-row tile (fp32 bits)
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kPrepTile;
     const int lane = threadIdx.x % LANES, lg = threadIdx.x / LANES;
@@ -464,9 +463,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
     // kept times 2^(ex_v - 15) (as the dS products see V times 2^ex_v)
     const float sdo = ldexpf(1.0f, a.ex[3 * a.H + h]);
     const float sdelta = ldexpf(1.0f, a.ex[2 * a.H + h] - 15);
-    if (threadIdx.x < kPrepTile / 32)
-        s_amax[threadIdx.x] = 0u;
-    __syncthreads();
     for (int r = lg; r < kPrepTile; r += NLG) {
         const int64_t s = s0 + r;
         const int64_t off = ((int64_t)h * a.S_pad + s) * D + lane * 8;
@@ -500,21 +496,12 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
         }
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
         *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
-        if (a.tmax) {
-            float m8 = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                m8 = fmaxf(m8, fabsf(xl[e]));
-#pragma unroll
-            for (int o = LANES / 2; o >= 1; o >>= 1) // over the row's lane group
-                m8 = fmaxf(m8, __shfl_xor(m8, o, LANES));
-            if (lane == 0 && m8 > 0.0f)
-                atomicMax(&s_amax[r / 32], __float_as_uint(m8));
+        if (a.dolo8 != nullptr) {
+            const int64_t tile0 = ((int64_t)h * a.S_pad + (s & ~int64_t(31))) * D;
+            *reinterpret_cast<uint2 *>(a.dolo8 + tile0 + fp8_tile_offset((int)(s & 31), lane)) =
+                pack8_fp8(xl, ldexpf(1.0f, -kFp8Exp[3]));
         }
     }
-    __syncthreads();
-    if (a.tmax && threadIdx.x < kPrepTile / 32)
-        a.tmax[(int64_t)h * (a.S_pad / 32) + s0 / 32 + threadIdx.x] = __uint_as_float(s_amax[threadIdx.x]);
 }
 
 // Largest dO_sub row norm of each 64-row tile of a head (rows past S are

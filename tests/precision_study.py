@@ -20,9 +20,10 @@ scheme the kernels use and for variants that drop one correction term:
 
 Staging follows the kernels: per-head powers of two bring the largest |q| and
 |k| element into [2^11, 2^12), the largest V row norm into [2^4, 2^5) and the
-largest dO_sub row norm into [2^8, 2^9); each e4m3 copy has one power-of-two
-scale per head, the smallest that keeps the head's largest magnitude within
-448; conversions round to nearest even. Left out: the fp32 summation order
+largest dO_sub row norm into [2^8, 2^9); each e4m3 copy holds x * 2^-e with
+one fixed e per tensor (FP8_EXP), which takes the bound the staging puts on
+that tensor to 256, inside e4m3's largest value 448; conversions round to
+nearest even. Left out: the fp32 summation order
 (products are added in fp64 here) and the bf16 rounding of the layer's outputs.
 
 --shared-v A replaces every value row by A c + v / 8, c one fixed N(0, 1)
@@ -89,12 +90,12 @@ def stage_exp(m: float, target: int) -> int:
     return (target - 1) - int(np.floor(np.log2(m)))
 
 
-def fp8_exp(amax: float) -> int:
-    """Smallest power of two e with amax / 2^e <= 448."""
-    e = int(np.ceil(np.log2(amax / 448.0)))
-    while amax / 2.0 ** e > 448.0:
-        e += 1
-    return e
+# Fixed scale exponents of the e4m3 copies. After staging, a query element is
+# below 2^12, so the lo part of its fp16 pair is at most half an fp16 ulp
+# there, 2^0; key elements are below 2^12; value elements below 2^5 (their row
+# norm is); dO_sub elements below 2^9, so its lo part is at most 2^-3. Each e
+# takes that bound to 2^8.
+FP8_EXP = {"q_lo": 0 - 8, "k": 12 - 8, "v": 5 - 8, "do_lo": -3 - 8}
 
 
 def head_inputs(w, h: int, shared_v: float = 0.0):
@@ -132,20 +133,22 @@ class Emulation:
         qs = f32(qt * 2.0 ** self.exq)
         self.q_hi = f16(qs)
         q_lo = f16(qs - self.q_hi)
-        self.sq = fp8_exp(np.abs(q_lo).max())
+        self.sq = FP8_EXP["q_lo"]
         self.q_lo8 = e4m3(q_lo / 2.0 ** self.sq)
         self.k16 = f16(f32(kt * 2.0 ** self.exk))
-        self.sk = fp8_exp(np.abs(self.k16).max())
+        self.sk = FP8_EXP["k"]
         self.k8 = e4m3(self.k16 / 2.0 ** self.sk)
         self.v16 = f16(f32(vt * 2.0 ** self.exv))
-        self.sv = fp8_exp(np.abs(self.v16).max())
+        self.sv = FP8_EXP["v"]
         self.v8 = e4m3(self.v16 / 2.0 ** self.sv)
         ds = f32(dot * 2.0 ** self.exd)
         self.do_hi = f16(ds)
         do_lo = f16(ds - self.do_hi)
-        self.sd = fp8_exp(np.abs(do_lo).max())
+        self.sd = FP8_EXP["do_lo"]
         self.do_lo8 = e4m3(do_lo / 2.0 ** self.sd)
         self.dot = dot
+        # the bounds above hold: no e4m3 copy reaches its largest value
+        self.fp8_peak = max(np.abs(x).max() for x in (self.q_lo8, self.k8, self.v8, self.do_lo8))
 
     def row(self, a: int, q_lo: bool, p_lo: bool, do_lo: bool):
         """O_sub and dQ_sub of sub-sequence row a under one variant."""

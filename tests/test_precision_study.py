@@ -26,7 +26,11 @@ def test_f16_rounding_fixed_points():
 def test_scale_exponents():
     assert ps.stage_exp(3.0, 12) == 10          # 3 * 2^10 in [2^11, 2^12)
     assert ps.stage_exp(2048.0, 12) == 0
-    assert ps.fp8_exp(448.0) == 0 and ps.fp8_exp(449.0) == 1 and ps.fp8_exp(1.0) == -8
+    # the largest staged magnitude of each e4m3 operand lands on 2^8 <= 448
+    assert ps.FP8_EXP == {"q_lo": -8, "k": 4, "v": -3, "do_lo": -11}
+    big = np.nextafter(np.float32(4096.0), np.float32(0.0))   # largest staged |q| below 2^12
+    q_lo = float(np.float32(big) - np.float32(ps.f16(big)))
+    assert abs(q_lo) <= 1.0 and abs(q_lo) / 2.0 ** ps.FP8_EXP["q_lo"] <= 256.0
 
 
 def test_emulated_scheme_small_workload():
@@ -48,5 +52,6 @@ def test_emulated_scheme_small_workload():
         for r, a in enumerate(rows):
             o[r], dq[r] = em.row(int(a), **flags)
         worst[name] = (np.max(np.abs(o - o_ref) / o_bound), np.max(np.abs(dq - dq_ref) / dq_bound))
+    assert em.fp8_peak <= 256.0
     assert worst["shipped"][0] < 1.0 and worst["shipped"][1] < 1.0
     assert worst["no-dO-lo"][1] >= worst["shipped"][1]
