@@ -60,9 +60,13 @@
  *
  * Range. Rows staged in fp16 for the attention (the gathered Q, K, V and
  * dO_sub) carry one power-of-two scale per head and tensor, chosen from the
- * head's largest values, and every result is scaled back exactly; inputs and
- * gradients may use bf16's whole range (pooled rows and gradient sums are
- * fp32).
+ * head's largest values, and every result is scaled back exactly, so inputs
+ * and gradients may lie far outside fp16's range (pooled rows and gradient
+ * sums are fp32). The scales cover a head whose largest |q| and |k| element
+ * is below 2^108 and whose value rows and dO_sub rows have norms below 2^64
+ * (their squares are summed in fp32, as are those of the norm scores);
+ * smaller magnitudes have no lower limit beyond fp16's subnormals, whose
+ * absolute error is far below the stated tolerance.
  *
  * Precision. Scores are fp32 in the stated order (bit-exact by design).
  * Pooling sums in fp32. The attention runs on fp16 matrix cores with fp32
@@ -173,7 +177,12 @@ lh_status lh_forward_scored(const void *q, const void *k, const void *v,
  * also adds the product with their fp16 residual so that O_sub agrees with
  * the probabilities the backward recomputes (delta = rowsum(dO_sub * O_sub)).
  * Each probability then carries a relative error up to 2^-11 (fp16 rounding)
- * before the fp32 accumulation; out stays within the forward's tolerance.
+ * before the fp32 accumulation, so an element (row, c) of one level's O_sub
+ * may move by up to 2^-11 times the largest |v[., c]| among the rows it
+ * attends, and out by up to L times that. On inputs of unit scale this stays
+ * well inside the forward's tolerance; with value rows some 30 times larger
+ * it reaches the tolerance's absolute term (lh_forward, with the fp16 pair
+ * of P, stays inside it there).
  * The context it leaves differs from lh_forward's only in O_sub; lh_backward
  * on it runs, but its gradients are not covered by the stated tolerance:
  * call lh_forward before a backward.

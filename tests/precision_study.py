@@ -14,6 +14,9 @@ scheme the kernels use and for variants that drop one correction term:
   no-P-lo    P.V with P * 2^15 rounded once to fp16 (O_sub, and with it
              delta = rowsum(dO_sub * O_sub), no longer carry the P the
              backward recomputes)
+  rounded-l  as no-P-lo, but the normaliser sums the fp16 values themselves,
+             so the weights that form O_sub sum to one and delta stays
+             consistent with them
   no-dO-lo   dP from dO_sub rounded once to fp16
   no-Q-lo    logits from the query row rounded once to fp16 (forward and
              backward, which share the logits)
@@ -29,7 +32,9 @@ nearest even. Left out: the fp32 summation order
 --shared-v A replaces every value row by A c + v / 8, c one fixed N(0, 1)
 row (shared by all tokens): the attended values then nearly agree, so dP -
 delta, dS and dQ are small by cancellation while |delta| is not, and the
-element-wise bound is mostly its absolute term.
+element-wise bound is mostly its absolute term. --v-scale F multiplies the
+value rows by F (a power of two: exact); the errors of P's rounding grow with
+them, the bound's absolute term does not.
 
 Rows: the R rows with the largest |dO_sub| (the entries whose dS = P (dP -
 delta) cancels most) and R rows drawn at random. Per variant the script prints
@@ -38,7 +43,7 @@ the largest error over those rows as a fraction of the parity tests' bounds,
     dQ_sub: |g - r| <= 2e-2 + 2^-7 max_row |r|
 (a fraction above 1 fails the bound), and the number of elements above it.
 
-    python tests/precision_study.py [--workload lh-fwdbwd-1m] [--head 0] [--rows 256] [--shared-v A]
+    python tests/precision_study.py [--workload lh-fwdbwd-1m] [--head 0] [--rows 256] [--shared-v A] [--v-scale F]
 """
 from __future__ import annotations
 
@@ -60,6 +65,7 @@ from synth_inputs import by_name, make_dout, make_qkv  # noqa: E402
 VARIANTS = {
     "shipped": dict(q_lo=True, p_lo=True, do_lo=True),
     "no-P-lo": dict(q_lo=True, p_lo=False, do_lo=True),
+    "rounded-l": dict(q_lo=True, p_lo=False, do_lo=True, l_rounded=True),
     "no-dO-lo": dict(q_lo=True, p_lo=True, do_lo=False),
     "no-Q-lo": dict(q_lo=False, p_lo=True, do_lo=True),
 }
@@ -98,7 +104,7 @@ def stage_exp(m: float, target: int) -> int:
 FP8_EXP = {"q_lo": 0 - 8, "k": 12 - 8, "v": 5 - 8, "do_lo": -3 - 8}
 
 
-def head_inputs(w, h: int, shared_v: float = 0.0):
+def head_inputs(w, h: int, shared_v: float = 0.0, v_scale: float = 1.0):
     q, k, v = make_qkv(w.N, w.H, w.d, w.dtype, w.n_plant, seed=0)
     dout = make_dout(w.N, w.H, w.d, w.dtype, seed=1)
     if shared_v:
@@ -106,7 +112,7 @@ def head_inputs(w, h: int, shared_v: float = 0.0):
         c = torch.randn(w.d, generator=torch.Generator().manual_seed(7))
         v = (shared_v * c[None, None, :] + v.float() / 8).to(w.dtype)
     f = lambda t: t[h].float().numpy().astype(np.float64)  # noqa: E731
-    return f(q), f(k), f(v), f(dout)
+    return f(q), f(k), f(v) * v_scale, f(dout)
 
 
 def subsequence(q, k, v, dout, w):
@@ -150,7 +156,7 @@ class Emulation:
         # the bounds above hold: no e4m3 copy reaches its largest value
         self.fp8_peak = max(np.abs(x).max() for x in (self.q_lo8, self.k8, self.v8, self.do_lo8))
 
-    def row(self, a: int, q_lo: bool, p_lo: bool, do_lo: bool):
+    def row(self, a: int, q_lo: bool, p_lo: bool, do_lo: bool, l_rounded: bool = False):
         """O_sub and dQ_sub of sub-sequence row a under one variant."""
         n = a + 1
         z = self.k16[:n] @ self.q_hi[a]
@@ -159,8 +165,8 @@ class Emulation:
         z = z * 2.0 ** -(self.exq + self.exk) / np.sqrt(self.d)
         m = z.max()
         p15 = f32(np.exp(z - m) * 2.0 ** 15)
-        lsum = p15.sum()
         p_hi = f16(p15)
+        lsum = p_hi.sum() if l_rounded else p15.sum()
         pv = p_hi + (f16(p15 - p_hi) if p_lo else 0.0)
         o = (pv @ self.v16[:n]) / lsum * 2.0 ** -self.exv
         lse = m + np.log(lsum * 2.0 ** -15)
@@ -181,10 +187,11 @@ def main():
     ap.add_argument("--head", type=int, default=0)
     ap.add_argument("--rows", type=int, default=256, help="rows of each kind (largest |dO_sub|, random)")
     ap.add_argument("--shared-v", type=float, default=0.0, help="value rows A c + v / 8 (see above)")
+    ap.add_argument("--v-scale", type=float, default=1.0, help="value rows times F (see above)")
     args = ap.parse_args()
     w = by_name(args.workload)
     t0 = time.time()
-    q, k, v, dout = head_inputs(w, args.head, args.shared_v)
+    q, k, v, dout = head_inputs(w, args.head, args.shared_v, args.v_scale)
     qt, kt, vt, dot = subsequence(q, k, v, dout, w)
     S = qt.shape[0]
     em = Emulation(q, k, v, qt, kt, vt, dot)
@@ -195,8 +202,9 @@ def main():
     rows = np.unique(np.concatenate([big, rnd]))
     o_ref, _ = oracle.attention_rows(qt, kt, vt, rows)
     dq_ref = oracle.attention_bwd_query_rows(qt, kt, vt, dot, rows)
-    print("%s%s, head %d: S = %d, %d rows (the %d of largest |dO_sub|, max %.0f, and %d random); staging 2^%d 2^%d 2^%d 2^%d"
-          % (w.name, ", value rows %g c + v / 8" % args.shared_v if args.shared_v else "", args.head, S, rows.shape[0], big.shape[0], np.linalg.norm(dot, axis=1).max(), rnd.shape[0],
+    print("%s%s%s, head %d: S = %d, %d rows (the %d of largest |dO_sub|, max %.0f, and %d random); staging 2^%d 2^%d 2^%d 2^%d"
+          % (w.name, ", value rows %g c + v / 8" % args.shared_v if args.shared_v else "",
+             ", value rows times %g" % args.v_scale if args.v_scale != 1.0 else "", args.head, S, rows.shape[0], big.shape[0], np.linalg.norm(dot, axis=1).max(), rnd.shape[0],
              em.exq, em.exk, em.exv, em.exd))
     o_bound = ATOL + RTOL * np.abs(o_ref)
     dq_bound = ATOL + RTOL * np.abs(dq_ref).max(axis=1, keepdims=True)

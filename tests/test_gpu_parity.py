@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import sparse_long_context_lh_amd as lh
-from parity import ATOL, RTOL, GpuRun, check_case, say
+from parity import ATOL, RTOL, GpuRun, assert_close, check_case, head_inputs, say
 from synth_inputs import make_dout, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -211,6 +211,33 @@ def test_forward_nograd(N, H, d, L, p, k, dtype):
     a, b = run.out.float(), full.out.float()
     say("  nograd vs lh_forward: max |out difference| %.3g" % (a - b).abs().max().item())
     assert bool(((a - b).abs() <= 2 * (ATOL + RTOL * b.abs())).all())
+
+
+def test_forward_nograd_large_values():
+    # lh_forward_nograd forms P.V from each probability rounded once to fp16
+    # (relative error at most 2^-11), so an element (row, c) of one level's
+    # O_sub moves by at most 2^-11 times the largest |v[:, c]| among the rows
+    # it attends, and out (a sum over at most L levels) by L times that. With
+    # value rows 32 times the seeded inputs (head 0; head 1: 1/32) that term
+    # is larger than the bound's absolute part, so the check adds it to the
+    # bound; the count over the plain bound is reported beside it.
+    N, H, d, L, p, k = 16384, 2, 128, 3, 4, 64
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 8, 11)
+    f = torch.tensor([32.0, 1.0 / 32.0]).view(H, 1, 1)  # powers of two: exact in bf16
+    v = (v.float() * f).to(torch.bfloat16)
+    say("case nograd, value rows times 32 and 1/32: N=%d H=%d d=%d L=%d p=%d k=%d" % (N, H, d, L, p, k))
+    run = GpuRun(q.cuda(), kk.cuda(), v.cuda(), L, p, k, nograd=True)
+    for h in range(H):
+        qh, kh, vh = head_inputs(q, h), head_inputs(kk, h), head_inputs(v, h)
+        ref = oracle.forward(qh, kh, vh, L, p, k)
+        extra = 2.0 ** -11 * np.abs(vh).max(axis=0, keepdims=True)  # per column c
+        osub = run.head("osub", h)[:run.S].numpy()
+        out = run.out[h].float().cpu().numpy()
+        st_o = assert_close(osub, ref["ot"], "nograd head %d O_sub" % h, atol=ATOL + extra)
+        st = assert_close(out, ref["out"], "nograd head %d output" % h, atol=ATOL + L * extra, stored_bf16=True)
+        plain = int((np.abs(out - ref["out"]) > ATOL + RTOL * np.abs(ref["out"])).sum())
+        say("  head %d: O_sub max-abs %.3g, out max-abs %.3g (largest |v| %.3g); %d outputs over the plain bound"
+            % (h, st_o["max_abs"], st["max_abs"], float(np.abs(vh).max()), plain))
 
 
 def test_selection_hook_and_forward_only_workspace():
