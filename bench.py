@@ -110,16 +110,17 @@ def algorithmic(stage: str, w, S: int) -> float:
         return 4.0 * (lvl - N) * H + 4.0 * (w.L - 1) * w.k * H
     if stage == "index":           # read the selection; write order and slots of S entries
         return 4.0 * (w.L - 1) * w.k * H + 8.0 * S * H
-    if stage == "gather":          # read the gathered rows once, write the fp16 operands (Q, K pairs, V;
-        # Q hi, K hi, V transposed) and, for bf16 inputs, the e4m3 Q lo, K and V tiles
-        return sub * s_io * 3.0 + sub * 2.0 * 8 + (sub * 3.0 if w.dtype_name == "bf16" else 0.0)
+    if stage == "gather":          # read the gathered rows once; write the fp16 operands (Q, K, V rows;
+        # K, V transposed) and the lo parts: fp32 inputs as fp16 (Q, K), bf16 as e4m3 tiles beside
+        # e4m3 copies of K and V
+        return sub * s_io * 3.0 + sub * 2.0 * 5 + (sub * 3.0 if w.dtype_name == "bf16" else sub * 2.0 * 2)
     if stage == "scatter":         # read O_sub, write O
         return sub * 4.0 + N * d * H * s_io
     if stage == "scatter_bwd":     # read dO, write dO_sub
         return N * d * H * s_io + sub * 4.0
-    if stage == "bwd_prep":        # read dO_sub, O_sub and the LSE; write the fp16 pair of dO_sub,
-        # delta and LSE - 15 and, for bf16 inputs, the e4m3 tile of the lo part
-        return sub * 8.0 + sub * 2.0 * 2 + 12.0 * S * H + (sub * 1.0 if w.dtype_name == "bf16" else 0.0)
+    if stage == "bwd_prep":        # read dO_sub, O_sub and the LSE; write dO_sub's fp16 hi part, its lo
+        # part (fp32 inputs: fp16; bf16: an e4m3 tile), delta and LSE - 15
+        return sub * 8.0 + sub * 2.0 + (sub * 1.0 if w.dtype_name == "bf16" else sub * 2.0) + 12.0 * S * H
     if stage == "pool_bwd":        # read dQ/dK/dV_sub, write dq, dk, dv
         return sub * 4.0 * 3 + 3.0 * N * d * H * s_io
     raise KeyError(stage)

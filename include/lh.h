@@ -296,10 +296,15 @@ lh_status lh_layer_backward(const void *x, const void *w_qkv, const void *dout, 
  *   LH_R_SLOT    int32 [H][sum_l n_l]  sub-sequence position of entry (l, i), or -1
  *   LH_R_ENT     int32 [H][S_pad]      entry at each position: (i << 3) | l; -1 past S
  *   LH_R_QHI/QLO fp16  [H][S_pad][d]   gathered query rows as an fp16 pair: hi =
- *                                      fp16(x), lo = fp16(x - hi) (pad rows zero)
- *   LH_R_KHI/KLO fp16  [H][S_pad][d]   the same for keys
+ *                                      fp16(x), lo = fp16(x - hi) (pad rows zero);
+ *                                      QLO is written for fp32 inputs only (size
+ *                                      0 for bf16, whose kernels take the lo
+ *                                      part from an internal e4m3 copy)
+ *   LH_R_KHI/KLO fp16  [H][S_pad][d]   the same for keys (KLO: fp32 inputs only)
  *   LH_R_V       fp16  [H][S_pad][d]   gathered value rows
- *   LH_R_QHI_T/KHI_T/V_T fp16 [H][d][S_pad]  transposes of QHI, KHI, V
+ *   LH_R_KHI_T/V_T fp16 [H][d][S_pad]  transposes of KHI and V
+ *   LH_R_QHI_T                         size 0: no kernel needs the transpose of
+ *                                      QHI (the id stays for compatibility)
  *   LH_R_OSUB    fp32  [H][S_pad][d]   attention output of the sub-sequence
  *   LH_R_LSE     fp32  [H][S_pad]      its row log-sum-exp in the log2 domain:
  *                                      log2 sum_b 2^(log2(e) q.k_b / sqrt(d))

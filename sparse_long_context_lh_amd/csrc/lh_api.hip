@@ -160,12 +160,18 @@ lh_status make_plan(int64_t N, int H, int d, int L, int p, int k, lh_dtype dt, P
     b[LH_R_ENT] = 4 * Hs * Sp;
     for (int r = LH_R_QHI; r <= LH_R_V_T; ++r)
         b[r] = 2 * Hs * Sp * D;
+    // no kernel reads Q^T; with bf16 inputs the lo parts of Q and dO_sub are
+    // kept as e4m3 tiles and K's is not used, so their fp16 copies are not made
+    b[LH_R_QHI_T] = 0;
+    if (pl->dt == LH_BF16)
+        b[LH_R_QLO] = b[LH_R_KLO] = 0;
     b[LH_R_OSUB] = 4 * Hs * Sp * D;
     b[LH_R_LSE] = 4 * Hs * Sp;
     b[LH_R_DOSUB] = 4 * Hs * Sp * D;
     b[LH_R_DQSUB] = b[LH_R_DKSUB] = b[LH_R_DVSUB] = 4 * Hs * Sp * D;
     b[IR_POOLED] = 4 * 3 * Hs * (size_t)pl->mat_rows * D;
-    b[IR_DOHI] = b[IR_DOLO] = 2 * Hs * Sp * D;
+    b[IR_DOHI] = 2 * Hs * Sp * D;
+    b[IR_DOLO] = pl->dt == LH_BF16 ? 0 : 2 * Hs * Sp * D;
     b[IR_DELTA] = 4 * Hs * Sp;
     b[IR_LSE15] = 4 * Hs * Sp;
     b[IR_DST] = pl->ds_tiles ? ds_bytes : 0;
@@ -323,11 +329,12 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
         ga.hi[0] = at<uint16_t>(ws, pl, LH_R_QHI);
         ga.hi[1] = at<uint16_t>(ws, pl, LH_R_KHI);
         ga.hi[2] = at<uint16_t>(ws, pl, LH_R_V);
-        ga.lo[0] = at<uint16_t>(ws, pl, LH_R_QLO);
-        ga.lo[1] = at<uint16_t>(ws, pl, LH_R_KLO);
-        ga.hi_t[0] = at<uint16_t>(ws, pl, LH_R_QHI_T);
-        ga.hi_t[1] = at<uint16_t>(ws, pl, LH_R_KHI_T);
-        ga.hi_t[2] = at<uint16_t>(ws, pl, LH_R_V_T);
+        if (dt == LH_F32) {
+            ga.lo[0] = at<uint16_t>(ws, pl, LH_R_QLO);
+            ga.lo[1] = at<uint16_t>(ws, pl, LH_R_KLO);
+        }
+        ga.hi_t[0] = at<uint16_t>(ws, pl, LH_R_KHI_T);
+        ga.hi_t[1] = at<uint16_t>(ws, pl, LH_R_V_T);
         if (dt == LH_BF16) { // e4m3 copies for the fp8 products: Q lo and K hi (logits), V (dP)
             ga.t8[0] = at<uint8_t>(ws, pl, IR_QLO8);
             ga.t8[1] = at<uint8_t>(ws, pl, IR_K8);
@@ -347,9 +354,9 @@ static lh_status forward_impl(const void *q, const void *k, const void *v, int64
     {
         AttnFwdArgs aa;
         aa.qhi = at<uint16_t>(ws, pl, LH_R_QHI);
-        aa.qlo = at<uint16_t>(ws, pl, LH_R_QLO);
+        aa.qlo = dt == LH_F32 ? at<uint16_t>(ws, pl, LH_R_QLO) : nullptr; // fp32 inputs only
         aa.khi = at<uint16_t>(ws, pl, LH_R_KHI);
-        aa.klo = at<uint16_t>(ws, pl, LH_R_KLO);
+        aa.klo = dt == LH_F32 ? at<uint16_t>(ws, pl, LH_R_KLO) : nullptr;
         aa.vt = at<uint16_t>(ws, pl, LH_R_V_T);
         aa.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
         aa.k8 = at<uint8_t>(ws, pl, IR_K8);
@@ -427,7 +434,8 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     {
         BwdPrepArgs a;
         a.dosub = dosub; a.osub = at<float>(ws, pl, LH_R_OSUB);
-        a.dohi = at<uint16_t>(ws, pl, IR_DOHI); a.dolo = at<uint16_t>(ws, pl, IR_DOLO);
+        a.dohi = at<uint16_t>(ws, pl, IR_DOHI);
+        a.dolo = pl.dt == LH_F32 ? at<uint16_t>(ws, pl, IR_DOLO) : nullptr;
         a.delta = at<float>(ws, pl, IR_DELTA);
         a.lse = at<float>(ws, pl, LH_R_LSE);
         a.lse15 = at<float>(ws, pl, IR_LSE15);
@@ -440,9 +448,9 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     record(events, 2, s);
     AttnBwdArgs ab;
     ab.qhi = at<uint16_t>(ws, pl, LH_R_QHI);
-    ab.qlo = at<uint16_t>(ws, pl, LH_R_QLO);
+    ab.qlo = pl.dt == LH_F32 ? at<uint16_t>(ws, pl, LH_R_QLO) : nullptr; // fp32 inputs only
     ab.khi = at<uint16_t>(ws, pl, LH_R_KHI);
-    ab.klo = at<uint16_t>(ws, pl, LH_R_KLO);
+    ab.klo = pl.dt == LH_F32 ? at<uint16_t>(ws, pl, LH_R_KLO) : nullptr;
     ab.v = at<uint16_t>(ws, pl, LH_R_V);
     ab.qlo8 = at<uint8_t>(ws, pl, IR_QLO8);
     ab.k8 = at<uint8_t>(ws, pl, IR_K8);
@@ -450,7 +458,7 @@ static lh_status backward_impl(const void *dout, int64_t N, int H, int d, int L,
     ab.dolo8 = at<uint8_t>(ws, pl, IR_DOLO8);
     ab.khi_t = at<uint16_t>(ws, pl, LH_R_KHI_T);
     ab.dohi = at<uint16_t>(ws, pl, IR_DOHI);
-    ab.dolo = at<uint16_t>(ws, pl, IR_DOLO);
+    ab.dolo = pl.dt == LH_F32 ? at<uint16_t>(ws, pl, IR_DOLO) : nullptr;
     ab.lse = at<float>(ws, pl, IR_LSE15);
     ab.delta = at<float>(ws, pl, IR_DELTA);
     ab.dq = at<float>(ws, pl, LH_R_DQSUB);

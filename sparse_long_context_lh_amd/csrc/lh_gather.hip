@@ -7,12 +7,13 @@
 // pooled rows: level 0 is the input row itself; a materialised level is
 // copied from the front pass (fp32); any other level is averaged here from
 // its p^l input rows (fp32 sum). Rows go out as fp16, the layouts the
-// attention kernels read as MFMA operands: queries and keys as an fp16 pair
-// (hi = fp16(x), lo = fp16(x - hi)) so the logits keep about 22 bits of the
-// pooled value, values as one fp16; row-major [S_pad][d] and, through an LDS
-// tile, the hi parts transposed [d][S_pad]; with bf16 inputs also e4m3
-// copies of the query's lo part, the key and the value rows, in operand-order
-// 32-row tiles with the fixed scales kFp8Exp. Positions past S are zero. Every
+// attention kernels read as MFMA operands: query, key and value rows as fp16
+// (hi = fp16(x)), row-major [S_pad][d], and through an LDS tile the key and
+// value rows transposed [d][S_pad]. The query's lo part lo = fp16(x - hi)
+// keeps the logits at about 22 bits of the pooled value: with fp32 inputs it
+// goes out as fp16 (and so does the key's), with bf16 inputs as an e4m3 copy
+// in operand-order 32-row tiles (fixed scale kFp8Exp), beside e4m3 copies of
+// the key and value rows. Positions past S are zero. Every
 // row is staged times its head's power-of-two scale 2^ex (see kExpTarget), so
 // that no input scale overflows fp16; the attention kernels undo it.
 #include "lh_device.h"
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
     constexpr int CHUNK = 4;  // window rows in flight per tensor
     constexpr int NR = kGatherTile / NLG; // rows per lane group
     constexpr bool F8 = DT == LH_BF16;    // e4m3 tiles for the lo products (see lh_device.h)
-    __shared__ __attribute__((aligned(16))) uint16_t tile[3][kGatherTile * LD];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kGatherTile * LD]; // K hi, V for the transposes
     __shared__ int32_t s_ent[kGatherTile];
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * kGatherTile;
@@ -108,10 +109,11 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 x[t][e] *= sc;
-            uint4 hi, lo;
-            if (t < 2) {
+            uint4 hi, lo = make_uint4(0u, 0u, 0u, 0u);
+            if (t == 0 || (!F8 && t == 1)) {
                 split8_f16(x[t], hi, lo);
-                *reinterpret_cast<uint4 *>(a.lo[t] + off) = lo;
+                if constexpr (!F8) // fp32 inputs: the fp16 lo parts (bf16: Q's lo part as the e4m3 tile below)
+                    *reinterpret_cast<uint4 *>(a.lo[t] + off) = lo;
             } else {
                 hi = pack8_f16(x[t]);
             }
@@ -123,14 +125,16 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a)
                     pack8_fp8(v8, ldexpf(1.0f, -kFp8Exp[t]));
             }
             *reinterpret_cast<uint4 *>(a.hi[t] + off) = hi;
-            *reinterpret_cast<uint4 *>(&tile[t][r * LD + lane * 8]) = hi;
+            if (t > 0)
+                *reinterpret_cast<uint4 *>(&tile[t - 1][r * LD + lane * 8]) = hi;
         }
     }
     __syncthreads();
 
-    // Transposed copy: 8 consecutive positions of one dimension per 16-byte store.
+    // Transposed copies of K hi and V (the dQ kernel's and the forward's P.V
+    // operands): 8 consecutive positions of one dimension per 16-byte store.
     constexpr int CH = kGatherTile / 8;
-    for (int c = threadIdx.x; c < 3 * D * CH; c += 256) {
+    for (int c = threadIdx.x; c < 2 * D * CH; c += 256) {
         const int t = c / (D * CH);
         const int rem = c - t * D * CH;
         const int dim = rem / CH;

@@ -170,8 +170,8 @@ struct GatherArgs {
     const float *pooled;       // [3][H][mat_rows][d]
     const int32_t *ent;        // [H][S_pad]
     uint16_t *hi[3];           // fp16 [H][S_pad][d]: Q hi, K hi, V
-    uint16_t *lo[2];           // fp16 [H][S_pad][d]: Q lo, K lo
-    uint16_t *hi_t[3];         // fp16 [H][d][S_pad]: transposes of hi[]
+    uint16_t *lo[2];           // fp32 inputs: fp16 [H][S_pad][d] Q lo, K lo (bf16 inputs: null)
+    uint16_t *hi_t[2];         // fp16 [H][d][S_pad]: transposes of K hi and V
     uint8_t *t8[3];            // bf16 inputs: e4m3 tiles of the Q lo part, K hi and V (else null)
     const int32_t *ex;         // LH_R_EXP: the rows are staged as x * 2^ex[t][h]
     int64_t N, S, S_pad, mat_rows, tensor_stride;
@@ -231,7 +231,7 @@ struct ScatterBwdArgs {
 
 struct BwdPrepArgs {
     const float *dosub, *osub;       // [H][S_pad][d]
-    uint16_t *dohi, *dolo;           // fp16 pair
+    uint16_t *dohi, *dolo;           // fp16 pair (dolo: fp32 inputs; bf16: null, the e4m3 tile instead)
     float *delta;              // [H][S_pad]: rowsum * 2^-15
     const float *lse;          // [H][S_pad]: log2-domain LSE of the forward
     float *lse15;              // [H][S_pad]: lse - 15

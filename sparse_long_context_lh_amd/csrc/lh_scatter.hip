@@ -495,7 +495,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a)
             a.lse15[(int64_t)h * a.S_pad + s] = s < a.S ? a.lse[(int64_t)h * a.S_pad + s] - 15.0f : 0.0f;
         }
         *reinterpret_cast<uint4 *>(a.dohi + off) = hi;
-        *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
+        if (a.dolo != nullptr) // fp32 inputs (bf16: the lo part as the e4m3 tile below)
+            *reinterpret_cast<uint4 *>(a.dolo + off) = lo;
         if (a.dolo8 != nullptr) {
             const int64_t tile0 = ((int64_t)h * a.S_pad + (s & ~int64_t(31))) * D;
             *reinterpret_cast<uint2 *>(a.dolo8 + tile0 + fp8_tile_offset((int)(s & 31), lane)) =

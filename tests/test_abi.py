@@ -103,6 +103,18 @@ def test_workspace_regions_disjoint(L):
     assert L.lh_region_info(*shape, len(REGIONS), ctypes.byref(off), ctypes.byref(nb)) == 1
 
 
+def test_unused_fp16_copies_take_no_space(L):
+    # no kernel reads Q hi transposed; with bf16 inputs the lo parts of Q and
+    # K exist only as the library's internal e4m3 tiles (Q) or not at all (K)
+    from sparse_long_context_lh_amd.binding import REGIONS
+    for dt, lo_bytes in ((0, 0), (1, 2 * 4 * 2048 * 64)):
+        shape = (4096, 4, 64, 3, 2, 256, dt)
+        assert _region(L, shape, REGIONS.index("qhi_t"))[1] == 0
+        assert _region(L, shape, REGIONS.index("khi_t"))[1] == 2 * 4 * 2048 * 64
+        assert _region(L, shape, REGIONS.index("qlo"))[1] == lo_bytes
+        assert _region(L, shape, REGIONS.index("klo"))[1] == lo_bytes
+
+
 def test_stage_names(L):
     from sparse_long_context_lh_amd import binding
     assert binding.stage_names(False) == ["front", "topk", "index", "gather", "attn_fwd", "scatter"]
