@@ -23,12 +23,18 @@
 
 namespace lh {
 
-__global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
+constexpr int kTopkThreads = 256;
+constexpr int kTopkPer = kStratum / kTopkThreads; // entries per thread
+constexpr int kTopkWaves = kTopkThreads / 64;
+static_assert(kStratum % kTopkThreads == 0, "a stratum fills whole chunks of the workgroup");
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk(TopkArgs a)
 {
-    constexpr int NW = 16; // waves of the workgroup
-    static_assert(kStratum == 2 * 1024, "two entries per thread");
-    __shared__ int hist[NW][256]; // per-wave digit counts (no contention across waves)
-    __shared__ int wave_count[NW];
+    constexpr int NW = kTopkWaves, U = kTopkPer;
+    // per-wave digit counts (no contention across waves), two buffers: the
+    // next pass's is cleared while this pass's is scanned
+    __shared__ int hist[2][NW][256];
+    __shared__ int s_cnt[U][NW]; // compaction: (above T) << 16 | (equal to T), per chunk and wave
     __shared__ int s_dig, s_need;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
@@ -43,12 +49,13 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
     const float *s = a.scores + (int64_t)h * a.lvl_total + a.lvl_off[l] + base;
 
     // Scores are non-negative, so their bit patterns order like the values.
-    // Entry tid and entry tid + 1024 of the stratum.
-    uint32_t v[2];
-    bool valid[2];
+    // Entry tid + 256 u of the stratum (chunk u, ascending index order is
+    // chunk, then wave, then lane).
+    uint32_t v[U];
+    bool valid[U];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int e = tid + 1024 * u;
+    for (int u = 0; u < U; ++u) {
+        const int e = tid + kTopkThreads * u;
         valid[u] = e < m;
         v[u] = valid[u] ? __float_as_uint(s[e]) : 0u;
     }
@@ -60,16 +67,17 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
     uint32_t T = 0u;
     int r = 0;
     if (q > 0) { // (uniform)
+        for (int i = tid; i < 2 * NW * 256; i += kTopkThreads)
+            (&hist[0][0][0])[i] = 0;
+        __syncthreads();
         uint32_t prefix = 0u, mask = 0u;
         int need = q;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < NW * 256; i += 1024)
-                (&hist[0][0])[i] = 0;
-            __syncthreads();
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass, b = pass & 1;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < U; ++u)
                 if (valid[u] && (v[u] & mask) == prefix)
-                    atomicAdd(&hist[wave][(v[u] >> shift) & 255u], 1);
+                    atomicAdd(&hist[b][wave][(v[u] >> shift) & 255u], 1);
             __syncthreads();
             if (wave == 0) {
                 // lane owns digits 4 lane .. 4 lane + 3; suf = entries with a
@@ -78,8 +86,9 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     int x = 0;
+#pragma unroll
                     for (int w = 0; w < NW; ++w)
-                        x += hist[w][4 * lane + j];
+                        x += hist[b][w][4 * lane + j];
                     cnt[j] = x;
                     tot += x;
                 }
@@ -103,6 +112,10 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
                     s_dig = 4 * lane + dsel;
                     s_need = need - acc;
                 }
+            } else if (pass < 3) {
+                // the other buffer was last scanned before the previous barrier
+                for (int i = tid - 64; i < NW * 256; i += kTopkThreads - 64)
+                    (&hist[b ^ 1][0][0])[i] = 0;
             }
             __syncthreads();
             prefix |= (uint32_t)s_dig << shift;
@@ -113,48 +126,44 @@ __global__ __launch_bounds__(1024) void k_topk(TopkArgs a)
         r = need;
     }
 
-    // Ballot compaction in ascending index order, 1024 entries per pass: an
-    // entry is kept if its score is above T, or equal to T with fewer than r
-    // equal ones before it.
+    // Compaction in ascending index order: every entry above T is kept, and
+    // the first r entries equal to T. The kept entries before entry e are
+    // (entries above T before e) + min(entries equal to T before e, r), so one
+    // exchange of per-wave counts places every entry.
+    uint64_t ab[U], tb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        ab[u] = __ballot(q > 0 && valid[u] && v[u] > T);
+        tb[u] = __ballot(q > 0 && valid[u] && v[u] == T);
+        if (lane == 0)
+            s_cnt[u][wave] = (__popcll(ab[u]) << 16) | __popcll(tb[u]);
+    }
+    __syncthreads();
     // selections are stored level-major, [L-1][H][k]
     int32_t *sel = a.sel + ((int64_t)(l - 1) * gridDim.y + h) * a.k + (int64_t)c * (a.k / C) + min(c, a.k % C);
     int32_t *child_slot = a.slot + (int64_t)h * a.lvl_total + a.lvl_off[l - 1];
     const int p = 1 << a.log2p;
-    int done = 0, tied = 0;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int run = 0; // packed counts of every (chunk, wave) before this wave's part of chunk u
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        if (1024 * u >= m) // (uniform)
-            break;
-        const int e = tid + 1024 * u;
-        const bool tie = q > 0 && valid[u] && v[u] == T;
-        const uint64_t tb = __ballot(tie);
-        if (lane == 0)
-            wave_count[wave] = __popcll(tb);
-        __syncthreads();
-        int tie_rank = tied + __popcll(tb & ((1ull << lane) - 1ull)), ties = 0;
+    for (int u = 0; u < U; ++u) {
+        int pre = run;
+#pragma unroll
         for (int w = 0; w < NW; ++w) {
-            tie_rank += w < wave ? wave_count[w] : 0;
-            ties += wave_count[w];
+            const int x = s_cnt[u][w];
+            pre += w < wave ? x : 0;
+            run += x;
         }
-        __syncthreads();
-        const bool keep = q > 0 && valid[u] && (v[u] > T || (tie && tie_rank < r));
-        const uint64_t kb = __ballot(keep);
-        if (lane == 0)
-            wave_count[wave] = __popcll(kb);
-        __syncthreads();
-        int before = done + __popcll(kb & ((1ull << lane) - 1ull)), total = 0;
-        for (int w = 0; w < NW; ++w) {
-            before += w < wave ? wave_count[w] : 0;
-            total += wave_count[w];
-        }
-        if (keep)
-            sel[before] = (int32_t)(base + e);
+        const int above_before = (pre >> 16) + __popcll(ab[u] & lt);
+        const int ties_before = (pre & 0xffff) + __popcll(tb[u] & lt);
+        const bool keep = ((ab[u] >> lane) & 1ull) || (((tb[u] >> lane) & 1ull) && ties_before < r);
+        const int e = tid + kTopkThreads * u;
+        const int pos = above_before + min(ties_before, r); // < q for a kept entry
+        if (keep && pos < q)
+            sel[pos] = (int32_t)(base + e);
         if (valid[u] && !keep)
             for (int cc = 0; cc < p; ++cc)
                 child_slot[((base + e) << a.log2p) + cc] = -1;
-        done += total;
-        tied += ties;
-        __syncthreads();
     }
 }
 
@@ -162,12 +171,13 @@ hipError_t launch_topk(const Plan &pl, const TopkArgs &a, hipStream_t s)
 {
     if (pl.L < 2 || pl.strata_total == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_topk, dim3(pl.strata_total, pl.H), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_topk, dim3(pl.strata_total, pl.H), dim3(kTopkThreads), 0, s, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- causal order
-constexpr int kIndexPerBlock = 1024;
+// one position per thread: at 10K-20K positions per head the grid still fills the chip
+constexpr int kIndexPerBlock = 256;
 
 __global__ __launch_bounds__(256) void k_index(IndexArgs a)
 {
