@@ -74,10 +74,29 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(TopkArgs a)
         int need = q;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass, b = pass & 1;
+            // a thread's entries with equal digits are counted together first:
+            // in the first passes most entries share a digit, and LDS atomics
+            // to one address serialise
+            bool live[U];
+            uint32_t dg[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (valid[u] && (v[u] & mask) == prefix)
-                    atomicAdd(&hist[b][wave][(v[u] >> shift) & 255u], 1);
+            for (int u = 0; u < U; ++u) {
+                live[u] = valid[u] && (v[u] & mask) == prefix;
+                dg[u] = (v[u] >> shift) & 255u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!live[u])
+                    continue;
+                int n = 1;
+#pragma unroll
+                for (int u2 = u + 1; u2 < U; ++u2)
+                    if (live[u2] && dg[u2] == dg[u]) {
+                        ++n;
+                        live[u2] = false;
+                    }
+                atomicAdd(&hist[b][wave][dg[u]], n);
+            }
             __syncthreads();
             if (wave == 0) {
                 // lane owns digits 4 lane .. 4 lane + 3; suf = entries with a

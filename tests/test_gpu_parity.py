@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import sparse_long_context_lh_amd as lh
-from parity import ATOL, RTOL, GpuRun, assert_close, check_case, head_inputs, say
+from parity import ATOL, RTOL, GpuRun, assert_close, check_case, compare_selection, head_inputs, say, selection_ref
 from synth_inputs import make_dout, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -104,6 +104,28 @@ def test_ties_take_lowest_index():
         assert np.array_equal(sel[l - 1], want)
     res = oracle.forward(q[0].float().cpu().numpy(), q[0].float().cpu().numpy(), q[0].float().cpu().numpy(), L, p, k)
     assert np.array_equal(sel[0], res["sel"][1]) and np.array_equal(sel[1], res["sel"][2])
+
+
+@pytest.mark.parametrize("p_two", [0.1, 0.02])
+def test_partial_ties_across_a_stratum(p_two):
+    # Rows are c_j times one fixed row (c_j = 2 with probability p_two, else
+    # 1), so every score takes one of two values and a stratum of 2048
+    # entries holds hundreds of equal ones. With p_two = 0.1 the quota-th
+    # largest score is the larger value and the kept ties (the first r in
+    # index order) run across several waves and chunks of the stratum; with
+    # 0.02 fewer than the quota hold the larger value and the threshold is the
+    # smaller one, most of the stratum tying with it.
+    N, H, d, L, p, k = 65536, 2, 64, 3, 2, 3000
+    g = torch.Generator().manual_seed(11)
+    u, w = torch.randn(d, generator=g), torch.randn(d, generator=g)
+    c = torch.where(torch.rand(H, N, 1, generator=g) < p_two, 2.0, 1.0)  # one factor per token
+    q, kk, v = ((c * row).to(torch.bfloat16).cuda() for row in (u, w, torch.randn(d, generator=g)))
+    run = GpuRun(q, kk, v, L, p, k)
+    for h in range(H):
+        ref = selection_ref(q, kk, h, L, p, k)
+        compare_selection(run, h, ref)
+        sc1 = ref["scores"][1]
+        say("  p_two=%.2f head %d: level 1 holds %d entries at the larger score" % (p_two, h, int((sc1 == sc1.max()).sum())))
 
 
 def test_deterministic_bitwise():
