@@ -1207,36 +1207,42 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a)
 // dQ without stored dS tiles (the plan drops them when the causal half of
 // S x S per head would take too much of the workspace): the query side of
 // the softmax gradient, with S and dP formed again from the gathered rows.
-// One workgroup per 128 queries (32 per wave); keys stream through a two-slot
-// LDS ring 32 at a time. Per key block, as in the forward, keys are the rows
-// of every product so that a lane owns one query:
+// One workgroup per 256 queries (eight waves of 32, one workgroup per CU);
+// keys stream through a three-slot LDS ring 32 at a time, two stages in
+// flight, each stage shared by the eight waves. Per key block, as in the
+// forward, keys are the rows of every product so that a lane owns one query:
 //   S^T = K Q^T (the logits the other kernels form, same operands),
 //   P^T = 2^(S^T log2(e)/sqrt(d) - LSE + 15)  (probabilities times 2^15),
 //   dP^T = V dO^T (the fp16 pair of dO_sub, as in the dK/dV kernel),
 //   dS^T = P^T (dP^T 2^-15 - delta 2^-15)    (delta is per query: per lane),
 //   dQ^T += K^T dS^T, with dS^T straight from the accumulator as operand B
 // (the kappa row order of K and V puts each lane's keys in runs of 8).
+//
+// A stage is a list of 64-chunk units (one MFMA operand fragment, or 1 KiB
+// of an fp8 tile), unit u at LDS chunk 64 u: K hi rows (NS units, k-step s
+// in unit s), V rows (NS), K^T (NS: fragment (hh, t) in unit hh NT + t), then
+// the fp8 K and V tiles (NS/2 each, linear copies) for bf16 inputs or the
+// fp16 K lo rows (NS) for fp32 inputs. Unit 8 r + w is transferred by wave w
+// in round r, so every thread issues the same number of transfers per stage.
 template <int D, bool KLO> struct DqrcStage {
-    static constexpr int BN = 32;
-    static constexpr int KCH = D / 8, TCH = BN / 8;
-    static constexpr int KROWS = BN * KCH, TROWS = D * TCH;
-    // K hi rows, the key's second operand (fp16 K lo for fp32 inputs, the fp8
-    // K tile for bf16 inputs, padded to one transfer per thread), V rows, the
-    // fp8 V tile (bf16 inputs), K^T
-    static constexpr int KH = 0, KL = KROWS, KLSIZE = KLO ? KROWS : 256;
-    static constexpr int VR = KL + KLSIZE, V8 = VR + KROWS, V8SIZE = KLO ? 0 : 256;
-    static constexpr int KT = V8 + V8SIZE;
-    static constexpr int SIZE = KT + TROWS;
-    static constexpr int KU = KROWS / 256, TU = TROWS / 256;
+    static constexpr int BN = 32, NW = 8;
+    static constexpr int NS = D / 16;
+    static constexpr int KH = 0, VR = 64 * NS, KT = 128 * NS;  // in chunks
+    static constexpr int KL = 192 * NS;                        // fp8 K tile, or K lo rows
+    static constexpr int V8 = KL + 32 * NS;                    // fp8 V tile (bf16 inputs)
+    static constexpr int UNITS = 4 * NS, SIZE = 64 * UNITS;    // 32 KiB per stage at d = 128
+    static constexpr int LOADS = UNITS / NW;                   // transfers per thread and stage
+    static constexpr int NSLOT = 3;
+    static_assert(UNITS % NW == 0, "whole rounds");
 };
 
 template <int D, bool KLO>
-__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dq_rc(AttnBwdArgs a)
 {
     typedef DqrcStage<D, KLO> St;
-    constexpr int BM = 128, BN = St::BN;
+    constexpr int BM = 32 * St::NW, BN = St::BN;
     constexpr int NS = D / 16, NT = D / 32, NM = D / 64;
-    __shared__ uint4 ring[2 * St::SIZE];
+    __shared__ uint4 ring[St::NSLOT * St::SIZE];
 
     const int nqb = (int)((a.S + BM - 1) / BM);
     const int h = blockIdx.x % a.H;
@@ -1252,45 +1258,55 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
     // workgroup's last one; their results are never read)
     const int jl = (int)min((int64_t)(nkb - 1), qw / BN);
 
-    // per-thread byte offsets inside a stage (operand order, as in the forward):
-    // K / V row chunk of k-step f = 4u + wave, key row kappa(c32); K^T chunk of
-    // fragment f = (hh, t): dimension 32t + c32, keys 16hh + 8g .. +7
-    uint32_t koff[St::KU], toff[St::TU];
-#pragma unroll
-    for (int u = 0; u < St::KU; ++u) {
-        const int f = 4 * u + wave;
-        koff[u] = 2u * (uint32_t)(kappa(c32) * D + (2 * f + g) * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < St::TU; ++u) {
-        const int f = 4 * u + wave, hh = f / NT, t = f % NT;
-        toff[u] = 2u * ((uint32_t)(32 * t + c32) * (uint32_t)a.S_pad + (uint32_t)(16 * hh + 8 * g));
-    }
     const uint16_t *khi = a.khi + hS * D, *klo = a.klo + hS * D, *vr = a.v + hS * D;
     const uint8_t *k8 = a.k8 + hS * D, *v8 = a.v8 + hS * D;
     const uint16_t *kt = a.khi_t + (int64_t)h * D * a.S_pad;
-    auto slot = [&](int kb) { return ring + (kb & 1) * St::SIZE; };
+    // Round r of this wave: unit 8 r + wave. kind: 0 K hi, 1 V, 2 K^T, 3 K lo
+    // rows, 4 fp8 K tile, 5 fp8 V tile (uniform over the wave); off: this
+    // lane's source byte offset within the stage's first key.
+    int kind[St::LOADS];
+    uint32_t off[St::LOADS];
+#pragma unroll
+    for (int r = 0; r < St::LOADS; ++r) {
+        const int u = St::NW * r + wave;
+        if (u < 3 * NS) {
+            const int f = u % NS;
+            kind[r] = u / NS;
+            if (kind[r] == 2) { // K^T fragment (hh, t): dimension 32 t + c32, keys 16 hh + 8 g .. +7
+                const int hh = f / NT, t = f % NT;
+                off[r] = 2u * ((uint32_t)(32 * t + c32) * (uint32_t)a.S_pad + (uint32_t)(16 * hh + 8 * g));
+            } else { // row fragment of k-step f: key row kappa(c32), dimensions 16 f + 8 g .. +7
+                off[r] = 2u * (uint32_t)(kappa(c32) * D + (2 * f + g) * 8);
+            }
+        } else if constexpr (KLO) {
+            kind[r] = 3;
+            off[r] = 2u * (uint32_t)(kappa(c32) * D + (2 * (u - 3 * NS) + g) * 8);
+        } else { // fp8 tiles: linear copies
+            const int i = u - 3 * NS;
+            kind[r] = i < NS / 2 ? 4 : 5;
+            off[r] = 16u * (uint32_t)(64 * (i % (NS / 2)) + lane);
+        }
+    }
+    auto slot = [&](int kb) { return ring + (kb % St::NSLOT) * St::SIZE; };
+    // Past the last stage the last one is loaded again (never read), so every
+    // stage is LOADS transfers per thread and a count of transfers in flight
+    // tells which stage has landed.
     auto issue = [&](int kb) {
-        if (kb >= nkb)
-            return;
-        const int64_t k0 = (int64_t)kb * BN;
+        const int64_t k0 = (int64_t)min(kb, nkb - 1) * BN;
         const uint4 *base = slot(kb);
 #pragma unroll
-        for (int u = 0; u < St::KU; ++u) {
-            dma16(khi + k0 * D, koff[u], base + St::KH + 256 * u + 64 * wave);
-            if constexpr (KLO)
-                dma16(klo + k0 * D, koff[u], base + St::KL + 256 * u + 64 * wave);
-            dma16(vr + k0 * D, koff[u], base + St::VR + 256 * u + 64 * wave);
+        for (int r = 0; r < St::LOADS; ++r) {
+            const uint4 *dst = base + 64 * (St::NW * r + wave);
+            switch (kind[r]) {
+            case 0: dma16(khi + k0 * D, off[r], dst); break;
+            case 1: dma16(vr + k0 * D, off[r], dst); break;
+            case 2: dma16(kt + k0, off[r], dst); break;
+            case 3: dma16(klo + k0 * D, off[r], dst); break;
+            case 4: dma16(k8 + k0 * D, off[r], dst); break;
+            default: dma16(v8 + k0 * D, off[r], dst); break;
+            }
         }
-        if constexpr (!KLO) { // fp8 tiles, stored in operand order: linear copies
-            dma16(k8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::KL + 64 * wave);
-            dma16(v8 + k0 * D, 16u * (uint32_t)(tid % (2 * D)), base + St::V8 + 64 * wave);
-        }
-#pragma unroll
-        for (int u = 0; u < St::TU; ++u)
-            dma16(kt + k0, toff[u], base + St::KT + 256 * u + 64 * wave);
     };
-    issue(0);
 
     // this lane's query as operand B: Q hi, dO_sub hi, and their lo parts
     // (fp16 for fp32 inputs; the fp8 tiles for bf16 inputs, which keep query
@@ -1325,7 +1341,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
     const float scale_log2 = ldexpf(a.scale_log2, -(exq + exk)); // staged rows: see the dK/dV kernel
     const float lq = a.lse[hS + qw + c32];   // log2-domain LSE - 15 of this lane's query
     const float dq8 = a.delta[hS + qw + c32]; // delta * 2^-15
-    // consume the loads here (see the forward kernel)
+    // consume the loads here, before the ring's transfers are in flight (see
+    // the forward kernel)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         asm volatile("" ::"v"(qh[s].x), "v"(dh[s].x));
@@ -1344,10 +1361,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         dq[t] = zero16();
+    issue(0);
+    issue(1);
     for (int j = 0; j < nkb; ++j) {
-        wait_async();  // stage j (the only one in flight)
-        lds_barrier(); // ... visible to all waves; the other slot (stage j-1) is free
-        issue(j + 1);
+        wait_async_n<St::LOADS>(); // stage j has landed (j + 1 may be in flight)
+        lds_barrier();             // ... visible to all waves; stage j - 1's slot is free
+        issue(j + 2);
         if (j > jl) // (uniform) keys after every query of this wave
             continue;
         const uint4 *base = slot(j);
@@ -1391,6 +1410,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_rc(AttnBwdArgs a)
             dq[t] = mfma32(base[St::KT + 64 * (NT + t) + lane], db1, dq[t]);
         }
     }
+    wait_async(); // the transfers past the last stage
+
     float *dqr = a.dq + qrow;
     const float sq = ldexpf(a.scale, -(exd + exv + exk));
 #pragma unroll
@@ -1410,11 +1431,12 @@ static void launch_dq_t(const Plan &pl, const AttnBwdArgs &a, bool klo, hipStrea
         hipLaunchKernelGGL((k_attn_bwd_dq<D>), grid, dim3(64 * DqStage<D>::NW), 0, s, a);
         return;
     }
-    const dim3 grid((unsigned)((pl.S + 127) / 128) * pl.H); // 128 queries per workgroup
+    constexpr int NW = DqrcStage<D, false>::NW; // 32 queries per wave
+    const dim3 grid((unsigned)((pl.S + 32 * NW - 1) / (32 * NW)) * pl.H);
     if (klo)
-        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, true>), grid, dim3(64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_attn_bwd_dq_rc<D, false>), grid, dim3(64 * NW), 0, s, a);
 }
 
 hipError_t launch_attn_bwd_dq(const Plan &pl, const AttnBwdArgs &a, hipStream_t s)
