@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_long_context_lh_amd as lh
 from parity import Failures, GpuRun, compare_backward, compare_forward, compare_selection, fmt_stats, head_inputs, say
 from synth_inputs import WORKLOADS, make_dout, make_qkv
 
@@ -108,3 +109,26 @@ def test_sweep_workload_sampled(name):
     rng = np.random.default_rng(11)
     tokens = np.concatenate([[0, 1, 2, 3, 1023, 1024, w.N // 2, w.N - 1], rng.integers(0, w.N, 24)])
     check_sampled_tokens(run, q, k, v, dout, 9, tokens, last=8, tag=w.name)
+
+
+
+@pytest.mark.timeout(600)
+def test_largest_selection_total():
+    # (L-1) k = 16384, the most the index kernel holds in LDS (64 KiB of
+    # selections); both ranked levels in strata; S = 49152 with the dS tiles
+    # stored. Selection, order and slot maps bit-exact on both heads; sampled
+    # tokens of one head against the oracle.
+    from parity import check_sampled_tokens, selection_ref
+    N, H, d, L, p, k = 65536, 2, 64, 3, 2, 8192
+    assert lh.check_shape(N, H, d, L, p, k, torch.bfloat16) == 0
+    assert lh.check_shape(N, H, d, L, p, k + 1, torch.bfloat16) == 3  # one more selection: unsupported
+    say("largest selection total: N=%d H=%d d=%d L=%d p=%d k=%d S=%d" % (N, H, d, L, p, k,
+                                                                       oracle.subseq_len(N, L, p, k)))
+    q, kk, v = make_qkv(N, H, d, torch.bfloat16, 16, seed=21, device="cuda")
+    dout = make_dout(N, H, d, torch.bfloat16, seed=22, device="cuda")
+    run = GpuRun(q, kk, v, L, p, k, dout)
+    for h in range(H):
+        compare_selection(run, h, selection_ref(q, kk, h, L, p, k))
+    rng = np.random.default_rng(23)
+    tokens = np.concatenate([[0, 1, 2, 3, 1023, 1024, N // 2, N - 1], rng.integers(0, N, 24)])
+    check_sampled_tokens(run, q, kk, v, dout, 1, tokens, last=8, tag="largest-selection")
