@@ -89,18 +89,21 @@ def ds_tiles_kept(w, S: int) -> bool:
     return 2 * w.H * (T * (T + 1) // 2) * 1024 <= lh.ds_tile_budget()
 
 
-def mfma_factor(stage: str, dtype_name: str, nograd: bool) -> float:
+def mfma_factor(stage: str, dtype_name: str, nograd: bool, ds_kept: bool = True) -> float:
     """Matrix-core cycles the attention kernels execute per algorithmic one:
     the precision scheme's extra products per 32x32 tile pair (fp16 32x32x16
     products take 32 cycles, block-scaled fp8 32x32x64 ones 64). bf16 inputs:
     forward 24 fp16 + 2 fp8 (without the backward's context 16 + 2) against
-    16; dK/dV 32 + 4 fp8 against 32; dQ 8 against 8. fp32 inputs: forward
-    40 (32 without the context), dK/dV 56."""
+    16; dK/dV 32 + 4 fp8 against 32; dQ from stored tiles 8 against 8, dQ
+    recomputing S and dP 24 + 4 fp8 against 24. fp32 inputs: forward 40 (32
+    without the context), dK/dV 56, recomputing dQ 48."""
     bf16 = dtype_name == "bf16"
     if stage == "attn_fwd":
         return ((16 if nograd else 24) * 32 + 2 * 64) / 512.0 if bf16 else (32.0 if nograd else 40.0) / 16.0
     if stage == "attn_bwd_dkdv":
         return (32 * 32 + 4 * 64) / 1024.0 if bf16 else 56.0 / 32.0
+    if stage == "attn_bwd_dq" and not ds_kept:
+        return (24 * 32 + 4 * 64) / 768.0 if bf16 else 48.0 / 24.0
     return 1.0
 
 
@@ -336,7 +339,7 @@ def measure(lh, hip, w0, steps, warmup, backward=True, nograd=False):
     for name, ms in stage_ms.items():
         a = algorithmic(name, w, S) / (ms / 1000.0) if ms > 0 else 0.0
         if name in MFMA_STAGES:
-            f = mfma_factor(name, w.dtype_name, nograd)
+            f = mfma_factor(name, w.dtype_name, nograd, ds_tiles_kept(w, S))
             stages[name] = {"ms": round(ms, 4), "TFLOP/s": round(a / 1e12, 1), "frac": round(a / 1e12 / MFMA_F16_PEAK_TFS, 4),
                             "executed_TFLOP/s": round(a * f / 1e12, 1), "mfma_factor": f}
         else:
